@@ -1,0 +1,243 @@
+/*
+ * pagedkv.h — C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * The library implements the decode-time hot path of a block-paged KV cache:
+ *   1. kv_cache_append: scatter each new token's K and V rows into a physical
+ *      block through a slot mapping;
+ *   2. paged_decode_attention: one query per sequence attends over its cached
+ *      tokens, gathered page by page through a per-sequence block table,
+ *      computing softmax(q K^T * scale) V, optionally restricted to a sliding
+ *      window plus sink tokens, or to a per-step list of selected pages.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [primer]  KV-cache primer "从一次线上事故说起：为什么聊到第三十轮，响应突然卡住了" (cf-1.com):
+ *             §2.2 (decode appends the new token's K/V, then attends over all cached tokens),
+ *             §3.1 (KV-size formula), §4.1 (PagedAttention: fixed 16-token blocks that need
+ *             not be contiguous, mapped by a per-sequence block table), §4.3 (sliding window).
+ *   [OVAL]    "OVAL — Output-Aware Local Page Bases for KV Cache Retrieval" (2kiu.com):
+ *             §2.2 and §3.3 (a small integer array of page base indices chosen per step;
+ *             32-token pages stored contiguously), §3.2 (window clamped to [0, cache length),
+ *             never reading uninitialised memory past the cache length).
+ *   [Novita]  "How KV Sparsity Achieves 1.5x Acceleration for vLLM" (Novita AI blog):
+ *             §關鍵技術 1 (per-layer choice of full cache or sliding window over one unified
+ *             paged memory), §關鍵技術 2 (one-pass online softmax; the kernel keeps rowmax and
+ *             the running sum l, which can be exported at negligible cost).
+ *   [naive]   koas-w blog "naive KV cache" post (2026-03-25), §"KV cache的思想": one write
+ *             position per step, shared by all layers, advanced once after the last layer.
+ *   [TF]      "Transformer模型中的KV Cache优化推理策略" (yutianautomatic.com), §"为什么传统推理方式
+ *             难以为继？" (Attention = softmax(Q K^T / sqrt(d_k)) V) and §"增量解码的接口设计"
+ *             (the new token attends over cached plus new keys).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host". The caller owns
+ *     every buffer (including workspaces); the library never allocates or frees
+ *     memory and keeps no state between calls, so calls are reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *     enqueued asynchronously; no entry point synchronises the host.
+ *   - The return value reports host-side argument validation and launch errors
+ *     only. Validation happens before anything is enqueued: on any error nothing
+ *     is launched and no output is touched.
+ *   - Device-side preconditions (listed per call) are not checked on the host.
+ *     Where a violation could address memory outside the caller's buffers the
+ *     kernels skip the offending element instead (documented per call), so a bad
+ *     index never faults; the result for that sequence is then unspecified.
+ *
+ * Cache layout ("lane-chunk order"). Both pools are arrays of
+ *   num_blocks x num_kv_heads page tiles, each tile holding block_size x head_dim
+ * elements of the cache dtype; the tile of (block, head) starts at element
+ *   (block * num_kv_heads + head) * block_size * head_dim.
+ * Within a tile, tokens come in sub-tiles of 16 (block_size is a multiple of 16):
+ * token t lives in sub-tile t / 16, which starts at element (t / 16) * 16 * head_dim.
+ * A sub-tile is a sequence of 16-byte chunks of E = 16 / sizeof(element) elements
+ * (E = 8 for bf16/fp16, 4 for fp32). With tau = t % 16, the element (tau, x),
+ * x in [0, head_dim), sits at  chunk * E + pos  where
+ *   K:  chunk = (x / (4E)) * 64 + ((x / E) % 4) * 16 + tau,       pos = x % E
+ *   V:  R = E / 4, n = x / 16, c = x % 16, j = tau / 4, i = tau % 4,
+ *       chunk = ((n / R) * 4 + j) * 16 + c,                      pos = (n % R) * 4 + i
+ * Every chunk a wavefront lane feeds to a matrix instruction is then one
+ * contiguous 16-byte load, and the 64 lanes of a wavefront read 1 KiB of
+ * consecutive bytes per load. The order is a bijection on each sub-tile, so the
+ * pool size equals that of a dense [num_blocks][num_kv_heads][block_size][head_dim]
+ * array; only kv_cache_append writes it and only the attention calls read it.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+    PKV_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent (e.g. Hq % Hkv != 0) */
+    PKV_ERR_UNSUPPORTED = 3, /* dtype / head_dim / block_size / group size not built */
+    PKV_ERR_MODE = 4,        /* window and page_list both set, or a bad sparsity field */
+    PKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
+    PKV_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Shape of one layer's cache (one K pool and one V pool, same shape and dtype).
+ * Supported: dtype in {F32, F16, BF16}; head_dim in {64, 128};
+ * block_size a multiple of 16 in [16, 256]. */
+typedef struct {
+    int32_t num_blocks;   /* physical blocks in each pool */
+    int32_t block_size;   /* tokens per block (page size P) */
+    int32_t num_kv_heads; /* Hkv */
+    int32_t head_dim;     /* d */
+    pkv_dtype dtype;      /* element type of the pools, of k_new/v_new and of q */
+} pkv_cache_desc;
+
+/* Which cached tokens one decode step attends to, and a tuning knob.
+ * A NULL pointer means full attention with automatic splitting. For a sequence
+ * of context length L (the new token included, at position L-1):
+ *   full:    tokens [0, L).
+ *   window:  window > 0 and window < L: the last `window` tokens [L-window, L)
+ *            plus the first min(num_sinks, L) tokens, each token once
+ *            ([primer] §4.3; [Novita] §關鍵技術 1). window >= L is full attention.
+ *   pages:   page_list != NULL: the tokens of the listed logical pages,
+ *            page p covering [p*P, min((p+1)*P, L)) ([OVAL] §2.2, §3.3). The list is
+ *            row b of a [batch][pages_per_seq] int32 device array; entries < 0 are
+ *            padding. Preconditions: the non-negative entries of a row are
+ *            distinct and ascending. Pages starting at or past L contribute nothing
+ *            and their block-table entries are never read.
+ * window > 0 together with page_list is PKV_ERR_MODE. num_sinks is ignored
+ * unless window > 0. */
+typedef struct {
+    int32_t window;          /* <= 0: no window */
+    int32_t num_sinks;       /* >= 0 */
+    const int32_t* page_list; /* device, nullable */
+    int32_t pages_per_seq;   /* row length of page_list; > 0 when page_list != NULL */
+    int32_t split_tokens;    /* 0: automatic. Otherwise tokens per split-K partition,
+                                a positive multiple of 64 (rounded up to one). */
+} pkv_decode_opts;
+
+/* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";
+ * [primer] §4.1 for the block addressing).
+ * For every i in [0, num_tokens) with slot_mapping[i] >= 0, with
+ * blk = slot / block_size and t = slot % block_size:
+ *     K pool element (blk, h, t, x) = k_new[i][h][x]   for all h < Hkv, x < d,
+ * and likewise V from v_new. The copy is bit-exact (no conversion).
+ *   k_cache, v_cache: the pools (lane-chunk order above), written in place.
+ *   k_new, v_new:     [num_tokens][num_kv_heads][head_dim], dtype == desc->dtype.
+ *   slot_mapping:     [num_tokens] int32; negative = skip that token.
+ * num_tokens == 0 is a no-op. Preconditions: the non-negative slots are distinct
+ * (two tokens writing one slot race). Slots >= num_blocks * block_size are
+ * skipped by the kernel. */
+pkv_status kv_cache_append(const pkv_cache_desc* desc /* host */,
+                           void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           void* stream);
+
+/* paged_decode_attention — one query per sequence over its paged cache
+ * ([TF] §"为什么传统推理方式难以为继？" for the formula; [primer] §4.1 for the block
+ * table; [Novita] §關鍵技術 2 for the one-pass online softmax).
+ * For each sequence b and query head h (kv head h / (Hq / Hkv), contiguous groups):
+ *     s_t = scale * <q[b][h], K_t>   over the attended tokens t (opts above),
+ *     out[b][h] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),  m = max_t s_t,
+ *     lse[b][h] = m + ln(sum_t exp(s_t - m))    (natural log).
+ * Token t of sequence b is read from physical block block_table[b][t / P] at
+ * position t % P. With no attended token (L == 0): out = 0, lse = -inf.
+ *   q:            [batch][num_q_heads][head_dim], dtype == desc->dtype.
+ *   block_table:  [batch][max_blocks_per_seq] int32.
+ *   context_lens: [batch] int32, device; L_b includes the token appended this step.
+ *   max_context_len (host): an upper bound on every L_b; it sizes the launch grid
+ *                 so the call never reads device data on the host (graph-capturable).
+ *   scale:        <= 0 selects 1 / sqrt(head_dim).
+ *   opts (host):  nullable, see pkv_decode_opts.
+ *   out:          [batch][num_q_heads][head_dim] of out_dtype (F32 or desc->dtype).
+ *   lse_out:      nullable [batch][num_q_heads] fp32.
+ *   workspace:    at least paged_decode_attention_workspace_size(...) bytes,
+ *                 device memory, 256-byte aligned; contents on entry are ignored.
+ * Kernel-side guards: L_b is clamped to min(max_context_len, max_blocks_per_seq * P);
+ * tokens whose block id falls outside [0, num_blocks) are skipped. */
+pkv_status paged_decode_attention(const pkv_cache_desc* desc /* host */,
+                                  const void* k_cache, const void* v_cache,
+                                  const void* q,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens,
+                                  int32_t batch, int32_t num_q_heads,
+                                  int32_t max_context_len,
+                                  float scale,
+                                  const pkv_decode_opts* opts /* host, nullable */,
+                                  void* out, pkv_dtype out_dtype,
+                                  float* lse_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Bytes of workspace paged_decode_attention needs for these arguments (0 when
+ * the call would need none). Returns 0 as well for arguments that the call
+ * would reject; pure host function. */
+size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc /* host */,
+                                             int32_t batch, int32_t num_q_heads,
+                                             int32_t max_context_len,
+                                             const pkv_decode_opts* opts /* host, nullable */);
+
+/* Number of split-K partitions per (sequence, head) that the partial call writes
+ * for these arguments (>= 1), or 0 for rejected arguments. Pure host function. */
+int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc /* host */,
+                                          int32_t max_context_len,
+                                          const pkv_decode_opts* opts /* host, nullable */);
+
+/* paged_decode_attention_partial — the split-K first phase, exporting per-split
+ * softmax statistics ([Novita] §關鍵技術 2: the attention kernel already holds the
+ * running max and sum l and can return them). The attended token set of each
+ * sequence (same rules as paged_decode_attention) is cut, in ascending token
+ * order, into S = paged_decode_attention_num_splits(...) partitions; for
+ * partition s of (b, h), over its tokens t:
+ *     m_part[b][h][s] = max_t s_t                       (natural-log units),
+ *     l_part[b][h][s] = sum_t exp(s_t - m_part),
+ *     o_part[b][h][s][:] = sum_t exp(s_t - m_part) V_t  (unnormalised).
+ * An empty partition stores m = -inf, l = 0 and leaves its o_part row unwritten.
+ * All arguments as in paged_decode_attention, plus
+ *   o_part: [batch][num_q_heads][S][head_dim] fp32;  m_part, l_part: [batch][num_q_heads][S] fp32;
+ *   num_splits: S as returned by the query (PKV_ERR_SHAPE otherwise).
+ * Partial results from several calls over disjoint token sets (for example
+ * different devices holding different pages) combine with paged_decode_combine. */
+pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc /* host */,
+                                          const void* k_cache, const void* v_cache,
+                                          const void* q,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens,
+                                          int32_t batch, int32_t num_q_heads,
+                                          int32_t max_context_len,
+                                          float scale,
+                                          const pkv_decode_opts* opts /* host, nullable */,
+                                          float* o_part, float* m_part, float* l_part,
+                                          int32_t num_splits,
+                                          void* stream);
+
+/* paged_decode_combine — cross-split log-sum-exp reduction. For each (b, h), over
+ * the partitions s with l_part > 0:  M = max_s m_s,  w_s = exp(m_s - M),
+ *     out[b][h] = sum_s w_s o_s / sum_s w_s l_s,   lse[b][h] = M + ln(sum_s w_s l_s).
+ * With no such partition: out = 0, lse = -inf. Layouts as in the partial call;
+ * out is [batch][num_q_heads][head_dim] of out_dtype (F32, F16 or BF16, rounded to
+ * nearest even); lse_out is nullable. */
+pkv_status paged_decode_combine(const float* o_part, const float* m_part, const float* l_part,
+                                int32_t batch, int32_t num_q_heads, int32_t num_splits,
+                                int32_t head_dim,
+                                void* out, pkv_dtype out_dtype, float* lse_out,
+                                void* stream);
+
+/* KV-cache size in bytes by the formula of [primer] §3.1,
+ *   2 x batch x layers x kv_heads x head_dim x seq_len x dtype_bytes,
+ * with seq_len rounded up to a multiple of block_size when block_size > 0 (a paged
+ * cache allocates whole blocks). Pure host function; 0 on negative inputs. */
+uint64_t pkv_kv_cache_bytes(int64_t batch, int64_t layers, int64_t kv_heads,
+                            int64_t head_dim, int64_t seq_len, int64_t dtype_bytes,
+                            int64_t block_size);
+
+/* Static description of a status code. */
+const char* pkv_status_string(pkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

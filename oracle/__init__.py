@@ -1,0 +1,221 @@
+"""CPU oracle for paged decode attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (``paged_kv_cache_16_amd``)
+never imports it, and it never imports the product path.
+
+This module is argument marshalling around ``oracle.c`` (plain fp64 C, built with
+gcc into ``liboracle.so``): numpy arrays in, numpy arrays out. Element types are
+passed as raw bits: ``uint16`` arrays for bf16/fp16, ``float32`` for fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def compile_oracle(src: str, so: str) -> str:
+    """gcc -O2, no fast-math: the oracle's summation order stays as written."""
+    tmp = so + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+                    "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, so)
+    return so
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_SO):
+        compile_oracle(SOURCE, _SO)
+    return _SO
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _raw(a: np.ndarray, dtype: str) -> np.ndarray:
+    want = np.float32 if dtype == "f32" else np.uint16
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError(f"{dtype} data must be passed as {np.dtype(want).name}, got {a.dtype}")
+    return a
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Oracle:
+    """One loaded build of oracle.c (the default build, or a test's mutated copy)."""
+
+    def __init__(self, so_path: str):
+        L = ctypes.CDLL(so_path)
+        L.oracle_k_index.restype = _I64
+        L.oracle_k_index.argtypes = [_I64, _I, _I, _I, _I, _I, _I, _I]
+        L.oracle_v_index.restype = _I64
+        L.oracle_v_index.argtypes = [_I64, _I, _I, _I, _I, _I, _I, _I]
+        L.oracle_kv_append.restype = _I
+        L.oracle_kv_append.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _I64]
+        L.oracle_decode_attention.restype = _I
+        L.oracle_decode_attention.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I,
+                                              _P, _D, _I, _I, _P, _I, _P, _P]
+        L.oracle_decode_attention_split.restype = _I
+        L.oracle_decode_attention_split.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _P, _I, _I,
+                                                    _P, _I, _P, _D, _I, _I, _P, _I, _I, _I, _P,
+                                                    _P, _P, _P, _P]
+        L.oracle_bruteforce.restype = _I
+        L.oracle_bruteforce.argtypes = [_I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _D, _I, _I, _I,
+                                        _P, _I, _P, _P]
+        L.oracle_kv_cache_bytes.restype = ctypes.c_uint64
+        L.oracle_kv_cache_bytes.argtypes = [_I64] * 7
+        self.lib = L
+
+    @staticmethod
+    def _check(rc: int, what: str) -> None:
+        if rc != 0:
+            raise OracleError(f"{what}: oracle returned {rc}")
+
+    def k_index(self, blk, h, t, x, Hkv, P, d, dtype) -> int:
+        return int(self.lib.oracle_k_index(blk, h, t, x, Hkv, P, d, DTYPE_CODE[dtype]))
+
+    def v_index(self, blk, h, t, x, Hkv, P, d, dtype) -> int:
+        return int(self.lib.oracle_v_index(blk, h, t, x, Hkv, P, d, DTYPE_CODE[dtype]))
+
+    def kv_append(self, dtype, kpool, vpool, k_new, v_new, slots, *, P, Hkv, d):
+        """Writes k_new/v_new ([N][Hkv][d] raw) into the flat raw pools, in place."""
+        for a in (kpool, vpool):
+            if not (isinstance(a, np.ndarray) and a.flags.c_contiguous):
+                raise TypeError("pools must be C-contiguous numpy arrays (written in place)")
+        kpool, vpool = _raw(kpool, dtype), _raw(vpool, dtype)
+        k_new, v_new = _raw(k_new, dtype), _raw(v_new, dtype)
+        slots = _i32(slots)
+        nb = kpool.size // (Hkv * P * d)
+        self._check(self.lib.oracle_kv_append(DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool),
+                                              _ptr(vpool), _ptr(k_new), _ptr(v_new),
+                                              _ptr(slots), slots.size), "kv_append")
+        return kpool, vpool
+
+    def _common(self, dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list):
+        kpool, vpool, q = _raw(kpool, dtype), _raw(vpool, dtype), _raw(q, dtype)
+        bt = _i32(block_table)
+        cl = _i32(context_lens).reshape(-1)
+        B = cl.size
+        Hq = q.size // (B * d) if B else 1
+        mb = bt.shape[1] if bt.ndim == 2 else 0
+        pl = None if page_list is None else _i32(page_list)
+        pps = 0 if pl is None else pl.shape[1]
+        nb = kpool.size // (Hkv * P * d)
+        return kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb
+
+    def decode_attention(self, dtype, kpool, vpool, q, block_table, context_lens, *, P, Hkv, d,
+                         scale=0.0, window=0, sinks=0, page_list=None):
+        """Returns (out [B][Hq][d] float64, lse [B][Hq] float64)."""
+        kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
+            dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list)
+        out = np.zeros((B, Hq, d), np.float64)
+        lse = np.zeros((B, Hq), np.float64)
+        self._check(self.lib.oracle_decode_attention(
+            DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool), _ptr(vpool), _ptr(q), B, Hq, _ptr(bt),
+            mb, _ptr(cl), float(scale), int(window), int(sinks), _ptr(pl), pps, _ptr(out),
+            _ptr(lse)), "decode_attention")
+        return out, lse
+
+    def decode_attention_split(self, dtype, kpool, vpool, q, block_table, context_lens, *, P,
+                               Hkv, d, units, max_splits, scale=0.0, window=0, sinks=0,
+                               page_list=None):
+        """Returns (o_part, m_part, l_part, out, lse), all float64."""
+        kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
+            dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list)
+        o_part = np.zeros((B, Hq, max_splits, d), np.float64)
+        m_part = np.zeros((B, Hq, max_splits), np.float64)
+        l_part = np.zeros((B, Hq, max_splits), np.float64)
+        out = np.zeros((B, Hq, d), np.float64)
+        lse = np.zeros((B, Hq), np.float64)
+        self._check(self.lib.oracle_decode_attention_split(
+            DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool), _ptr(vpool), _ptr(q), B, Hq, _ptr(bt),
+            mb, _ptr(cl), float(scale), int(window), int(sinks), _ptr(pl), pps, int(units),
+            int(max_splits), _ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(out), _ptr(lse)),
+            "decode_attention_split")
+        return o_part, m_part, l_part, out, lse
+
+    def bruteforce(self, dtype, K_log, V_log, q, context_lens, *, Hkv, d, scale=0.0, P=16,
+                   window=0, sinks=0, page_list=None):
+        """Contiguous-cache reference; K_log/V_log: [B][Lmax][Hkv][d] raw. Long doubles out."""
+        K_log, V_log, q = _raw(K_log, dtype), _raw(V_log, dtype), _raw(q, dtype)
+        cl = _i32(context_lens).reshape(-1)
+        B = cl.size
+        Lmax = K_log.shape[1]
+        Hq = q.size // (B * d) if B else 1
+        pl = None if page_list is None else _i32(page_list)
+        pps = 0 if pl is None else pl.shape[1]
+        out = np.zeros((B, Hq, d), np.longdouble)
+        lse = np.zeros((B, Hq), np.longdouble)
+        self._check(self.lib.oracle_bruteforce(
+            DTYPE_CODE[dtype], _ptr(K_log), _ptr(V_log), Lmax, _ptr(q), B, Hq, Hkv, d, _ptr(cl),
+            float(scale), int(P), int(window), int(sinks), _ptr(pl), pps, _ptr(out), _ptr(lse)),
+            "bruteforce")
+        return out, lse
+
+    def kv_cache_bytes(self, batch, layers, heads, head_dim, seq_len, dtype_bytes,
+                       block_size=0) -> int:
+        return int(self.lib.oracle_kv_cache_bytes(batch, layers, heads, head_dim, seq_len,
+                                                  dtype_bytes, block_size))
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(SOURCE):
+            build(force=True)
+        _default = Oracle(_SO)
+    return _default
+
+
+def k_index(*a, **k):
+    return default().k_index(*a, **k)
+
+
+def v_index(*a, **k):
+    return default().v_index(*a, **k)
+
+
+def kv_append(*a, **k):
+    return default().kv_append(*a, **k)
+
+
+def decode_attention(*a, **k):
+    return default().decode_attention(*a, **k)
+
+
+def decode_attention_split(*a, **k):
+    return default().decode_attention_split(*a, **k)
+
+
+def bruteforce(*a, **k):
+    return default().bruteforce(*a, **k)
+
+
+def kv_cache_bytes(*a, **k):
+    return default().kv_cache_bytes(*a, **k)

@@ -1,0 +1,422 @@
+/*
+ * oracle.c — plain, slow CPU reference for paged decode attention.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library; the product path never does. It shares
+ * no code, header, table or helper with the HIP library: everything it needs,
+ * including the cache layout, is written out again here from its definition.
+ *
+ * Arithmetic: every input element (fp32, fp16 or bf16) is decoded exactly into a
+ * double; dot products, the softmax and the weighted sums run in double in
+ * ascending index order; the brute-force path runs in long double.
+ *
+ * Sources (web pages, by title and section):
+ *   [primer] KV-cache primer "从一次线上事故说起：为什么聊到第三十轮，响应突然卡住了"
+ *            (cf-1.com): §2.2 decode = append the new token's K/V, then attend over all
+ *            cached tokens; §3.1 KV-size formula; §4.1 block table; §4.3 sliding window.
+ *   [OVAL]   "OVAL — Output-Aware Local Page Bases for KV Cache Retrieval" (2kiu.com):
+ *            §2.2/§3.3 per-step page base indices; §3.2 window clamps.
+ *   [Novita] "How KV Sparsity Achieves 1.5x Acceleration for vLLM": §關鍵技術 1 per-layer
+ *            full cache or sliding window; §關鍵技術 2 online softmax keeping rowmax and l.
+ *   [TF]     "Transformer模型中的KV Cache优化推理策略": §"为什么传统推理方式难以为继？"
+ *            Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - the scale defaults to 1/sqrt(head_dim) ([TF] formula) and may be overridden;
+ *   - query head h uses kv head h / (Hq / Hkv) (contiguous GQA groups);
+ *   - the window is the last W tokens including the new one, plus the first S
+ *     "sink" tokens, each token once; W >= L is full attention;
+ *   - page_list entries are logical page ids per sequence, shared by all heads,
+ *     translated through the block table; entries < 0 are padding;
+ *   - L == 0 gives out = 0 and lse = -inf.
+ *
+ * Parity status: every function here is pinned by the CPU tests (closed forms,
+ * invariants, brute force, the primer's worked KV-size values); none is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_PRECONDITION = 2, ORC_ERR_NOMEM = 3 };
+
+static size_t elem_size(int dt) { return dt == ORC_F32 ? 4u : 2u; }
+
+/* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24); /* subnormal: f * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25); /* (1.f) * 2^(e-15), as an integer * 2^-10 */
+    return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+static double decode_bf16(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double load_elem(const void* base, size_t idx, int dt) {
+    if (dt == ORC_F32) {
+        float f;
+        memcpy(&f, (const char*)base + idx * 4, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + idx * 2, 2);
+    return dt == ORC_F16 ? decode_f16(h) : decode_bf16(h);
+}
+
+/* Cache layout, as the library's interface documents it ("lane-chunk order").
+ * Element (block blk, kv head h, token-in-block t, dim x) of a pool lives at the
+ * returned element index. E = elements per 16-byte chunk. */
+static size_t k_index(size_t blk, int h, int t, int x, int Hkv, int P, int d, int dt) {
+    int E = (int)(16 / elem_size(dt));
+    size_t tile = ((size_t)blk * Hkv + h) * (size_t)P * d;
+    size_t sub = (size_t)(t / 16) * 16 * d;
+    int tau = t % 16;
+    size_t chunk = (size_t)(x / (4 * E)) * 64 + (size_t)((x / E) % 4) * 16 + tau;
+    return tile + sub + chunk * E + (size_t)(x % E);
+}
+
+static size_t v_index(size_t blk, int h, int t, int x, int Hkv, int P, int d, int dt) {
+    int E = (int)(16 / elem_size(dt));
+    int R = E / 4;
+    size_t tile = ((size_t)blk * Hkv + h) * (size_t)P * d;
+    size_t sub = (size_t)(t / 16) * 16 * d;
+    int tau = t % 16;
+    int n = x / 16, c = x % 16, j = tau / 4, i = tau % 4;
+    size_t chunk = ((size_t)(n / R) * 4 + j) * 16 + c;
+    return tile + sub + chunk * E + (size_t)((n % R) * 4 + i);
+}
+
+static int shape_ok(int dt, int P, int d) {
+    if (dt != ORC_F32 && dt != ORC_F16 && dt != ORC_BF16) return 0;
+    if (P <= 0 || P % 16 != 0) return 0;
+    int E = (int)(16 / elem_size(dt));
+    return d > 0 && d % (4 * E) == 0 && d % 16 == 0;
+}
+
+/* Exposed so the tests can check the layout against hand-computed positions. */
+int64_t oracle_k_index(int64_t blk, int h, int t, int x, int Hkv, int P, int d, int dt) {
+    if (!shape_ok(dt, P, d)) return -1;
+    return (int64_t)k_index((size_t)blk, h, t, x, Hkv, P, d, dt);
+}
+int64_t oracle_v_index(int64_t blk, int h, int t, int x, int Hkv, int P, int d, int dt) {
+    if (!shape_ok(dt, P, d)) return -1;
+    return (int64_t)v_index((size_t)blk, h, t, x, Hkv, P, d, dt);
+}
+
+/* Append ([primer] §2.2; [primer] §4.1): token i goes to slot s = slots[i],
+ * block s / P, position s % P, for every kv head and dim; bytes are copied. */
+int oracle_kv_append(int dt, int64_t num_blocks, int P, int Hkv, int d,
+                     void* kpool, void* vpool, const void* knew, const void* vnew,
+                     const int32_t* slots, int64_t n) {
+    if (!shape_ok(dt, P, d) || Hkv <= 0 || num_blocks < 0 || n < 0) return ORC_ERR_ARG;
+    size_t es = elem_size(dt);
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t s = slots[i];
+        if (s < 0) continue;
+        if (s >= num_blocks * (int64_t)P) return ORC_ERR_PRECONDITION;
+        int64_t blk = s / P;
+        int t = (int)(s % P);
+        for (int h = 0; h < Hkv; ++h)
+            for (int x = 0; x < d; ++x) {
+                size_t src = ((size_t)i * Hkv + h) * d + x;
+                memcpy((char*)kpool + k_index(blk, h, t, x, Hkv, P, d, dt) * es,
+                       (const char*)knew + src * es, es);
+                memcpy((char*)vpool + v_index(blk, h, t, x, Hkv, P, d, dt) * es,
+                       (const char*)vnew + src * es, es);
+            }
+    }
+    return ORC_OK;
+}
+
+/* Is logical token t (0 <= t < L) attended? Full / window+sinks / page list. */
+static int attended(int t, int L, int P, int window, int sinks,
+                    const int32_t* pages, int npages) {
+    if (pages) {
+        for (int k = 0; k < npages; ++k)
+            if (pages[k] >= 0 && pages[k] == t / P) return 1;
+        return 0;
+    }
+    if (window > 0 && window < L) return t < sinks || t >= L - window;
+    return 1;
+}
+
+/* Checks the page-list preconditions of one row: non-negative entries distinct
+ * and ascending. */
+static int pages_ok(const int32_t* pages, int npages) {
+    int last = -1;
+    for (int k = 0; k < npages; ++k) {
+        if (pages[k] < 0) continue;
+        if (pages[k] <= last) return 0;
+        last = pages[k];
+    }
+    return 1;
+}
+
+static int common_args_ok(int dt, int64_t num_blocks, int P, int Hkv, int d, int B, int Hq,
+                          int max_blocks, int window, int sinks, const int32_t* page_list,
+                          int pps) {
+    if (!shape_ok(dt, P, d) || Hkv <= 0 || num_blocks < 0 || B < 0 || Hq <= 0) return 0;
+    if (Hq % Hkv != 0 || max_blocks < 0 || sinks < 0) return 0;
+    if (page_list && (window > 0 || pps <= 0)) return 0;
+    return 1;
+}
+
+/* Gathers the logits of one (b, h) over the attended tokens, ascending.
+ * Returns the count, or -1 on a precondition violation. */
+static int64_t gather_logits(int dt, int64_t num_blocks, int P, int Hkv, int d,
+                             const void* kpool, const void* q, int Hq, int b, int h,
+                             const int32_t* bt_row, int max_blocks, int L, double scale,
+                             int window, int sinks, const int32_t* pages, int npages,
+                             double* logits, int64_t* toks) {
+    int G = Hq / Hkv;
+    int kvh = h / G;
+    int64_t cnt = 0;
+    for (int t = 0; t < L; ++t) {
+        if (!attended(t, L, P, window, sinks, pages, npages)) continue;
+        if (t / P >= max_blocks) return -1;
+        int64_t blk = bt_row[t / P];
+        if (blk < 0 || blk >= num_blocks) return -1;
+        double dot = 0.0;
+        for (int x = 0; x < d; ++x)
+            dot += load_elem(q, ((size_t)b * Hq + h) * d + x, dt) *
+                   load_elem(kpool, k_index(blk, kvh, t % P, x, Hkv, P, d, dt), dt);
+        logits[cnt] = scale * dot;
+        toks[cnt] = t;
+        ++cnt;
+    }
+    return cnt;
+}
+
+/* Decode attention ([TF] formula; [primer] §2.2, §4.1; [OVAL] §3.3 page indices;
+ * [primer] §4.3 window). out: [B][Hq][d] doubles; lse: [B][Hq]. */
+int oracle_decode_attention(int dt, int64_t num_blocks, int P, int Hkv, int d,
+                            const void* kpool, const void* vpool, const void* q,
+                            int B, int Hq, const int32_t* block_table, int max_blocks,
+                            const int32_t* context_lens, double scale,
+                            int window, int sinks, const int32_t* page_list, int pps,
+                            double* out, double* lse) {
+    if (!common_args_ok(dt, num_blocks, P, Hkv, d, B, Hq, max_blocks, window, sinks,
+                        page_list, pps))
+        return ORC_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        int L = context_lens[b];
+        if (L < 0) return ORC_ERR_PRECONDITION;
+        const int32_t* pages = page_list ? page_list + (size_t)b * pps : NULL;
+        if (pages && !pages_ok(pages, pps)) return ORC_ERR_PRECONDITION;
+        double* logits = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+        if (!logits || !toks) { free(logits); free(toks); return ORC_ERR_NOMEM; }
+        for (int h = 0; h < Hq; ++h) {
+            double* o = out + ((size_t)b * Hq + h) * d;
+            int64_t cnt = gather_logits(dt, num_blocks, P, Hkv, d, kpool, q, Hq, b, h,
+                                        block_table + (size_t)b * max_blocks, max_blocks, L,
+                                        scale, window, sinks, pages, pps, logits, toks);
+            if (cnt < 0) { free(logits); free(toks); return ORC_ERR_PRECONDITION; }
+            for (int x = 0; x < d; ++x) o[x] = 0.0;
+            if (cnt == 0) { lse[(size_t)b * Hq + h] = -INFINITY; continue; }
+            double m = logits[0];
+            for (int64_t k = 1; k < cnt; ++k) if (logits[k] > m) m = logits[k];
+            double z = 0.0;
+            for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);
+            int kvh = h / G;
+            for (int64_t k = 0; k < cnt; ++k) {
+                double w = exp(logits[k] - m);
+                int64_t t = toks[k];
+                int64_t blk = block_table[(size_t)b * max_blocks + t / P];
+                for (int x = 0; x < d; ++x)
+                    o[x] += w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);
+            }
+            for (int x = 0; x < d; ++x) o[x] /= z;
+            lse[(size_t)b * Hq + h] = m + log(z);
+        }
+        free(logits);
+        free(toks);
+    }
+    return ORC_OK;
+}
+
+/* Split partials and their log-sum-exp combination ([Novita] §關鍵技術 2: a
+ * partition's running max and sum l are enough to merge it with others).
+ * The attended tokens of (b, h), grouped by aligned 16-token unit (t / 16) in
+ * ascending order, are cut into partitions of `units` consecutive units;
+ * partition s gets m_s, l_s and the unnormalised o_s. Writes the partials
+ * (o_part [B][Hq][S][d], m_part/l_part [B][Hq][S]; empty partitions: m = -inf,
+ * l = 0, o = 0) when the pointers are non-NULL, and always the combined
+ * out/lse. S = max_splits; more partitions than that is an argument error. */
+int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, int d,
+                                  const void* kpool, const void* vpool, const void* q,
+                                  int B, int Hq, const int32_t* block_table, int max_blocks,
+                                  const int32_t* context_lens, double scale,
+                                  int window, int sinks, const int32_t* page_list, int pps,
+                                  int units, int max_splits,
+                                  double* o_part, double* m_part, double* l_part,
+                                  double* out, double* lse) {
+    if (!common_args_ok(dt, num_blocks, P, Hkv, d, B, Hq, max_blocks, window, sinks,
+                        page_list, pps) || units <= 0 || max_splits <= 0)
+        return ORC_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    int G = Hq / Hkv;
+    double* po = (double*)calloc((size_t)max_splits * d, sizeof(double));
+    double* pm = (double*)malloc(sizeof(double) * (size_t)max_splits);
+    double* pl = (double*)malloc(sizeof(double) * (size_t)max_splits);
+    if (!po || !pm || !pl) { free(po); free(pm); free(pl); return ORC_ERR_NOMEM; }
+    int rc = ORC_OK;
+    for (int b = 0; b < B && rc == ORC_OK; ++b) {
+        int L = context_lens[b];
+        const int32_t* pages = page_list ? page_list + (size_t)b * pps : NULL;
+        if (L < 0 || (pages && !pages_ok(pages, pps))) { rc = ORC_ERR_PRECONDITION; break; }
+        double* logits = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+        if (!logits || !toks) { free(logits); free(toks); rc = ORC_ERR_NOMEM; break; }
+        for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
+            int64_t cnt = gather_logits(dt, num_blocks, P, Hkv, d, kpool, q, Hq, b, h,
+                                        block_table + (size_t)b * max_blocks, max_blocks, L,
+                                        scale, window, sinks, pages, pps, logits, toks);
+            if (cnt < 0) { rc = ORC_ERR_PRECONDITION; break; }
+            for (int s = 0; s < max_splits; ++s) { pm[s] = -INFINITY; pl[s] = 0.0; }
+            memset(po, 0, sizeof(double) * (size_t)max_splits * d);
+            /* Assign each attended token to its partition: unit rank / units. */
+            int64_t unit_rank = -1, last_unit = -1;
+            int kvh = h / G;
+            /* First pass: maxima per partition. */
+            for (int64_t k = 0; k < cnt; ++k) {
+                int64_t u = toks[k] / 16;
+                if (u != last_unit) { ++unit_rank; last_unit = u; }
+                int64_t s = unit_rank / units;
+                if (s >= max_splits) { rc = ORC_ERR_ARG; break; }
+                if (logits[k] > pm[s]) pm[s] = logits[k];
+            }
+            if (rc != ORC_OK) break;
+            /* Second pass: sums per partition. */
+            unit_rank = -1; last_unit = -1;
+            for (int64_t k = 0; k < cnt; ++k) {
+                int64_t u = toks[k] / 16;
+                if (u != last_unit) { ++unit_rank; last_unit = u; }
+                int64_t s = unit_rank / units;
+                double w = exp(logits[k] - pm[s]);
+                pl[s] += w;
+                int64_t t = toks[k];
+                int64_t blk = block_table[(size_t)b * max_blocks + t / P];
+                for (int x = 0; x < d; ++x)
+                    po[(size_t)s * d + x] +=
+                        w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);
+            }
+            size_t bh = (size_t)b * Hq + h;
+            if (o_part) memcpy(o_part + bh * max_splits * d, po, sizeof(double) * (size_t)max_splits * d);
+            if (m_part) memcpy(m_part + bh * max_splits, pm, sizeof(double) * (size_t)max_splits);
+            if (l_part) memcpy(l_part + bh * max_splits, pl, sizeof(double) * (size_t)max_splits);
+            /* Combine: M = max over non-empty partitions; weights exp(m_s - M). */
+            double M = -INFINITY;
+            for (int s = 0; s < max_splits; ++s) if (pl[s] > 0.0 && pm[s] > M) M = pm[s];
+            double* o = out + bh * d;
+            for (int x = 0; x < d; ++x) o[x] = 0.0;
+            if (M == -INFINITY) { lse[bh] = -INFINITY; continue; }
+            double z = 0.0;
+            for (int s = 0; s < max_splits; ++s) {
+                if (!(pl[s] > 0.0)) continue;
+                double w = exp(pm[s] - M);
+                z += w * pl[s];
+                for (int x = 0; x < d; ++x) o[x] += w * po[(size_t)s * d + x];
+            }
+            for (int x = 0; x < d; ++x) o[x] /= z;
+            lse[bh] = M + log(z);
+        }
+        free(logits);
+        free(toks);
+    }
+    free(po); free(pm); free(pl);
+    return rc;
+}
+
+/* Brute force on a contiguous cache: no pool, no block table, no layout.
+ * K_log / V_log: [B][Lmax][Hkv][d] logical rows (as a contiguous per-sequence
+ * cache would hold them). The token set is built as an explicit list of ranges,
+ * and the softmax is the textbook two-pass form in long double. */
+int oracle_bruteforce(int dt, const void* K_log, const void* V_log, int Lmax,
+                      const void* q, int B, int Hq, int Hkv, int d,
+                      const int32_t* context_lens, double scale, int P,
+                      int window, int sinks, const int32_t* page_list, int pps,
+                      long double* out, long double* lse) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || Lmax < 0) return ORC_ERR_ARG;
+    if (dt != ORC_F32 && dt != ORC_F16 && dt != ORC_BF16) return ORC_ERR_ARG;
+    if (page_list && (P <= 0 || pps <= 0)) return ORC_ERR_ARG;
+    long double sc = scale > 0.0 ? (long double)scale : 1.0L / sqrtl((long double)d);
+    int G = Hq / Hkv;
+    int* idx = (int*)malloc(sizeof(int) * (size_t)(Lmax > 0 ? Lmax : 1));
+    long double* lg = (long double*)malloc(sizeof(long double) * (size_t)(Lmax > 0 ? Lmax : 1));
+    if (!idx || !lg) { free(idx); free(lg); return ORC_ERR_NOMEM; }
+    for (int b = 0; b < B; ++b) {
+        int L = context_lens[b];
+        if (L < 0 || L > Lmax) { free(idx); free(lg); return ORC_ERR_PRECONDITION; }
+        int n = 0;
+        if (page_list) {
+            for (int k = 0; k < pps; ++k) {
+                int p = page_list[(size_t)b * pps + k];
+                if (p < 0) continue;
+                for (int t = p * P; t < (p + 1) * P && t < L; ++t) idx[n++] = t;
+            }
+        } else if (window > 0 && window < L) {
+            int s_end = sinks < L ? sinks : L;
+            int w_begin = L - window > s_end ? L - window : s_end;
+            for (int t = 0; t < s_end; ++t) idx[n++] = t;
+            for (int t = w_begin; t < L; ++t) idx[n++] = t;
+        } else {
+            for (int t = 0; t < L; ++t) idx[n++] = t;
+        }
+        for (int h = 0; h < Hq; ++h) {
+            int kvh = h / G;
+            long double* o = out + ((size_t)b * Hq + h) * d;
+            for (int x = 0; x < d; ++x) o[x] = 0.0L;
+            if (n == 0) { lse[(size_t)b * Hq + h] = -INFINITY; continue; }
+            for (int k = 0; k < n; ++k) {
+                long double acc = 0.0L;
+                for (int x = 0; x < d; ++x)
+                    acc += (long double)load_elem(q, ((size_t)b * Hq + h) * d + x, dt) *
+                           (long double)load_elem(K_log, (((size_t)b * Lmax + idx[k]) * Hkv + kvh) * d + x, dt);
+                lg[k] = acc * sc;
+            }
+            long double m = lg[0];
+            for (int k = 1; k < n; ++k) m = lg[k] > m ? lg[k] : m;
+            long double z = 0.0L;
+            for (int k = 0; k < n; ++k) z += expl(lg[k] - m);
+            for (int k = 0; k < n; ++k) {
+                long double p = expl(lg[k] - m) / z;
+                for (int x = 0; x < d; ++x)
+                    o[x] += p * (long double)load_elem(V_log, (((size_t)b * Lmax + idx[k]) * Hkv + kvh) * d + x, dt);
+            }
+            lse[(size_t)b * Hq + h] = m + logl(z);
+        }
+    }
+    free(idx);
+    free(lg);
+    return ORC_OK;
+}
+
+/* KV-cache size ([primer] §3.1): 2 (K and V) x batch x layers x heads x head_dim
+ * x seq_len x bytes per element; with block_size > 0 the sequence occupies whole
+ * blocks, so seq_len is rounded up to a multiple of block_size. */
+uint64_t oracle_kv_cache_bytes(int64_t batch, int64_t layers, int64_t heads, int64_t head_dim,
+                               int64_t seq_len, int64_t dtype_bytes, int64_t block_size) {
+    if (batch < 0 || layers < 0 || heads < 0 || head_dim < 0 || seq_len < 0 || dtype_bytes < 0)
+        return 0;
+    uint64_t seq = (uint64_t)seq_len;
+    if (block_size > 0) seq = (seq + (uint64_t)block_size - 1) / (uint64_t)block_size * (uint64_t)block_size;
+    return 2ull * (uint64_t)batch * (uint64_t)layers * (uint64_t)heads * (uint64_t)head_dim * seq *
+           (uint64_t)dtype_bytes;
+}

@@ -1,0 +1,343 @@
+"""Pins that tie the CPU oracle to facts fixed outside itself.
+
+Each pin takes an ``oracle.Oracle`` instance and raises AssertionError (or lets an
+OracleError through) when the oracle disagrees with what the pages or the
+mathematics fix: the primer's worked KV-size values, hand-computed layout
+positions, closed forms of softmax attention, invariances, and a brute-force
+contiguous-cache evaluation in long double. The same pins run against mutated
+copies of the oracle (test_oracle_pins.py) to show that each plausible mistake is
+caught by at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import os
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NAN_BITS = {"f32": np.float32(np.nan), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+TOL = 1e-12
+
+
+def _raw_dtype(dtype):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact decode of a CPU tensor of any cache dtype (torch's own conversion)."""
+    return t.to(torch.float64).numpy()
+
+
+def build(o, seed, *, B, Hq, Hkv, d, dtype, P, lens, spare=1, q=None, K=None, V=None,
+          table_seed=None):
+    """A paged problem: logical K/V rows appended through the oracle into NaN-filled pools."""
+    lens = [int(x) for x in lens]
+    Lmax = max(lens + [1])
+    q = synth.normal((B, Hq, d), seed, "q", dtype=dtype) if q is None else q
+    K = synth.normal((B, Lmax, Hkv, d), seed, "k", dtype=dtype) if K is None else K
+    V = synth.normal((B, Lmax, Hkv, d), seed, "v", dtype=dtype) if V is None else V
+    bt, nb = synth.block_tables(lens, P, seed if table_seed is None else table_seed,
+                                spare_blocks=spare)
+    n_el = nb * Hkv * P * d
+    kpool = np.full(n_el, NAN_BITS[dtype], dtype=_raw_dtype(dtype))
+    vpool = np.full(n_el, NAN_BITS[dtype], dtype=_raw_dtype(dtype))
+    slots = synth.token_slots(bt, lens, P)
+    k_new = torch.cat([K[b, :L] for b, L in enumerate(lens)]) if lens else K[:0, 0]
+    v_new = torch.cat([V[b, :L] for b, L in enumerate(lens)]) if lens else V[:0, 0]
+    o.kv_append(dtype, kpool, vpool, synth.raw_numpy(k_new), synth.raw_numpy(v_new),
+                slots.numpy(), P=P, Hkv=Hkv, d=d)
+    return SimpleNamespace(q=q, K=K, V=V, bt=bt, nb=nb, lens=lens, kpool=kpool, vpool=vpool,
+                           P=P, Hkv=Hkv, Hq=Hq, d=d, dtype=dtype, B=B, slots=slots)
+
+
+def attend(o, pr, **kw):
+    return o.decode_attention(pr.dtype, pr.kpool, pr.vpool, synth.raw_numpy(pr.q), pr.bt.numpy(),
+                              np.array(pr.lens, np.int32), P=pr.P, Hkv=pr.Hkv, d=pr.d, **kw)
+
+
+def brute(o, pr, **kw):
+    return o.bruteforce(pr.dtype, synth.raw_numpy(pr.K), synth.raw_numpy(pr.V),
+                        synth.raw_numpy(pr.q), np.array(pr.lens, np.int32), Hkv=pr.Hkv, d=pr.d,
+                        P=pr.P, **kw)
+
+
+# ---------------------------------------------------------------------------------------
+def pin_kv_bytes(o):
+    """The primer's worked KV-size values (§3.2, §3.3, §5.3), exact."""
+    with open(os.path.join(GOLDEN, "kv_cache_bytes.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        got = o.kv_cache_bytes(c["batch"], c["layers"], c["heads"], c["head_dim"], c["seq_len"],
+                               c["dtype_bytes"])
+        assert got == c["bytes"], (c["where"], got, c["bytes"])
+    # Paged allocation rounds the sequence up to whole blocks: 4001 tokens -> 251 blocks of 16.
+    assert o.kv_cache_bytes(1, 1, 8, 128, 4001, 2, 16) == 2 * 8 * 128 * 4016 * 2
+    assert o.kv_cache_bytes(1, 1, 8, 128, 4096, 2, 16) == 2 * 8 * 128 * 4096 * 2
+
+
+def pin_layout_golden(o):
+    """Hand-computed element positions of the documented cache layout."""
+    with open(os.path.join(GOLDEN, "layout_positions.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        args = (c["blk"], c["h"], c["t"], c["x"], c["Hkv"], c["P"], c["d"], c["dtype"])
+        assert o.k_index(*args) == c["k"], ("K", c)
+        assert o.v_index(*args) == c["v"], ("V", c)
+
+
+def pin_layout_bijection(o):
+    """Each tile of the layout is a permutation of its P*d element slots."""
+    for dtype in ("f32", "f16", "bf16"):
+        for d in (64, 128):
+            for P in (16, 32):
+                base = (1 * 2 + 1) * P * d  # block 1, head 1 of 2
+                for fn in (o.k_index, o.v_index):
+                    pos = [fn(1, 1, t, x, 2, P, d, dtype) - base
+                           for t in range(P) for x in range(d)]
+                    assert sorted(pos) == list(range(P * d)), (fn.__name__, dtype, d, P)
+
+
+def pin_append_roundtrip(o):
+    """Appended rows read back at their slots; every other slot keeps its NaN canary."""
+    for dtype, d, P in (("bf16", 128, 16), ("f16", 128, 32), ("f32", 64, 16)):
+        pr = build(o, 11, B=2, Hq=2, Hkv=2, d=d, dtype=dtype, P=P, lens=[37, 16], spare=2)
+        K, V = synth.raw_numpy(pr.K), synth.raw_numpy(pr.V)
+        written = np.zeros(pr.kpool.size, bool)
+        for b, L in enumerate(pr.lens):
+            for t in range(L):
+                blk = int(pr.bt[b, t // P])
+                for h in range(pr.Hkv):
+                    for x in range(0, d, 7):
+                        ki = o.k_index(blk, h, t % P, x, pr.Hkv, P, d, dtype)
+                        vi = o.v_index(blk, h, t % P, x, pr.Hkv, P, d, dtype)
+                        assert pr.kpool[ki].tobytes() == K[b, t, h, x].tobytes()
+                        assert pr.vpool[vi].tobytes() == V[b, t, h, x].tobytes()
+                    for x in range(d):
+                        written[o.k_index(blk, h, t % P, x, pr.Hkv, P, d, dtype)] = True
+        canary = NAN_BITS[dtype].tobytes()
+        untouched = pr.kpool[~written]
+        assert untouched.size > 0
+        assert all(u.tobytes() == canary for u in untouched[:: max(1, untouched.size // 97)])
+        # a skipped slot (negative) writes nothing
+        before = pr.kpool.copy()
+        o.kv_append(dtype, pr.kpool, pr.vpool, synth.raw_numpy(pr.K[0, :1]),
+                    synth.raw_numpy(pr.V[0, :1]), np.array([-1], np.int32), P=P, Hkv=pr.Hkv, d=d)
+        assert np.array_equal(before.view(np.uint8), pr.kpool.view(np.uint8))
+
+
+def pin_bruteforce(o):
+    """Main oracle == long-double brute force on a contiguous cache, all modes, tiny shapes."""
+    rng = np.random.default_rng(5)
+    for case in range(18):
+        dtype = ("f32", "f16", "bf16")[case % 3]
+        d = (64, 128)[(case // 3) % 2]
+        P = (16, 32)[case % 2]
+        G = (1, 2, 3)[case % 3]
+        Hkv = 1 + case % 2
+        B = 1 + case % 3
+        lens = [int(x) for x in rng.integers(1, 41, size=B)]
+        pr = build(o, 100 + case, B=B, Hq=G * Hkv, Hkv=Hkv, d=d, dtype=dtype, P=P, lens=lens)
+        modes = [dict(), dict(window=int(rng.integers(1, 20)), sinks=int(rng.integers(0, 6)))]
+        pl = np.full((B, 3), -1, np.int32)
+        for b, L in enumerate(lens):
+            npg = (L + P - 1) // P
+            pick = sorted(rng.choice(npg, size=min(2, npg), replace=False).tolist())
+            pl[b, :len(pick)] = pick
+        modes.append(dict(page_list=pl))
+        for kw in modes:
+            out, lse = attend(o, pr, **kw)
+            bo, bl = brute(o, pr, **kw)
+            assert np.abs(out - bo.astype(np.float64)).max() <= TOL, (case, kw)
+            assert np.abs(lse - bl.astype(np.float64)).max() <= TOL, (case, kw)
+
+
+def pin_permutation(o):
+    """Placing the same logical pages in other physical blocks changes nothing (bitwise)."""
+    for dtype in ("bf16", "f32"):
+        kw = dict(B=2, Hq=4, Hkv=2, d=64, dtype=dtype, P=16, lens=[256, 77])
+        a = build(o, 7, table_seed=1, **kw)
+        b = build(o, 7, table_seed=2, spare=5, **kw)
+        assert not np.array_equal(a.bt.numpy(), b.bt.numpy())
+        for mode in (dict(), dict(window=40, sinks=3)):
+            oa, la = attend(o, a, **mode)
+            ob, lb = attend(o, b, **mode)
+            assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def pin_window_reductions(o):
+    """W >= L and W + S >= L are full attention (bitwise); W = 1, S = s attends {0..s-1, L-1}."""
+    pr = build(o, 21, B=2, Hq=2, Hkv=1, d=64, dtype="bf16", P=16, lens=[40, 19])
+    full, fl = attend(o, pr)
+    for w, s in ((40, 0), (100, 2), (30, 10), (21, 19), (1, 40)):
+        out, lse = attend(o, pr, window=w, sinks=s)
+        assert np.array_equal(out, full) and np.array_equal(lse, fl), (w, s)
+    # W = 1, S = 3 on L = 40: exactly tokens 0, 1, 2 and 39
+    keep = [0, 1, 2, 39]
+    sub = build(o, 0, B=1, Hq=2, Hkv=1, d=64, dtype="bf16", P=16, lens=[4],
+                q=pr.q[:1], K=pr.K[:1, keep], V=pr.V[:1, keep])
+    so, sl = attend(o, sub)
+    out, lse = attend(o, pr, window=1, sinks=3)
+    assert np.abs(out[0] - so[0]).max() <= TOL and np.abs(lse[0] - sl[0]).max() <= TOL
+    # and W = 8, S = 0 on L = 40 is tokens 32..39
+    sub = build(o, 0, B=1, Hq=2, Hkv=1, d=64, dtype="bf16", P=16, lens=[8],
+                q=pr.q[:1], K=pr.K[:1, 32:40], V=pr.V[:1, 32:40])
+    so, _ = attend(o, sub)
+    out, _ = attend(o, pr, window=8, sinks=0)
+    assert np.abs(out[0] - so[0]).max() <= TOL
+
+
+def pin_identical_keys(o):
+    """All keys equal -> every weight equal -> the output is the mean of V over the attended set."""
+    B, Hkv, d, L = 1, 1, 64, 45
+    K = synth.normal((1, 1, Hkv, d), 3, "k", dtype="bf16").expand(B, L, Hkv, d).contiguous()
+    V = synth.normal((B, L, Hkv, d), 3, "v", dtype="bf16")
+    pr = build(o, 3, B=B, Hq=2, Hkv=Hkv, d=d, dtype="bf16", P=16, lens=[L], K=K, V=V)
+    Vd = to_f64(V)[0, :, 0]
+    for kw, toks in ((dict(), range(L)),
+                     (dict(window=10, sinks=2), [0, 1] + list(range(35, 45))),
+                     (dict(page_list=np.array([[0, 2]], np.int32)), list(range(16)) + list(range(32, 45)))):
+        out, _ = attend(o, pr, **kw)
+        ref = Vd[list(toks)].mean(axis=0)
+        assert np.abs(out[0, 0] - ref).max() <= TOL and np.abs(out[0, 1] - ref).max() <= TOL, kw
+
+
+def pin_identical_values(o):
+    """All value rows equal to v -> the output is v whatever the weights."""
+    B, Hkv, d, L = 2, 2, 128, 33
+    V = synth.normal((1, 1, Hkv, d), 4, "v", dtype="f16").expand(B, L, Hkv, d).contiguous()
+    pr = build(o, 4, B=B, Hq=4, Hkv=Hkv, d=d, dtype="f16", P=32, lens=[L, 5], V=V)
+    out, _ = attend(o, pr)
+    Vd = to_f64(V)[0, 0]
+    for b in range(B):
+        for h in range(4):
+            assert np.abs(out[b, h] - Vd[h // 2]).max() <= TOL
+
+
+def pin_small_closed_forms(o):
+    """L = 1: out = v0, lse = s0. L = 2: out = v0 + sigmoid(s1 - s0)(v1 - v0), lse = logaddexp."""
+    for dtype in ("f32", "f16", "bf16"):
+        d = 64
+        pr = build(o, 9, B=2, Hq=1, Hkv=1, d=d, dtype=dtype, P=16, lens=[1, 2])
+        out, lse = attend(o, pr)
+        q = to_f64(pr.q)
+        K, V = to_f64(pr.K), to_f64(pr.V)
+        s0 = q[0, 0] @ K[0, 0, 0] / np.sqrt(d)
+        assert np.array_equal(out[0, 0], V[0, 0, 0]), dtype
+        assert abs(lse[0, 0] - s0) <= TOL
+        s = [q[1, 0] @ K[1, t, 0] / np.sqrt(d) for t in range(2)]
+        sig = 1.0 / (1.0 + np.exp(-(s[1] - s[0])))
+        ref = V[1, 0, 0] + sig * (V[1, 1, 0] - V[1, 0, 0])
+        assert np.abs(out[1, 0] - ref).max() <= TOL, dtype
+        assert abs(lse[1, 0] - np.logaddexp(s[0], s[1])) <= TOL
+        # an explicit scale is used as given; 0 selects 1/sqrt(d)
+        o2, _ = attend(o, pr, scale=1.0 / np.sqrt(d))
+        assert np.array_equal(o2, out)
+        o3, l3 = attend(o, pr, scale=0.5)
+        s = [q[1, 0] @ K[1, t, 0] * 0.5 for t in range(2)]
+        assert abs(l3[1, 0] - np.logaddexp(s[0], s[1])) <= TOL
+
+
+def pin_peaked(o):
+    """Logits hundreds apart: the result is the top key's value, finite (max-shifted softmax)."""
+    d, L = 64, 20
+    K = synth.normal((1, L, 1, d), 8, "k", dtype="f32")
+    q = (K[0, 13, 0] * 200.0).reshape(1, 1, d).contiguous()  # s_13 ~ 1600, the rest ~ +-200
+    pr = build(o, 8, B=1, Hq=1, Hkv=1, d=d, dtype="f32", P=16, lens=[L], q=q, K=K)
+    out, lse = attend(o, pr)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert np.abs(out[0, 0] - to_f64(pr.V)[0, 13, 0]).max() <= TOL
+
+
+def pin_key_shift(o):
+    """Adding one vector u to every key shifts all logits equally: the output is unchanged."""
+    d, L = 64, 30
+    g = torch.Generator().manual_seed(1)
+    K = (torch.randint(-64, 64, (1, L, 1, d), generator=g).float() / 32.0)
+    u = (torch.randint(-64, 64, (1, 1, 1, d), generator=g).float() / 32.0)
+    q = (torch.randint(-64, 64, (1, 2, d), generator=g).float() / 64.0)
+    a = build(o, 2, B=1, Hq=2, Hkv=1, d=d, dtype="f32", P=16, lens=[L], q=q, K=K)
+    b = build(o, 2, B=1, Hq=2, Hkv=1, d=d, dtype="f32", P=16, lens=[L], q=q, K=K + u)
+    oa, la = attend(o, a)
+    ob, lb = attend(o, b)
+    assert np.abs(oa - ob).max() <= TOL
+    shift = to_f64(q[0]) @ to_f64(u)[0, 0, 0] / np.sqrt(d)
+    assert np.abs((lb - la)[0] - shift).max() <= TOL
+
+
+def pin_gqa_grouping(o):
+    """Query head h reads kv head h // G (contiguous groups): V of kv head g is constant g+1."""
+    Hkv, G, d, L = 3, 2, 64, 18
+    V = torch.stack([torch.full((L, d), float(g + 1)) for g in range(Hkv)], dim=1)[None]
+    pr = build(o, 6, B=1, Hq=Hkv * G, Hkv=Hkv, d=d, dtype="f32", P=16, lens=[L], V=V)
+    out, _ = attend(o, pr)
+    for h in range(Hkv * G):
+        assert np.abs(out[0, h] - (h // G + 1)).max() <= TOL, h
+
+
+def pin_page_list_reductions(o):
+    """All pages == full (bitwise); the last k pages with L % P == 0 == window k*P, no sinks."""
+    for P in (16, 32):
+        L = 4 * P
+        pr = build(o, 12, B=1, Hq=2, Hkv=1, d=128, dtype="bf16", P=P, lens=[L])
+        full, fl = attend(o, pr)
+        pa, la = attend(o, pr, page_list=np.array([[0, 1, 2, 3]], np.int32))
+        assert np.array_equal(pa, full) and np.array_equal(la, fl)
+        pa, _ = attend(o, pr, page_list=np.array([[-1, 2, 3, -1]], np.int32))
+        wa, _ = attend(o, pr, window=2 * P, sinks=0)
+        assert np.array_equal(pa, wa)
+        # pages at or beyond the context contribute nothing
+        pb, _ = attend(o, pr, page_list=np.array([[2, 3, 7, 9]], np.int32))
+        assert np.array_equal(pb, wa)
+
+
+def pin_split_combine(o):
+    """Split partials merged by log-sum-exp equal the direct result; partials are consistent."""
+    pr = build(o, 13, B=3, Hq=4, Hkv=2, d=64, dtype="bf16", P=16, lens=[130, 1, 64])
+    for kw in (dict(), dict(window=50, sinks=4),
+               dict(page_list=np.array([[0, 3, 8], [0, -1, -1], [1, 2, -1]], np.int32))):
+        direct, dl = attend(o, pr, **kw)
+        for units in (1, 2, 3, 16):
+            op, mp, lp, out, lse = o.decode_attention_split(
+                pr.dtype, pr.kpool, pr.vpool, synth.raw_numpy(pr.q), pr.bt.numpy(),
+                np.array(pr.lens, np.int32), P=16, Hkv=2, d=64, units=units, max_splits=9, **kw)
+            assert np.abs(out - direct).max() <= TOL and np.abs(lse - dl).max() <= TOL
+            # each partition's own softmax mass, weighted back by the global lse, sums to 1
+            live = lp > 0
+            mass = np.where(live, lp * np.exp(np.where(live, mp, 0.0) - dl[..., None]), 0.0)
+            assert np.abs(mass.sum(-1) - 1.0).max() <= 1e-12
+            assert np.all(np.isneginf(mp[~live]))
+
+
+def pin_empty(o):
+    pr = build(o, 14, B=2, Hq=2, Hkv=1, d=64, dtype="f16", P=16, lens=[0, 3])
+    out, lse = attend(o, pr)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0])) and np.isfinite(lse[1]).all()
+
+
+PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundtrip,
+        pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
+        pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
+        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_empty]
+
+
+if __name__ == "__main__":
+    # Runs every pin against the oracle build given on the command line; prints the names
+    # of the failing pins and exits 1 if any failed (used for planted-mistake builds).
+    import sys
+
+    import oracle as _oracle
+
+    o = _oracle.Oracle(sys.argv[1])
+    failed = []
+    for pin in PINS:
+        try:
+            pin(o)
+        except (AssertionError, _oracle.OracleError):
+            failed.append(pin.__name__)
+    print(" ".join(failed))
+    sys.exit(1 if failed else 0)

@@ -1,0 +1,59 @@
+"""CPU tests: the oracle against its pins, and mutated oracles against the same pins."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+# Plausible mistakes, each planted into a copy of oracle.c: (name, original text, mutated text).
+MUTATIONS = [
+    ("scale dropped", "logits[cnt] = scale * dot;", "logits[cnt] = dot;"),
+    ("lse sign", "lse[(size_t)b * Hq + h] = m + log(z);", "lse[(size_t)b * Hq + h] = m - log(z);"),
+    ("gqa interleaved", "int kvh = h / G;\n    int64_t cnt = 0;", "int kvh = h % Hkv;\n    int64_t cnt = 0;"),
+    ("window off by one", "return t < sinks || t >= L - window;", "return t < sinks || t > L - window;"),
+    ("sinks ignored", "return t < sinks || t >= L - window;", "return t >= L - window;"),
+    ("K chunk strides swapped", "(size_t)(x / (4 * E)) * 64 + (size_t)((x / E) % 4) * 16 + tau",
+     "(size_t)(x / (4 * E)) * 16 + (size_t)((x / E) % 4) * 64 + tau"),
+    ("V token split transposed", "int n = x / 16, c = x % 16, j = tau / 4, i = tau % 4;",
+     "int n = x / 16, c = x % 16, j = tau % 4, i = tau / 4;"),
+    ("V read from K pool", "o[x] += w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);",
+     "o[x] += w * load_elem(kpool, k_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);"),
+    ("normaliser not shifted", "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);",
+     "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k]);"),
+    ("block index uses offset", "int64_t blk = bt_row[t / P];", "int64_t blk = bt_row[t % P];"),
+    ("combine weight inverted", "double w = exp(pm[s] - M);", "double w = exp(M - pm[s]);"),
+    ("fp16 exponent bias", "v = ldexp((double)(f | 0x400), e - 25);", "v = ldexp((double)(f | 0x400), e - 24);"),
+    ("bf16 wrong half", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("KV formula missing K/V factor", "return 2ull * (uint64_t)batch", "return 1ull * (uint64_t)batch"),
+    ("page test uses offset", "if (pages[k] >= 0 && pages[k] == t / P) return 1;",
+     "if (pages[k] >= 0 && pages[k] == t % P) return 1;"),
+    ("min instead of max", "for (int64_t k = 1; k < cnt; ++k) if (logits[k] > m) m = logits[k];",
+     "for (int64_t k = 1; k < cnt; ++k) if (logits[k] < m) m = logits[k];"),
+    ("append skips last head", "for (int h = 0; h < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src",
+     "for (int h = 0; h + 1 < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src"),
+    ("paged rounding dropped", "if (block_size > 0) seq =", "if (block_size < 0) seq ="),
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(oracle.default())
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, orig, mut):
+    src = open(oracle.SOURCE).read()
+    assert src.count(orig) >= 1, f"mutation anchor not found: {name}"
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(src.replace(orig, mut))
+    so = oracle.compile_oracle(str(path), str(tmp_path / "liboracle_mut.so"))
+    # A mutated oracle may write out of bounds, so its pins run in a child process; a crash
+    # there also counts as the mistake being caught.
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([os.path.dirname(here), here]))
+    r = subprocess.run([sys.executable, os.path.join(here, "oracle_pins.py"), so], env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"no pin catches the planted mistake: {name}"
