@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode path on one MI355X.
+
+Default workload: one Llama-3-8B-shaped attention layer at decode time — batch 32,
+32 query / 8 kv heads (GQA 4), head_dim 128, bf16 cache, 16-token blocks, context
+lengths drawn uniformly from [1024, 4096], random block tables. One step is the whole
+hot path over one batch: the append of the 32 new tokens (kv_cache_append), the split-K
+attention kernel and the log-sum-exp combine (exactly the two kernels
+paged_decode_attention launches). Several replica caches (own pools, tables, queries)
+are cycled so that consecutive steps never find their K/V in the 256 MB last-level
+cache; every replica has the same context lengths, so the bytes per step are fixed.
+
+Prints one JSON line. value = algorithmic KV bytes per step (the attended tokens' K and
+V rows, sum(L) * 2 * Hkv * d * 2 bytes) / wall time per step. roofline = the split
+kernel alone: the same bytes / its mean duration from HIP events recorded on the
+launch stream around every timed launch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode-attention KV GB/s and % of HBM peak; decode steps/s per layer"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama3_8b_layer_bf16")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--split-tokens", type=int, default=0, help="0 = the library's automatic plan")
+    ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
+                    help="sequences of replica 0 the oracle runs for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+def build_replica(w, lens, seed, r, dev):
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
+    tdt = synth.TORCH_DTYPE[w.dtype]
+    bt, nb = synth.block_tables(lens, P, seed, w.name, r)
+    gk = torch.empty((nb, Hkv, P, d), dtype=tdt, device=dev)
+    gv = torch.empty_like(gk)
+    for b, L in enumerate(lens):  # prefill: tokens [0, L-1) of every sequence
+        if L > 1:
+            kb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "k", dtype=w.dtype, device=dev)
+            vb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "v", dtype=w.dtype, device=dev)
+            sl = synth.token_slots(bt[b:b + 1], [L - 1], P).to(dev)
+            pkv.kv_cache_append(gk, gv, kb, vb, sl)
+    rep = dict(
+        k=gk, v=gv, bt=bt.to(dev),
+        cl=torch.tensor(lens, dtype=torch.int32, device=dev),
+        q=synth.normal((B, Hq, d), seed, w.name, r, "q", dtype=w.dtype, device=dev),
+        k_new=synth.normal((B, Hkv, d), seed, w.name, r, "knew", dtype=w.dtype, device=dev),
+        v_new=synth.normal((B, Hkv, d), seed, w.name, r, "vnew", dtype=w.dtype, device=dev),
+        slots=torch.tensor([synth.slot_of(bt, b, L - 1, P) for b, L in enumerate(lens)],
+                           dtype=torch.int32, device=dev),
+        bt_cpu=bt,
+    )
+    return rep
+
+
+def cpu_baseline(w, lens, seed, reps, nseq, dev):
+    """Times the oracle, as it is, on the first `nseq` sequences of replica 0."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    P, d, Hkv, Hq = w.block_size, w.head_dim, w.kv_heads, w.q_heads
+    rep = reps[0]
+    total_s, total_bytes, total_tokens = 0.0, 0, 0
+    for b in range(min(nseq, len(lens))):
+        L = lens[b]
+        kb = synth.normal((L - 1, Hkv, d), seed, w.name, 0, b, "k", dtype=w.dtype, device=dev)
+        vb = synth.normal((L - 1, Hkv, d), seed, w.name, 0, b, "v", dtype=w.dtype, device=dev)
+        kb = torch.cat([kb, rep["k_new"][b:b + 1]]).cpu()
+        vb = torch.cat([vb, rep["v_new"][b:b + 1]]).cpu()
+        bt, nb = synth.block_tables([L], P, seed, "cpu", b)
+        kp = np.zeros(nb * Hkv * P * d, np.uint16)
+        vp = np.zeros_like(kp)
+        oracle.kv_append(w.dtype, kp, vp, synth.raw_numpy(kb), synth.raw_numpy(vb),
+                         synth.token_slots(bt, [L], P).numpy(), P=P, Hkv=Hkv, d=d)
+        q = synth.raw_numpy(rep["q"][b:b + 1].cpu())
+        t0 = time.perf_counter()
+        oracle.decode_attention(w.dtype, kp, vp, q, bt.numpy(), np.array([L], np.int32), P=P,
+                                Hkv=Hkv, d=d)
+        total_s += time.perf_counter() - t0
+        total_bytes += L * w.kv_bytes_per_token()
+        total_tokens += L
+    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{min(nseq, len(lens))} of {len(lens)} sequences of one replica "
+                       f"({total_tokens} tokens, full attention, all 32 heads), single-threaded "
+                       f"fp64 C oracle, {total_s:.2f} s",
+                seconds=round(total_s, 3))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU; the decode path shards by kv head or by "
+              "sequence with no exchange (see the design notes), and multi-GPU runs are not "
+              "part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1 or w.pages_per_step or w.window:
+        print(f"bench.py: workload {w.name} is a parity workload; the benchmark line is the "
+              "single-layer llama3_8b_layer_bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
+    kv_bytes = sum(lens) * w.kv_bytes_per_token()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    reps = [build_replica(w, lens, args.seed, r, dev) for r in range(args.replicas)]
+    torch.cuda.synchronize()
+    B, Hq, d = w.batch, w.q_heads, w.head_dim
+    mcl = max(lens)
+    S = pkv.num_splits(reps[0]["k"], B, mcl, split_tokens=args.split_tokens)
+    o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device=dev)
+    m_part = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    l_part = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+    def step(rep, ev=None):
+        pkv.kv_cache_append(rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"])
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_decode_attention_partial(rep["q"], rep["k"], rep["v"], rep["bt"], rep["cl"],
+                                           max_context_len=mcl, split_tokens=args.split_tokens,
+                                           o_part=o_part, m_part=m_part, l_part=l_part)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_decode_combine(o_part, m_part, l_part, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(reps[i % len(reps)], events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    kern_ms = sorted(a.elapsed_time(b) for a, b in events)
+    kern_mean = statistics.fmean(kern_ms)
+    q = lambda f: kern_ms[min(len(kern_ms) - 1, int(f * len(kern_ms)))]
+    achieved = kv_bytes / (kern_mean * 1e-3) / 1e9
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
+            "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
+            "replicas": args.replicas, "num_splits": S, "split_tokens": args.split_tokens,
+            "step": "append 32 tokens + split-K attention + LSE combine",
+            "parallelism": "single GPU",
+        },
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_split_kernel<BF16,128,full>",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
+            "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
+            "p90_us": round(q(0.9) * 1e3, 3),
+        },
+    }
+    if args.cpu_sample_seqs > 0:
+        res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_sample_seqs, dev)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -113,8 +113,9 @@ typedef struct {
     int32_t num_sinks;       /* >= 0 */
     const int32_t* page_list; /* device, nullable */
     int32_t pages_per_seq;   /* row length of page_list; > 0 when page_list != NULL */
-    int32_t split_tokens;    /* 0: automatic. Otherwise tokens per split-K partition,
-                                a positive multiple of 64 (rounded up to one). */
+    int32_t split_tokens;    /* 0: automatic (depends on batch and bounds). Otherwise the
+                                tokens per split-K partition, rounded up to a multiple of 16
+                                and clamped to [16, 4096]. */
 } pkv_decode_opts;
 
 /* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";
@@ -179,18 +180,21 @@ size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc /* host 
                                              int32_t max_context_len,
                                              const pkv_decode_opts* opts /* host, nullable */);
 
-/* Number of split-K partitions per (sequence, head) that the partial call writes
- * for these arguments (>= 1), or 0 for rejected arguments. Pure host function. */
+/* Number of split-K partitions per (sequence, head), S >= 1, that the partial call
+ * writes for these arguments (the same plan paged_decode_attention uses), or 0 for
+ * rejected arguments. Pure host function. */
 int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc /* host */,
-                                          int32_t max_context_len,
+                                          int32_t batch, int32_t max_context_len,
                                           const pkv_decode_opts* opts /* host, nullable */);
 
 /* paged_decode_attention_partial — the split-K first phase, exporting per-split
  * softmax statistics ([Novita] §關鍵技術 2: the attention kernel already holds the
- * running max and sum l and can return them). The attended token set of each
- * sequence (same rules as paged_decode_attention) is cut, in ascending token
- * order, into S = paged_decode_attention_num_splits(...) partitions; for
- * partition s of (b, h), over its tokens t:
+ * running max and sum l and can return them). Partitions: the attended tokens are
+ * grouped into aligned 16-token units t / 16 — for full and window attention the units
+ * that hold attended tokens, ascending; for a page list every 16-token quarter of every
+ * list entry in list order, padding included — and partition s of a sequence takes
+ * units [s*U, (s+1)*U), U = split size / 16, S = paged_decode_attention_num_splits(...).
+ * For partition s of (b, h), over its tokens t:
  *     m_part[b][h][s] = max_t s_t                       (natural-log units),
  *     l_part[b][h][s] = sum_t exp(s_t - m_part),
  *     o_part[b][h][s][:] = sum_t exp(s_t - m_part) V_t  (unnormalised).
@@ -199,7 +203,8 @@ int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc /* host */,
  *   o_part: [batch][num_q_heads][S][head_dim] fp32;  m_part, l_part: [batch][num_q_heads][S] fp32;
  *   num_splits: S as returned by the query (PKV_ERR_SHAPE otherwise).
  * Partial results from several calls over disjoint token sets (for example
- * different devices holding different pages) combine with paged_decode_combine. */
+ * different devices holding different pages) combine with paged_decode_combine;
+ * paged_decode_attention with S > 1 is exactly this call followed by the combine. */
 pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc /* host */,
                                           const void* k_cache, const void* v_cache,
                                           const void* q,
@@ -213,7 +218,8 @@ pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc /* host */,
                                           int32_t num_splits,
                                           void* stream);
 
-/* paged_decode_combine — cross-split log-sum-exp reduction. For each (b, h), over
+/* paged_decode_combine — cross-split log-sum-exp reduction ([Novita] §關鍵技術 2:
+ * partial softmax results merge through their max and sum). For each (b, h), over
  * the partitions s with l_part > 0:  M = max_s m_s,  w_s = exp(m_s - M),
  *     out[b][h] = sum_s w_s o_s / sum_s w_s l_s,   lse[b][h] = M + ln(sum_s w_s l_s).
  * With no such partition: out = 0, lse = -inf. Layouts as in the partial call;

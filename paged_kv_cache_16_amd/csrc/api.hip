@@ -1,0 +1,309 @@
+// api.hip — the C ABI declared in include/pagedkv.h: argument validation, split planning
+// and kernel dispatch. Validation always runs before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using namespace pkv;
+
+constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 256 CUs
+constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
+constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : 2; }
+
+bool dtype_ok(int t) { return t == PKV_F32 || t == PKV_F16 || t == PKV_BF16; }
+
+pkv_status check_desc(const pkv_cache_desc* d) {
+    if (!d) return PKV_ERR_NULL;
+    if (!dtype_ok(d->dtype)) return PKV_ERR_UNSUPPORTED;
+    if (d->num_blocks < 0 || d->num_kv_heads <= 0 || d->block_size <= 0) return PKV_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (d->block_size % 16 != 0 || d->block_size > 256) return PKV_ERR_UNSUPPORTED;
+    // the split kernel addresses sub-tiles in 16-byte units with 32-bit offsets
+    const double chunks = (double)d->num_blocks * d->num_kv_heads * d->block_size * d->head_dim *
+                          elem_bytes(d->dtype) / 16.0;
+    if (chunks > 4294967295.0) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+struct Plan {
+    int mode = kFull;
+    int units_bound = 0;  // upper bound on 16-token units per sequence
+    int units_per_split = kMinUnitsPerSplit;
+    int num_splits = 1;
+    int len_cap = 0;
+};
+
+pkv_status check_opts(const pkv_decode_opts* o) {
+    if (!o) return PKV_OK;
+    if (o->num_sinks < 0 || o->split_tokens < 0) return PKV_ERR_MODE;
+    if (o->page_list && o->window > 0) return PKV_ERR_MODE;
+    if (o->page_list && o->pages_per_seq <= 0) return PKV_ERR_MODE;
+    return PKV_OK;
+}
+
+// Split plan from host-known bounds only (never reads device data).
+Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_blocks,
+               const pkv_decode_opts* o) {
+    Plan pl;
+    const int P = d->block_size;
+    long long cap = max_context_len;
+    if (max_blocks >= 0 && (long long)max_blocks * P < cap) cap = (long long)max_blocks * P;
+    if (cap < 0) cap = 0;
+    pl.len_cap = (int)cap;
+    const int full_units = (int)((cap + 15) / 16);
+    if (o && o->page_list) {
+        pl.mode = kPages;
+        long long u = (long long)o->pages_per_seq * (P / 16);
+        pl.units_bound = (int)(u > 0x3fffffff ? 0x3fffffff : u);
+    } else if (o && o->window > 0 && o->window < cap) {
+        pl.mode = kWindow;
+        const long long sinks = o->num_sinks < cap ? o->num_sinks : cap;
+        long long u = (sinks + 15) / 16 + ((long long)o->window + 15) / 16 + 1;
+        pl.units_bound = (int)(u < full_units ? u : full_units);
+    } else {
+        pl.mode = kFull;
+        pl.units_bound = full_units;
+    }
+    int U;
+    if (o && o->split_tokens > 0) {
+        U = (o->split_tokens + 15) / 16;
+    } else {
+        const double total = (double)batch * d->num_kv_heads * pl.units_bound;
+        U = (int)ceil(total / kTargetWorkgroups);
+        U = (U + kMinUnitsPerSplit - 1) / kMinUnitsPerSplit * kMinUnitsPerSplit;
+    }
+    if (U < kMinUnitsPerSplit && !(o && o->split_tokens > 0)) U = kMinUnitsPerSplit;
+    if (U < 1) U = 1;
+    if (U > kMaxUnitsPerSplit) U = kMaxUnitsPerSplit;
+    pl.units_per_split = U;
+    pl.num_splits = pl.units_bound > 0 ? (pl.units_bound + U - 1) / U : 1;
+    return pl;
+}
+
+struct WsLayout {
+    size_t o_off, m_off, l_off, total;
+};
+
+WsLayout ws_layout(int batch, int q_heads, int splits, int head_dim) {
+    WsLayout w;
+    const size_t rows = (size_t)batch * q_heads * splits;
+    w.o_off = 0;
+    w.m_off = align_up(rows * head_dim * sizeof(float));
+    w.l_off = w.m_off + align_up(rows * sizeof(float));
+    w.total = w.l_off + align_up(rows * sizeof(float));
+    return w;
+}
+
+pkv_status check_decode_args(const pkv_cache_desc* d, const void* k, const void* v, const void* q,
+                             const int32_t* bt, int32_t max_blocks, const int32_t* cl, int32_t batch,
+                             int32_t q_heads, int32_t max_context_len, const pkv_decode_opts* o) {
+    pkv_status st = check_desc(d);
+    if (st != PKV_OK) return st;
+    if (batch < 0 || q_heads <= 0 || max_context_len < 0 || max_blocks < 0) return PKV_ERR_SHAPE;
+    if (batch > 65535) return PKV_ERR_UNSUPPORTED;
+    if (q_heads % d->num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (q_heads / d->num_kv_heads > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+    if (d->num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+    st = check_opts(o);
+    if (st != PKV_OK) return st;
+    if (batch > 0 && (!k || !v || !q || !bt || !cl)) return PKV_ERR_NULL;
+    if (batch > 0 && max_blocks == 0) return PKV_ERR_SHAPE;
+    return PKV_OK;
+}
+
+DecodeParams fill_params(const pkv_cache_desc* d, const void* k, const void* v, const void* q,
+                         const int32_t* bt, int32_t max_blocks, const int32_t* cl, int32_t q_heads,
+                         float scale, const pkv_decode_opts* o, const Plan& pl) {
+    DecodeParams p = {};
+    p.k_cache = (const char*)k;
+    p.v_cache = (const char*)v;
+    p.q = (const char*)q;
+    p.block_table = bt;
+    p.context_lens = cl;
+    p.page_list = o ? o->page_list : nullptr;
+    p.num_blocks = d->num_blocks;
+    p.block_size = d->block_size;
+    p.kv_heads = d->num_kv_heads;
+    p.q_heads = q_heads;
+    p.group = q_heads / d->num_kv_heads;
+    p.max_blocks = max_blocks;
+    p.len_cap = pl.len_cap;
+    p.window = o ? o->window : 0;
+    p.sinks = o ? o->num_sinks : 0;
+    p.pages_per_seq = o ? o->pages_per_seq : 0;
+    p.units_per_split = pl.units_per_split;
+    p.num_splits = pl.num_splits;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->head_dim);
+    p.qk_scale_log2 = sc * 1.4426950408889634f;
+    return p;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+pkv_status kv_cache_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache, const void* k_new,
+                           const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                           void* stream) {
+    pkv_status st = check_desc(desc);
+    if (st != PKV_OK) return st;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+    AppendParams p;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
+    p.block_size = desc->block_size;
+    p.kv_heads = desc->num_kv_heads;
+    p.head_dim = desc->head_dim;
+    return hip_status(launch_append(desc->dtype, p, (hipStream_t)stream));
+}
+
+size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                             int32_t max_context_len, const pkv_decode_opts* opts) {
+    if (check_desc(desc) != PKV_OK || check_opts(opts) != PKV_OK) return 0;
+    if (batch <= 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+    const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    if (pl.num_splits <= 1) return 0;
+    return ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim).total;
+}
+
+int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc, int32_t batch, int32_t max_context_len,
+                                          const pkv_decode_opts* opts) {
+    if (check_desc(desc) != PKV_OK || check_opts(opts) != PKV_OK || max_context_len < 0 || batch < 0) return 0;
+    return make_plan(desc, batch, max_context_len, -1, opts).num_splits;
+}
+
+pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_context_len, float scale, const pkv_decode_opts* opts,
+                                  void* out, pkv_dtype out_dtype, float* lse_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq,
+                                      context_lens, batch, num_q_heads, max_context_len, opts);
+    if (st != PKV_OK) return st;
+    if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PKV_OK;
+    if (!out) return PKV_ERR_NULL;
+    // The plan (and so the workspace size) ignores max_blocks_per_seq so that the size
+    // query needs no block-table argument; the kernels clamp to the table separately.
+    const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    Plan run = pl;
+    run.len_cap = make_plan(desc, batch, max_context_len, max_blocks_per_seq, opts).len_cap;
+    DecodeParams p = fill_params(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens,
+                                 num_q_heads, scale, opts, run);
+    p.out_dtype = out_dtype;
+    const hipStream_t s = (hipStream_t)stream;
+    if (pl.num_splits == 1) {
+        p.out = out;
+        p.lse = lse_out;
+        return hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
+    }
+    const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
+    if (!workspace) return PKV_ERR_WORKSPACE;
+    if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
+    if (((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
+    p.o_part = (float*)((char*)workspace + wl.o_off);
+    p.m_part = (float*)((char*)workspace + wl.m_off);
+    p.l_part = (float*)((char*)workspace + wl.l_off);
+    st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch, s));
+    if (st != PKV_OK) return st;
+    CombineParams cp;
+    cp.o_part = p.o_part;
+    cp.m_part = p.m_part;
+    cp.l_part = p.l_part;
+    cp.out = out;
+    cp.lse = lse_out;
+    cp.rows = batch * num_q_heads;
+    cp.num_splits = pl.num_splits;
+    cp.head_dim = desc->head_dim;
+    cp.out_dtype = out_dtype;
+    return hip_status(launch_combine(cp, s));
+}
+
+pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void* k_cache,
+                                          const void* v_cache, const void* q, const int32_t* block_table,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                          float scale, const pkv_decode_opts* opts, float* o_part,
+                                          float* m_part, float* l_part, int32_t num_splits, void* stream) {
+    pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq,
+                                      context_lens, batch, num_q_heads, max_context_len, opts);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    if (num_splits != pl.num_splits) return PKV_ERR_SHAPE;
+    if (batch == 0) return PKV_OK;
+    if (!o_part || !m_part || !l_part) return PKV_ERR_NULL;
+    Plan run = pl;
+    run.len_cap = make_plan(desc, batch, max_context_len, max_blocks_per_seq, opts).len_cap;
+    DecodeParams p = fill_params(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens,
+                                 num_q_heads, scale, opts, run);
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    return hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch,
+                                    (hipStream_t)stream));
+}
+
+pkv_status paged_decode_combine(const float* o_part, const float* m_part, const float* l_part, int32_t batch,
+                                int32_t num_q_heads, int32_t num_splits, int32_t head_dim, void* out,
+                                pkv_dtype out_dtype, float* lse_out, void* stream) {
+    if (batch < 0 || num_q_heads <= 0 || num_splits <= 0) return PKV_ERR_SHAPE;
+    if (head_dim <= 0 || head_dim > 256) return PKV_ERR_UNSUPPORTED;
+    if (!dtype_ok(out_dtype)) return PKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PKV_OK;
+    if (!o_part || !m_part || !l_part || !out) return PKV_ERR_NULL;
+    if ((long long)batch * num_q_heads > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+    CombineParams cp;
+    cp.o_part = o_part;
+    cp.m_part = m_part;
+    cp.l_part = l_part;
+    cp.out = out;
+    cp.lse = lse_out;
+    cp.rows = batch * num_q_heads;
+    cp.num_splits = num_splits;
+    cp.head_dim = head_dim;
+    cp.out_dtype = out_dtype;
+    return hip_status(launch_combine(cp, (hipStream_t)stream));
+}
+
+uint64_t pkv_kv_cache_bytes(int64_t batch, int64_t layers, int64_t kv_heads, int64_t head_dim, int64_t seq_len,
+                            int64_t dtype_bytes, int64_t block_size) {
+    if (batch < 0 || layers < 0 || kv_heads < 0 || head_dim < 0 || seq_len < 0 || dtype_bytes < 0) return 0;
+    uint64_t seq = (uint64_t)seq_len;
+    if (block_size > 0) seq = (seq + (uint64_t)block_size - 1) / (uint64_t)block_size * (uint64_t)block_size;
+    return 2ull * (uint64_t)batch * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim * seq *
+           (uint64_t)dtype_bytes;
+}
+
+const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "inconsistent or non-positive size";
+        case PKV_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size or group size";
+        case PKV_ERR_MODE: return "invalid sparsity options (window with page_list, bad field)";
+        case PKV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case PKV_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,387 @@
+// decode.hip — split-K paged decode attention and the cross-split log-sum-exp combine.
+//
+// What is computed ([TF] "Transformer模型中的KV Cache优化推理策略", §"为什么传统推理方式难以为继？":
+// softmax(q K^T / sqrt(d)) V for the one new query of each sequence; [primer]
+// "从一次线上事故说起…" §4.1: the keys and values sit in fixed-size blocks reached through
+// a per-sequence block table; [primer] §4.3 and [Novita] "How KV Sparsity Achieves 1.5x
+// Acceleration for vLLM" §關鍵技術 1: a per-layer sliding window; [OVAL] "Output-Aware Local
+// Page Bases for KV Cache Retrieval" §2.2/§3.3: a per-step list of pages to read).
+//
+// How (gfx950):
+//  * One workgroup = 4 wavefronts = one (partition, kv head, sequence). The attended token
+//    set of a sequence is enumerated as aligned 16-token units; a partition is a run of
+//    consecutive units, dealt round-robin to the 4 waves, two units per step.
+//  * All G query heads of a kv head ride in the N dimension of the matrix instructions, so
+//    every K/V sub-tile is read from HBM once per group.
+//  * Per unit a lane issues 2 * D / (4E) 16-byte loads; each load instruction of a wave
+//    reads 1 KiB of consecutive bytes (the pool layout puts each lane's operand chunk in
+//    lane order). Loads of the next pair of units are in flight while the current pair is
+//    multiplied.
+//  * S^T = K . Q^T and O^T += V^T . P^T on the matrix cores; the logits land in exactly the
+//    registers the second product takes as its B operand, so P never moves between lanes.
+//  * Online softmax per head in the log2 domain ([Novita] §關鍵技術 2: one pass keeping the
+//    running max and the running sum l); the running max is shared by the 4 lanes that hold
+//    one head's column (two cross-lane exchanges per pair of units).
+//  * Masked tokens get weight exactly 0 by selection, and their V elements are zeroed before
+//    the product, so stale or NaN memory past the context never leaks in ([OVAL] §3.2:
+//    never read uninitialised memory past the cache length).
+//  * Waves merge through LDS; the workgroup writes (o, m, l) of its partition, or the final
+//    normalised row when the whole sequence is one partition.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+struct SeqPlan {
+    int L;        // context length, clamped to the table / grid bounds
+    int e0;       // attended: t < e0 (sinks) or t >= s1 (window); full: e0 = s1 = 0
+    int s1;
+    int n0;       // units of the sink range
+    int u1a;      // unit index (t / 16) where the window range starts
+    int n_units;  // units enumerated for this sequence
+};
+
+template <int MODE>
+__device__ __forceinline__ SeqPlan make_plan(const DecodeParams& p, int b) {
+    SeqPlan sp;
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+    sp.L = L;
+    sp.e0 = 0;
+    sp.s1 = 0;
+    sp.n0 = 0;
+    sp.u1a = 0;
+    const int nu_full = (L + 15) >> 4;
+    if (MODE == kPages) {
+        sp.n_units = p.pages_per_seq * (p.block_size >> 4);
+    } else if (MODE == kWindow && p.window < L) {
+        const int e0 = p.sinks < L ? p.sinks : L;
+        int s1 = L - p.window;
+        if (s1 < e0) s1 = e0;
+        sp.e0 = e0;
+        sp.s1 = s1;
+        sp.n0 = (e0 + 15) >> 4;
+        sp.u1a = (s1 >> 4) > sp.n0 ? (s1 >> 4) : sp.n0;
+        sp.n_units = sp.n0 + (nu_full - sp.u1a);
+    } else {
+        sp.n_units = nu_full;
+    }
+    return sp;
+}
+
+// First logical token of unit u, or -1 when the unit holds no attended token.
+template <int MODE>
+__device__ __forceinline__ int unit_token(const DecodeParams& p, const SeqPlan& sp, int b, int u) {
+    if (MODE == kPages) {
+        const int per = p.block_size >> 4;
+        const int k = u / per;
+        const int pg = p.page_list[(size_t)b * p.pages_per_seq + k];
+        if (pg < 0) return -1;
+        const int64_t t0 = (int64_t)pg * p.block_size + (int64_t)(u - k * per) * 16;
+        return t0 < sp.L ? (int)t0 : -1;
+    } else if (MODE == kWindow) {
+        return (u < sp.n0 ? u : sp.u1a + (u - sp.n0)) << 4;
+    }
+    return u << 4;
+}
+
+// Bit i set: token t0 + 4j + i is attended.
+__device__ __forceinline__ unsigned token_keep(const SeqPlan& sp, int t0, int j) {
+    if (t0 < 0) return 0u;
+    unsigned keep = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * j + i;
+        const bool ok = t < sp.L && (t < sp.e0 || t >= sp.s1);
+        keep |= ok ? (1u << i) : 0u;
+    }
+    return keep;
+}
+
+// Whole unit attended (uniform across the wave).
+__device__ __forceinline__ bool unit_full(const SeqPlan& sp, int t0) {
+    return t0 >= 0 && t0 + 16 <= sp.L && (t0 >= sp.s1 || t0 + 16 <= sp.e0);
+}
+
+template <class DT, int D>
+struct UnitBuf {
+    static constexpr int NC = D / (4 * DT::kE);
+    u32x4 k[NC], v[NC];
+    int t0;  // first logical token, -1 = no unit
+};
+
+// Issues the loads of this wave's unit number k (its descriptor sits in lane k).
+template <class DT, int D>
+__device__ __forceinline__ void load_unit(const DecodeParams& p, UnitBuf<DT, D>& ub, int my_tok,
+                                          unsigned my_off, int k, int nk, int lane) {
+    constexpr int NC = D / (4 * DT::kE);
+    const int t0 = k < nk ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+    ub.t0 = t0;
+    if (t0 >= 0) {
+        const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
+        const char* kp = p.k_cache + off + lane * 16;
+        const char* vp = p.v_cache + off + lane * 16;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) ub.k[cc] = load16(kp + cc * 1024);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) ub.v[cc] = load16(vp + cc * 1024);
+    } else {
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            ub.k[cc] = u32x4{0u, 0u, 0u, 0u};
+            ub.v[cc] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+__device__ __forceinline__ void store_out(void* out, int out_dtype, size_t idx, float v) {
+    if (out_dtype == kF32) {
+        reinterpret_cast<float*>(out)[idx] = v;
+    } else if (out_dtype == kF16) {
+        reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
+    } else {
+        reinterpret_cast<__bf16*>(out)[idx] = (__bf16)v;
+    }
+}
+
+template <class DT, int D, int MODE, bool DIRECT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeParams p) {
+    using T = Tile<DT, D / (4 * DT::kE)>;
+    constexpr int NC = D / (4 * DT::kE);
+    constexpr int NACC = T::kAcc;
+    __shared__ float s_m[kWaves][kMaxGroup];
+    __shared__ float s_l[kWaves][kMaxGroup];
+    __shared__ __attribute__((aligned(16))) float s_o[kWaves][kMaxGroup][D + 4];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane >> 4, c = lane & 15;
+    const int G = p.group;
+
+    const SeqPlan sp = make_plan<MODE>(p, b);
+    const int u_begin = split * p.units_per_split;
+    int u_end = u_begin + p.units_per_split;
+    if (u_end > sp.n_units) u_end = sp.n_units;
+
+    if (u_begin >= u_end) {  // empty partition
+        if (DIRECT) {
+            for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
+                const int g = idx / D, x = idx - g * D;
+                const size_t h = (size_t)b * p.q_heads + kvh * G + g;
+                store_out(p.out, p.out_dtype, h * D + x, 0.f);
+                if (x == 0 && p.lse) p.lse[h] = kNegInf;
+            }
+        } else if (tid < G) {
+            const size_t r = ((size_t)b * p.q_heads + kvh * G + tid) * p.num_splits + split;
+            p.m_part[r] = kNegInf;
+            p.l_part[r] = 0.f;
+        }
+        return;
+    }
+
+    // Descriptors of this wave's units, one per lane: unit u_begin + w + k * kWaves in lane k.
+    const int span = u_end - u_begin;
+    const int nk = span > w ? (span - w + kWaves - 1) / kWaves : 0;
+    int my_tok = -1;
+    unsigned my_off = 0;
+    if (lane < nk) {
+        const int u = u_begin + w + lane * kWaves;
+        const int t0 = unit_token<MODE>(p, sp, b, u);
+        if (t0 >= 0) {
+            const int phys = p.block_table[(size_t)b * p.max_blocks + t0 / p.block_size];
+            if (phys >= 0 && phys < p.num_blocks) {
+                const size_t elem = (((size_t)phys * p.kv_heads + kvh) * p.block_size + (t0 % p.block_size)) * D;
+                my_off = (unsigned)(elem * DT::kBytes / 16);
+                my_tok = t0;
+            }
+        }
+    }
+
+    // Q^T operand: lane (j, c) holds head (c % 8)'s dims [kk*4E + j*E, +E) for chunk group kk.
+    const int qhead = c & 7;
+    u32x4 q[NC];
+#pragma unroll
+    for (int kk = 0; kk < NC; ++kk) q[kk] = u32x4{0u, 0u, 0u, 0u};
+    if (qhead < G) {
+        const char* qp = p.q + (((size_t)b * p.q_heads + kvh * G + qhead) * D + j * DT::kE) * DT::kBytes;
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qp + kk * 4 * DT::kE * DT::kBytes);
+    }
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 acc[NACC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] = zero4();
+
+    const float qk_scale = p.qk_scale_log2;
+    const bool upper = c >= 8;
+    auto process = [&](UnitBuf<DT, D>& X, UnitBuf<DT, D>& Y) __attribute__((always_inline)) {
+        f32x4 s0 = zero4(), s1 = zero4();
+        T::qk(s0, X.k, q);
+        T::qk(s1, Y.k, q);
+        const unsigned keep0 = token_keep(sp, X.t0, j);
+        const unsigned keep1 = token_keep(sp, Y.t0, j);
+        float x0[4], x1[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x0[i] = (keep0 >> i) & 1 ? s0[i] * qk_scale : kNegInf;
+            x1[i] = (keep1 >> i) & 1 ? s1[i] * qk_scale : kNegInf;
+            mx = fmaxf(mx, fmaxf(x0[i], x1[i]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        f32x4 p0, p1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p0[i] = __builtin_amdgcn_exp2f(x0[i] - m_use);
+            p1[i] = __builtin_amdgcn_exp2f(x1[i] - m_use);
+        }
+        l_run = l_run * alpha + ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+        if (!unit_full(sp, X.t0)) T::mask_v(X.v, keep0);
+        if (!unit_full(sp, Y.t0)) T::mask_v(Y.v, keep1);
+        T::pv(acc, X.v, p0, upper);
+        T::pv(acc, Y.v, p1, upper);
+        m_run = m_new;
+    };
+
+    UnitBuf<DT, D> A0, A1, B0, B1;
+    load_unit<DT, D>(p, A0, my_tok, my_off, 0, nk, lane);
+    load_unit<DT, D>(p, A1, my_tok, my_off, 1, nk, lane);
+    for (int k = 0; k < nk; k += 4) {
+        if (k + 2 < nk) {
+            load_unit<DT, D>(p, B0, my_tok, my_off, k + 2, nk, lane);
+            load_unit<DT, D>(p, B1, my_tok, my_off, k + 3, nk, lane);
+        }
+        process(A0, A1);
+        if (k + 2 >= nk) break;
+        if (k + 4 < nk) {
+            load_unit<DT, D>(p, A0, my_tok, my_off, k + 4, nk, lane);
+            load_unit<DT, D>(p, A1, my_tok, my_off, k + 5, nk, lane);
+        }
+        process(B0, B1);
+    }
+
+    // The 4 lanes of one column hold partial sums of the same head under the same max.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    const int head = T::acc_head(c);
+    if (j == 0 && c < 8 && head < G) {
+        s_m[w][head] = m_run;
+        s_l[w][head] = l_run;
+    }
+    if (head < G && T::acc_owner(c)) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) *reinterpret_cast<f32x4*>(&s_o[w][head][T::acc_dim(a, j, c)]) = acc[a];
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
+        const int g = idx / D, x = idx - g * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][g]);
+        float Ls = 0.f, O = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float mw = s_m[ww][g];
+            const float sc = mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            Ls += s_l[ww][g] * sc;
+            O += s_o[ww][g][x] * sc;
+        }
+        const size_t h = (size_t)b * p.q_heads + kvh * G + g;
+        if (DIRECT) {
+            store_out(p.out, p.out_dtype, h * D + x, Ls > 0.f ? O / Ls : 0.f);
+            if (x == 0 && p.lse) p.lse[h] = Ls > 0.f ? M * kLn2 + logf(Ls) : kNegInf;
+        } else {
+            const size_t r = h * p.num_splits + split;
+            p.o_part[r * D + x] = O;
+            if (x == 0) {
+                p.m_part[r] = Ls > 0.f ? M * kLn2 : kNegInf;
+                p.l_part[r] = Ls;
+            }
+        }
+    }
+}
+
+// Cross-split combine: one wavefront per (sequence, query head) row.
+__global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int S = p.num_splits, D = p.head_dim;
+    const float* mr = p.m_part + (size_t)r * S;
+    const float* lr = p.l_part + (size_t)r * S;
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s)
+        if (lr[s] > 0.f) M = fmaxf(M, mr[s]);
+    float Ls = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};  // D <= 256
+    for (int s = 0; s < S; ++s) {
+        const float l = lr[s];
+        if (!(l > 0.f)) continue;
+        const float wgt = expf(mr[s] - M);
+        Ls += wgt * l;
+        const float* op = p.o_part + ((size_t)r * S + s) * D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (lane + 64 * e < D) o[e] += wgt * op[lane + 64 * e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int x = lane + 64 * e;
+        if (x < D) store_out(p.out, p.out_dtype, (size_t)r * D + x, M == kNegInf ? 0.f : o[e] / Ls);
+    }
+    if (lane == 0 && p.lse) p.lse[r] = M == kNegInf ? kNegInf : M + logf(Ls);
+}
+
+template <class DT, int D, int MODE>
+static hipError_t launch_decode_t(bool direct, const DecodeParams& p, int batch, hipStream_t s) {
+    const dim3 grid((unsigned)p.num_splits, (unsigned)p.kv_heads, (unsigned)batch);
+    const dim3 block(64 * kWaves);
+    if (direct)
+        decode_split_kernel<DT, D, MODE, true><<<grid, block, 0, s>>>(p);
+    else
+        decode_split_kernel<DT, D, MODE, false><<<grid, block, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <class DT, int D>
+static hipError_t launch_decode_m(int mode, bool direct, const DecodeParams& p, int batch, hipStream_t s) {
+    switch (mode) {
+        case kWindow: return launch_decode_t<DT, D, kWindow>(direct, p, batch, s);
+        case kPages: return launch_decode_t<DT, D, kPages>(direct, p, batch, s);
+        default: return launch_decode_t<DT, D, kFull>(direct, p, batch, s);
+    }
+}
+
+template <class DT>
+static hipError_t launch_decode_d(int head_dim, int mode, bool direct, const DecodeParams& p, int batch,
+                                  hipStream_t s) {
+    return head_dim == 64 ? launch_decode_m<DT, 64>(mode, direct, p, batch, s)
+                          : launch_decode_m<DT, 128>(mode, direct, p, batch, s);
+}
+
+hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const DecodeParams& p, int batch,
+                         hipStream_t s) {
+    if (batch <= 0 || p.num_splits <= 0) return hipSuccess;
+    switch (dtype) {
+        case kF32: return launch_decode_d<F32>(head_dim, mode, direct, p, batch, s);
+        case kF16: return launch_decode_d<F16>(head_dim, mode, direct, p, batch, s);
+        default: return launch_decode_d<BF16>(head_dim, mode, direct, p, batch, s);
+    }
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    combine_kernel<<<dim3((unsigned)p.rows), dim3(64), 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,193 @@
+// pkv_device.h — device-side building blocks of the gfx950 paged decode-attention kernels.
+//
+// Element types, 16-byte chunk loads, the matrix-core (MFMA) tile products and the
+// cache-layout arithmetic shared by the append and attention kernels of this library.
+//
+// Lane conventions (wave64). Lane l is written (j, c) with j = l / 16 and c = l % 16.
+// The 16x16 MFMA shapes used here hand lane (j, c) row/column c of each operand and
+// rows 4j..4j+3 of column c of the 16x16 fp32 result. The decode kernel computes
+//   S^T = K . Q^T   (A = a 16-token sub-tile of K, B = Q^T, query heads in the columns)
+// so lane (j, c) ends up holding the logits of column c's head for tokens 4j..4j+3, and
+//   O^T += V^T . P^T (A = V^T straight from the loaded chunk, B = P^T built in place from
+// the lane's own logits), so P never moves between lanes. Every value a lane needs from the
+// cache is one 16-byte chunk at index (chunk group) * 64 + l of the sub-tile, by
+// construction of the cache layout (see include/pagedkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// dtype tags -----------------------------------------------------------------------------
+struct F32 {
+    static constexpr int kBytes = 4;
+    static constexpr int kE = 4;  // elements per 16-byte chunk
+};
+struct F16 {
+    static constexpr int kBytes = 2;
+    static constexpr int kE = 8;
+};
+struct BF16 {
+    static constexpr int kBytes = 2;
+    static constexpr int kE = 8;
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Packs two fp32 values into bf16 (round to nearest even, hardware conversion).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (unsigned)__builtin_bit_cast(unsigned short, a) |
+           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+__device__ __forceinline__ float bf16_lo_f32(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ unsigned pack_f16(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (unsigned)__builtin_bit_cast(unsigned short, a) |
+           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+__device__ __forceinline__ float f16_lo_f32(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi_f32(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+// Tile products for one 16-token sub-tile ----------------------------------------------------
+//
+// Query heads: a kv head's G <= 8 query heads sit in MFMA columns c and c + 8 (column c holds
+// head c % 8), so both halves of the 16 columns compute the same logits.
+//
+// 2-byte types. S^T (+)= K . Q^T with 16x16x32 MFMAs, one per chunk group of 32 dims.
+// PV: a lane's V chunk np holds tokens 4j..4j+3 of dim 32np + c (elements 0..3) and of dim
+// 32np + 16 + c (elements 4..7). Used as the A operand of a 16x16x32 MFMA against a B operand
+// whose lane (j, c) carries P[head c % 8][4j..4j+3] in elements 0..3 when c < 8 and in
+// elements 4..7 when c >= 8 (zeros elsewhere), one instruction yields dims 32np + r for the
+// columns c < 8 and dims 32np + 16 + r for the columns c >= 8. Accumulator np of lane (j, c)
+// therefore holds head c % 8, dims 32np + 16 * (c / 8) + 4j + i. P is split into a high part
+// and a residual of the 2-byte type (two instructions), keeping ~16 significant bits.
+template <class DT, int NC>
+struct Tile;
+
+template <class DT>
+struct Pack2;
+template <>
+struct Pack2<BF16> {
+    __device__ __forceinline__ static unsigned pack(float lo, float hi) { return pack_bf16(lo, hi); }
+    __device__ __forceinline__ static float lo(unsigned w) { return bf16_lo_f32(w); }
+    __device__ __forceinline__ static float hi(unsigned w) { return bf16_hi_f32(w); }
+    __device__ __forceinline__ static f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct Pack2<F16> {
+    __device__ __forceinline__ static unsigned pack(float lo, float hi) { return pack_f16(lo, hi); }
+    __device__ __forceinline__ static float lo(unsigned w) { return f16_lo_f32(w); }
+    __device__ __forceinline__ static float hi(unsigned w) { return f16_hi_f32(w); }
+    __device__ __forceinline__ static f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <class DT, int NC>
+struct Tile2B {
+    static constexpr int kAcc = NC;  // accumulators per lane
+    __device__ __forceinline__ static void qk(f32x4& s, const u32x4 (&k)[NC], const u32x4 (&q)[NC]) {
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) s = Pack2<DT>::mfma(k[kk], q[kk], s);
+    }
+    __device__ __forceinline__ static void pv(f32x4 (&acc)[NC], const u32x4 (&v)[NC], const f32x4& p,
+                                              bool upper) {
+        const unsigned h01 = Pack2<DT>::pack(p.x, p.y);
+        const unsigned h23 = Pack2<DT>::pack(p.z, p.w);
+        const unsigned l01 = Pack2<DT>::pack(p.x - Pack2<DT>::lo(h01), p.y - Pack2<DT>::hi(h01));
+        const unsigned l23 = Pack2<DT>::pack(p.z - Pack2<DT>::lo(h23), p.w - Pack2<DT>::hi(h23));
+        const u32x4 bh = upper ? u32x4{0u, 0u, h01, h23} : u32x4{h01, h23, 0u, 0u};
+        const u32x4 bl = upper ? u32x4{0u, 0u, l01, l23} : u32x4{l01, l23, 0u, 0u};
+#pragma unroll
+        for (int np = 0; np < NC; ++np) {
+            acc[np] = Pack2<DT>::mfma(v[np], bh, acc[np]);
+            acc[np] = Pack2<DT>::mfma(v[np], bl, acc[np]);
+        }
+    }
+    // Zero the V elements of tokens 4j+i whose bit i of `keep` is clear (exact zero, even for NaN).
+    __device__ __forceinline__ static void mask_v(u32x4 (&v)[NC], unsigned keep) {
+        const unsigned m01 = ((keep & 1) ? 0x0000ffffu : 0u) | ((keep & 2) ? 0xffff0000u : 0u);
+        const unsigned m23 = ((keep & 4) ? 0x0000ffffu : 0u) | ((keep & 8) ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int np = 0; np < NC; ++np) {
+            v[np].x &= m01;
+            v[np].y &= m23;
+            v[np].z &= m01;
+            v[np].w &= m23;
+        }
+    }
+    // Head and first dim of accumulator a in lane (j, c).
+    __device__ __forceinline__ static int acc_head(int c) { return c & 7; }
+    __device__ __forceinline__ static int acc_dim(int a, int j, int c) { return 32 * a + 16 * (c >> 3) + 4 * j; }
+    __device__ __forceinline__ static bool acc_owner(int c) { return true; }
+};
+
+template <int NC>
+struct Tile<BF16, NC> : Tile2B<BF16, NC> {};
+template <int NC>
+struct Tile<F16, NC> : Tile2B<F16, NC> {};
+
+// fp32: 16x16x4 MFMAs, one element per lane. K chunk kk of lane (j, c) carries dims
+// 16kk + 4j .. +3 of token c; V chunk n carries tokens 4j..4j+3 of dim 16n + c, and MFMA
+// number i contracts token 4j+i of every lane group j, i.e. element i of the chunk with
+// element i of P. Accumulator n of lane (j, c) holds head c % 8, dims 16n + 4j + i (the
+// columns c >= 8 duplicate the columns c < 8).
+template <int NC>
+struct Tile<F32, NC> {
+    static constexpr int kAcc = NC;
+    __device__ __forceinline__ static void qk(f32x4& s, const u32x4 (&k)[NC], const u32x4 (&q)[NC]) {
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[kk].x), __uint_as_float(q[kk].x), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[kk].y), __uint_as_float(q[kk].y), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[kk].z), __uint_as_float(q[kk].z), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[kk].w), __uint_as_float(q[kk].w), s, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ static void pv(f32x4 (&acc)[NC], const u32x4 (&v)[NC], const f32x4& p, bool) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[n].x), p.x, acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[n].y), p.y, acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[n].z), p.z, acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[n].w), p.w, acc[n], 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ static void mask_v(u32x4 (&v)[NC], unsigned keep) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            v[n].x &= (keep & 1) ? ~0u : 0u;
+            v[n].y &= (keep & 2) ? ~0u : 0u;
+            v[n].z &= (keep & 4) ? ~0u : 0u;
+            v[n].w &= (keep & 8) ? ~0u : 0u;
+        }
+    }
+    __device__ __forceinline__ static int acc_head(int c) { return c & 7; }
+    __device__ __forceinline__ static int acc_dim(int a, int j, int c) { return 16 * a + 4 * j; }
+    __device__ __forceinline__ static bool acc_owner(int c) { return c < 8; }
+};
+
+}  // namespace pkv

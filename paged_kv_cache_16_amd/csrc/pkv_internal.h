@@ -1,0 +1,75 @@
+// pkv_internal.h — kernel parameter blocks and launchers shared by the host dispatch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum Mode : int { kFull = 0, kWindow = 1, kPages = 2 };
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+constexpr int kWaves = 4;           // wavefronts per workgroup of the split kernel
+constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
+constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
+
+struct AppendParams {
+    void* k_cache;
+    void* v_cache;
+    const void* k_new;
+    const void* v_new;
+    const int32_t* slots;
+    int64_t num_tokens;
+    int64_t num_slots;  // num_blocks * block_size
+    int32_t block_size;
+    int32_t kv_heads;
+    int32_t head_dim;
+};
+
+struct DecodeParams {
+    const char* k_cache;  // byte pointers to the pools
+    const char* v_cache;
+    const char* q;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    const int32_t* page_list;
+    void* out;       // direct mode: [B][Hq][D] of out dtype
+    float* lse;      // direct mode, nullable
+    float* o_part;   // split mode: [B][Hq][S][D]
+    float* m_part;   // split mode: [B][Hq][S]
+    float* l_part;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t kv_heads;
+    int32_t q_heads;
+    int32_t group;
+    int32_t max_blocks;
+    int32_t len_cap;       // min(max_context_len, max_blocks * block_size)
+    int32_t window;
+    int32_t sinks;
+    int32_t pages_per_seq;
+    int32_t units_per_split;
+    int32_t num_splits;
+    int32_t out_dtype;     // DType
+    float qk_scale_log2;   // scale * log2(e)
+};
+
+struct CombineParams {
+    const float* o_part;
+    const float* m_part;
+    const float* l_part;
+    void* out;
+    float* lse;
+    int32_t rows;  // batch * q_heads
+    int32_t num_splits;
+    int32_t head_dim;
+    int32_t out_dtype;
+};
+
+hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s);
+hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const DecodeParams& p,
+                         int batch, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+}  // namespace pkv

@@ -42,7 +42,12 @@ def seed_of(*parts) -> int:
     h = 0x5EED0000
     for p in parts:
         if isinstance(p, str):
-            p = int.from_bytes(p.encode()[:8].ljust(8, b"\0"), "little")
+            raw = p.encode()
+            words = [int.from_bytes(raw[i:i + 8].ljust(8, b"\0"), "little")
+                     for i in range(0, max(len(raw), 1), 8)]
+            for wd in words + [len(raw)]:
+                h = _mix(h ^ wd)
+            continue
         h = _mix(h ^ (int(p) & _MASK64))
     return h & ((1 << 63) - 1)
 

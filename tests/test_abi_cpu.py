@@ -1,0 +1,107 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/pagedkv.h
+declares, and its host-only paths (validation, sizing, accounting) behave as documented.
+Nothing here launches a kernel."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:pkv_status|size_t|int32_t|uint64_t|const char\s*\*)\s+(\w+)\s*\(",
+                       text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_16_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("kv_cache_append", "paged_decode_attention", "paged_decode_attention_workspace_size",
+                 "paged_decode_attention_partial", "paged_decode_combine", "pkv_status_string",
+                 "pkv_kv_cache_bytes", "paged_decode_attention_num_splits"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(pkv):
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(pkv):
+    for s in range(7):
+        assert pkv.status_string(s) and pkv.status_string(s) != "unknown status"
+    assert pkv.status_string(99) == "unknown status"
+
+
+def test_kv_cache_bytes_worked_values(pkv):
+    with open(os.path.join(ROOT, "tests", "golden", "kv_cache_bytes.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert pkv.kv_cache_bytes(c["batch"], c["layers"], c["heads"], c["head_dim"], c["seq_len"],
+                                  c["dtype_bytes"]) == c["bytes"]
+    assert pkv.kv_cache_bytes(1, 1, 8, 128, 4001, 2, 16) == 2 * 8 * 128 * 4016 * 2
+
+
+def _desc(pkv, nb=64, P=16, hkv=8, d=128, dt=2):
+    return pkv.CacheDesc(nb, P, hkv, d, dt)
+
+
+def test_workspace_and_split_queries(pkv):
+    lib = pkv._lib
+    d = _desc(pkv)
+    o = pkv.DecodeOpts(0, 0, None, 0, 256)
+    # 4096 tokens in 256-token partitions -> 16 partitions; workspace holds o, m, l for each
+    assert lib.paged_decode_attention_num_splits(ctypes.byref(d), 32, 4096, ctypes.byref(o)) == 16
+    ws = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(o))
+    rows = 32 * 32 * 16
+    assert ws >= rows * (128 + 2) * 4
+    # a single partition needs no workspace
+    o1 = pkv.DecodeOpts(0, 0, None, 0, 4096)
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(o1)) == 0
+    # window mode bounds the partitions by the window, not the context
+    ow = pkv.DecodeOpts(512, 4, None, 0, 64)
+    assert lib.paged_decode_attention_num_splits(ctypes.byref(d), 8, 30000, ctypes.byref(ow)) <= 9
+    # rejected arguments give 0
+    bad = _desc(pkv, d=96)
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(bad), 1, 8, 10, None) == 0
+
+
+def test_validation_precedes_any_launch(pkv):
+    lib = pkv._lib
+    d = _desc(pkv)
+    # NULL descriptor
+    assert lib.kv_cache_append(None, None, None, None, None, None, 1, None) == 1
+    # zero tokens is a no-op even with NULL buffers
+    assert lib.kv_cache_append(ctypes.byref(d), None, None, None, None, None, 0, None) == 0
+    # missing buffers
+    assert lib.kv_cache_append(ctypes.byref(d), None, None, None, None, None, 4, None) == 1
+    # unsupported head_dim / block size
+    assert lib.kv_cache_append(ctypes.byref(_desc(pkv, d=96)), None, None, None, None, None, 4, None) == 3
+    assert lib.kv_cache_append(ctypes.byref(_desc(pkv, P=24)), None, None, None, None, None, 4, None) == 3
+    call = lib.paged_decode_attention
+    fake = ctypes.c_void_p(256)  # never dereferenced: every case below fails validation first
+    args = lambda hq=32, opts=None, out=fake, mcl=100, batch=2, ws=None, wsn=0: (
+        ctypes.byref(d), fake, fake, fake, fake, 8, fake, batch, hq, mcl, 0.0, opts, out, 2, None, ws, wsn, None)
+    assert call(*args(hq=30)) == 2                      # Hq % Hkv != 0
+    assert call(*args(hq=8 * 9)) == 3                   # group of 9 > 8
+    both = pkv.DecodeOpts(16, 0, fake, 4, 0)
+    assert call(*args(opts=ctypes.byref(both))) == 4    # window and page list together
+    assert call(*args(out=None)) == 1                   # no output
+    assert call(*args(batch=0)) == 0                    # empty batch: nothing to do
+    many = pkv.DecodeOpts(0, 0, None, 0, 64)
+    assert call(*args(opts=ctypes.byref(many), mcl=4096)) == 5   # needs a workspace, none given
+    assert lib.paged_decode_combine(None, None, None, 2, 4, 3, 128, None, 0, None, None) == 1
+    assert lib.paged_decode_combine(fake, fake, fake, 2, 4, 0, 128, fake, 0, None, None) == 2
