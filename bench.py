@@ -41,11 +41,40 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--seed", type=int, default=2026)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
-                    help="sequences of replica 0 the oracle runs for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU baseline: run the oracle on whole sequences of the workload until "
+                         "this much oracle time is spent (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its launch stream)."""
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        h = self._ct.c_void_p()
+        if self.lib.hipEventCreate(self._ct.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self._ct.c_float()
+        if self.lib.hipEventElapsedTime(self._ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, h: int) -> None:
+        self.lib.hipEventDestroy(h)
 
 
 def build_replica(w, lens, seed, r, dev):
@@ -78,39 +107,42 @@ def build_replica(w, lens, seed, r, dev):
     return rep
 
 
-def cpu_baseline(w, lens, seed, reps, nseq, dev):
-    """Times the oracle, as it is, on the first `nseq` sequences of replica 0."""
+def cpu_baseline(w, lens, seed, reps, seconds, dev):
+    """Times the oracle, as it is, on whole sequences of the workload (replica 0, then 1, ...)
+    until `seconds` of oracle time are spent. Only the attention call is timed."""
     import numpy as np
     import torch
 
     import oracle
     import synth
 
-    P, d, Hkv, Hq = w.block_size, w.head_dim, w.kv_heads, w.q_heads
-    rep = reps[0]
-    total_s, total_bytes, total_tokens = 0.0, 0, 0
-    for b in range(min(nseq, len(lens))):
-        L = lens[b]
-        kb = synth.normal((L - 1, Hkv, d), seed, w.name, 0, b, "k", dtype=w.dtype, device=dev)
-        vb = synth.normal((L - 1, Hkv, d), seed, w.name, 0, b, "v", dtype=w.dtype, device=dev)
-        kb = torch.cat([kb, rep["k_new"][b:b + 1]]).cpu()
-        vb = torch.cat([vb, rep["v_new"][b:b + 1]]).cpu()
-        bt, nb = synth.block_tables([L], P, seed, "cpu", b)
-        kp = np.zeros(nb * Hkv * P * d, np.uint16)
-        vp = np.zeros_like(kp)
-        oracle.kv_append(w.dtype, kp, vp, synth.raw_numpy(kb), synth.raw_numpy(vb),
-                         synth.token_slots(bt, [L], P).numpy(), P=P, Hkv=Hkv, d=d)
-        q = synth.raw_numpy(rep["q"][b:b + 1].cpu())
-        t0 = time.perf_counter()
-        oracle.decode_attention(w.dtype, kp, vp, q, bt.numpy(), np.array([L], np.int32), P=P,
-                                Hkv=Hkv, d=d)
-        total_s += time.perf_counter() - t0
-        total_bytes += L * w.kv_bytes_per_token()
-        total_tokens += L
+    P, d, Hkv = w.block_size, w.head_dim, w.kv_heads
+    total_s, total_bytes, total_tokens, nseq = 0.0, 0, 0, 0
+    for r, rep in enumerate(reps):
+        for b, L in enumerate(lens):
+            if total_s >= seconds:
+                break
+            kb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "k", dtype=w.dtype, device=dev)
+            vb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "v", dtype=w.dtype, device=dev)
+            kb = torch.cat([kb, rep["k_new"][b:b + 1]]).cpu()
+            vb = torch.cat([vb, rep["v_new"][b:b + 1]]).cpu()
+            bt, nb = synth.block_tables([L], P, seed, "cpu", r, b)
+            kp = np.zeros(nb * Hkv * P * d, np.uint16)
+            vp = np.zeros_like(kp)
+            oracle.kv_append(w.dtype, kp, vp, synth.raw_numpy(kb), synth.raw_numpy(vb),
+                             synth.token_slots(bt, [L], P).numpy(), P=P, Hkv=Hkv, d=d)
+            q = synth.raw_numpy(rep["q"][b:b + 1].cpu())
+            t0 = time.perf_counter()
+            oracle.decode_attention(w.dtype, kp, vp, q, bt.numpy(), np.array([L], np.int32), P=P,
+                                    Hkv=Hkv, d=d)
+            total_s += time.perf_counter() - t0
+            total_bytes += L * w.kv_bytes_per_token()
+            total_tokens += L
+            nseq += 1
     return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{min(nseq, len(lens))} of {len(lens)} sequences of one replica "
-                       f"({total_tokens} tokens, full attention, all 32 heads), single-threaded "
-                       f"fp64 C oracle, {total_s:.2f} s",
+                sample=f"{nseq} whole sequences ({total_tokens} tokens, all {w.q_heads} query heads, "
+                       f"full attention) of the same workload, one oracle call each, "
+                       f"single-threaded fp64 C oracle, {total_s:.2f} s of oracle time",
                 seconds=round(total_s, 3))
 
 
@@ -153,30 +185,24 @@ def main():
     torch.cuda.synchronize()
     B, Hq, d = w.batch, w.q_heads, w.head_dim
     mcl = max(lens)
-    S = pkv.num_splits(reps[0]["k"], B, mcl, split_tokens=args.split_tokens)
-    o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device=dev)
-    m_part = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    l_part = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    hip = HipEvents()
 
     def step(rep, ev=None):
         pkv.kv_cache_append(rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"])
-        if ev is not None:
-            ev[0].record()
-        pkv.paged_decode_attention_partial(rep["q"], rep["k"], rep["v"], rep["bt"], rep["cl"],
-                                           max_context_len=mcl, split_tokens=args.split_tokens,
-                                           o_part=o_part, m_part=m_part, l_part=l_part)
-        if ev is not None:
-            ev[1].record()
-        pkv.paged_decode_combine(o_part, m_part, l_part, out=out, lse=lse)
+        pkv.paged_decode_attention(rep["q"], rep["k"], rep["v"], rep["bt"], rep["cl"],
+                                   max_context_len=mcl, split_tokens=args.split_tokens, out=out,
+                                   lse=lse, workspace=workspace, timing=ev)
 
     for i in range(args.warmup):
         step(reps[i % len(reps)])
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # HIP events recorded by the library on the launch stream, right around the main kernel.
+    events = [(hip.create(), hip.create()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -184,7 +210,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    kern_ms = sorted(a.elapsed_time(b) for a, b in events)
+    kern_ms = sorted(hip.elapsed_ms(a, b) for a, b in events)
+    for a, b in events:
+        hip.destroy(a)
+        hip.destroy(b)
     kern_mean = statistics.fmean(kern_ms)
     q = lambda f: kern_ms[min(len(kern_ms) - 1, int(f * len(kern_ms)))]
     achieved = kv_bytes / (kern_mean * 1e-3) / 1e9
@@ -207,15 +236,16 @@ def main():
             "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
             "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
-            "replicas": args.replicas, "num_splits": S, "split_tokens": args.split_tokens,
-            "step": "append 32 tokens + split-K attention + LSE combine",
+            "replicas": args.replicas, "split_tokens": args.split_tokens,
+            "step": "append 32 tokens + paged_decode_attention (persistent split kernel + LSE combine)",
             "parallelism": "single GPU",
         },
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": "decode_split_kernel<BF16,128,full>",
+            "bound": "hbm", "kernel": "decode_stream_kernel<BF16,128,full>" if args.split_tokens == 0
+            else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
@@ -223,8 +253,8 @@ def main():
             "p90_us": round(q(0.9) * 1e3, 3),
         },
     }
-    if args.cpu_sample_seqs > 0:
-        res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_sample_seqs, dev)
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_seconds, dev)
     print(json.dumps(res), flush=True)
 
 

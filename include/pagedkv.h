@@ -113,9 +113,11 @@ typedef struct {
     int32_t num_sinks;       /* >= 0 */
     const int32_t* page_list; /* device, nullable */
     int32_t pages_per_seq;   /* row length of page_list; > 0 when page_list != NULL */
-    int32_t split_tokens;    /* 0: automatic (depends on batch and bounds). Otherwise the
-                                tokens per split-K partition, rounded up to a multiple of 16
-                                and clamped to [16, 4096]. */
+    int32_t split_tokens;    /* 0: automatic work split (see paged_decode_attention).
+                                Otherwise fixed split-K partitions of this many tokens,
+                                rounded up to a multiple of 16 and clamped to [16, 4096]. */
+    void* timing_start;      /* nullable hipEvent_t: recorded on the stream right before the */
+    void* timing_stop;       /* main attention kernel, and right after it (profiling hook) */
 } pkv_decode_opts;
 
 /* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";
@@ -156,6 +158,12 @@ pkv_status kv_cache_append(const pkv_cache_desc* desc /* host */,
  *   lse_out:      nullable [batch][num_q_heads] fp32.
  *   workspace:    at least paged_decode_attention_workspace_size(...) bytes,
  *                 device memory, 256-byte aligned; contents on entry are ignored.
+ * Work split: with split_tokens == 0 the library launches as many wavefronts as the GPU
+ * holds at once and gives each an equal, contiguous share of all (sequence, kv head, 16-token
+ * unit) work, whatever the spread of context lengths; shares that end inside a sequence
+ * leave partials that a second kernel merges by log-sum-exp. Problems of at most 128
+ * attended tokens per sequence run as one kernel without a workspace. With split_tokens > 0
+ * the split is the fixed partitioning of paged_decode_attention_partial plus the combine.
  * Kernel-side guards: L_b is clamped to min(max_context_len, max_blocks_per_seq * P);
  * tokens whose block id falls outside [0, num_blocks) are skipped. */
 pkv_status paged_decode_attention(const pkv_cache_desc* desc /* host */,

@@ -45,7 +45,8 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("window", _i32), ("num_sinks", _i32), ("page_list", _vp),
-                ("pages_per_seq", _i32), ("split_tokens", _i32)]
+                ("pages_per_seq", _i32), ("split_tokens", _i32), ("timing_start", _vp),
+                ("timing_stop", _vp)]
 
 
 _P_DESC = ctypes.POINTER(CacheDesc)
@@ -111,8 +112,10 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(nb, P, hkv, d, DTYPE_CODE[k_cache.dtype])
 
 
-def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0) -> DecodeOpts:
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens))
+def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None) -> DecodeOpts:
+    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None)
+    if timing is not None:
+        o.timing_start, o.timing_stop = int(timing[0]), int(timing[1])
     if page_list is not None:
         o.page_list = _dev(page_list, "page_list", torch.int32)
         o.pages_per_seq = page_list.shape[1]
@@ -156,15 +159,17 @@ def num_splits(k_cache, batch: int, max_context_len: int, *, window=0, num_sinks
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, max_context_len: int,
                            scale: float = 0.0, window: int = 0, num_sinks: int = 0, page_list=None,
                            split_tokens: int = 0, out=None, out_dtype=None, lse=None, workspace=None,
-                           want_lse: bool = True):
-    """One decode query per sequence over its paged cache. Returns (out, lse)."""
+                           want_lse: bool = True, timing=None):
+    """One decode query per sequence over its paged cache. Returns (out, lse).
+
+    timing: optional pair of raw hipEvent_t handles recorded around the main kernel."""
     desc = cache_desc(k_cache)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:

@@ -11,6 +11,8 @@ namespace {
 using namespace pkv;
 
 constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 256 CUs
+constexpr int kStreamChunkMin = 8;       // minimum units per wave in the persistent kernel
+constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
 constexpr size_t kAlign = 256;
@@ -40,7 +42,54 @@ struct Plan {
     int units_per_split = kMinUnitsPerSplit;
     int num_splits = 1;
     int len_cap = 0;
+    // how paged_decode_attention runs: one kernel, fixed partitions + combine, or the
+    // persistent kernel + combine
+    enum Path { kDirect, kPartitions, kStream } path = kDirect;
+    int kmax = 0;       // stream path: partial slots per segment
+    int chunk_min = 0;  // stream path: minimum units per wave
 };
+
+// Path selection for paged_decode_attention (the partial call always uses partitions).
+void choose_path(Plan& pl, const pkv_decode_opts* o) {
+    if (o && o->split_tokens > 0) {
+        pl.path = pl.num_splits > 1 ? Plan::kPartitions : Plan::kDirect;
+    } else if (pl.units_bound <= kDirectMaxUnits) {
+        pl.path = Plan::kDirect;
+        pl.num_splits = 1;
+        pl.units_per_split = kDirectMaxUnits;
+    } else {
+        pl.path = Plan::kStream;
+        // at least kStreamChunkMin units per wave, and few enough slots per segment for
+        // the combine's LDS table
+        pl.chunk_min = kStreamChunkMin;
+        while ((pl.units_bound + pl.chunk_min - 1) / pl.chunk_min + 1 > kMaxSlots) pl.chunk_min *= 2;
+        pl.kmax = (pl.units_bound + pl.chunk_min - 1) / pl.chunk_min + 1;
+    }
+}
+
+struct DeviceInfo {
+    int cus = 0;
+    int occupancy[3][2][3] = {};  // [dtype][head_dim 64/128][mode] workgroups per CU
+};
+DeviceInfo g_dev[64];
+
+int device_cus(int dev) {
+    if (dev < 0 || dev >= 64) return 256;
+    if (g_dev[dev].cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_dev[dev].cus = n;
+    }
+    return g_dev[dev].cus;
+}
+
+int device_occupancy(int dev, int dtype, int head_dim, int mode) {
+    int* slot = (dev >= 0 && dev < 64) ? &g_dev[dev].occupancy[dtype][head_dim == 128][mode] : nullptr;
+    if (slot && *slot) return *slot;
+    const int n = stream_blocks_per_cu(dtype, head_dim, mode);
+    if (slot) *slot = n;
+    return n;
+}
 
 pkv_status check_opts(const pkv_decode_opts* o) {
     if (!o) return PKV_OK;
@@ -92,6 +141,21 @@ Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_
 struct WsLayout {
     size_t o_off, m_off, l_off, total;
 };
+
+struct StreamWs {
+    size_t o_off, m_off, l_off, cnt_off, total;
+};
+
+StreamWs stream_ws(int batch, int kv_heads, int group, int kmax, int head_dim) {
+    StreamWs w;
+    const size_t rows = (size_t)batch * kv_heads * kmax * group;
+    w.o_off = 0;
+    w.m_off = align_up(rows * head_dim * sizeof(float));
+    w.l_off = w.m_off + align_up(rows * sizeof(float));
+    w.cnt_off = w.l_off + align_up(rows * sizeof(float));
+    w.total = w.cnt_off + align_up((size_t)batch * kv_heads * sizeof(int32_t));
+    return w;
+}
 
 WsLayout ws_layout(int batch, int q_heads, int splits, int head_dim) {
     WsLayout w;
@@ -179,8 +243,14 @@ size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc, int32_t
                                              int32_t max_context_len, const pkv_decode_opts* opts) {
     if (check_desc(desc) != PKV_OK || check_opts(opts) != PKV_OK) return 0;
     if (batch <= 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
-    const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
-    if (pl.num_splits <= 1) return 0;
+    Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    choose_path(pl, opts);
+    if (pl.path == Plan::kDirect) return 0;
+    if (pl.path == Plan::kStream) {
+        if (num_q_heads % desc->num_kv_heads) return 0;
+        return stream_ws(batch, desc->num_kv_heads, num_q_heads / desc->num_kv_heads, pl.kmax, desc->head_dim)
+            .total;
+    }
     return ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim).total;
 }
 
@@ -204,27 +274,58 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
     if (!out) return PKV_ERR_NULL;
     // The plan (and so the workspace size) ignores max_blocks_per_seq so that the size
     // query needs no block-table argument; the kernels clamp to the table separately.
-    const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
+    choose_path(pl, opts);
     Plan run = pl;
     run.len_cap = make_plan(desc, batch, max_context_len, max_blocks_per_seq, opts).len_cap;
     DecodeParams p = fill_params(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens,
                                  num_q_heads, scale, opts, run);
     p.out_dtype = out_dtype;
+    p.out = out;
+    p.lse = lse_out;
     const hipStream_t s = (hipStream_t)stream;
-    if (pl.num_splits == 1) {
-        p.out = out;
-        p.lse = lse_out;
-        return hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
+    hipEvent_t ev0 = opts ? (hipEvent_t)opts->timing_start : nullptr;
+    hipEvent_t ev1 = opts ? (hipEvent_t)opts->timing_stop : nullptr;
+    if (pl.path == Plan::kDirect) {
+        if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
+        st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
+        if (st == PKV_OK && ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
+        return st;
+    }
+    if (!workspace) return PKV_ERR_WORKSPACE;
+    if (((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
+    if (pl.path == Plan::kStream) {
+        const int G = num_q_heads / desc->num_kv_heads;
+        const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim);
+        if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
+        const long long n_bound = (long long)batch * desc->num_kv_heads * pl.units_bound;
+        if (n_bound > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+        const long long resident =
+            (long long)device_cus(dev) * device_occupancy(dev, desc->dtype, desc->head_dim, pl.mode) * kWaves;
+        long long waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
+        if (waves > resident) waves = resident;
+        waves = (waves + kWaves - 1) / kWaves * kWaves;
+        p.o_part = (float*)((char*)workspace + wl.o_off);
+        p.m_part = (float*)((char*)workspace + wl.m_off);
+        p.l_part = (float*)((char*)workspace + wl.l_off);
+        p.seg_count = (int32_t*)((char*)workspace + wl.cnt_off);
+        p.batch = batch;
+        p.waves_total = (int)waves;
+        p.chunk_min = pl.chunk_min;
+        p.kmax = pl.kmax;
+        return hip_status(launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, p, s, ev0, ev1));
     }
     const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
-    if (!workspace) return PKV_ERR_WORKSPACE;
     if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
-    if (((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
     p.o_part = (float*)((char*)workspace + wl.o_off);
     p.m_part = (float*)((char*)workspace + wl.m_off);
     p.l_part = (float*)((char*)workspace + wl.l_off);
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
     st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch, s));
     if (st != PKV_OK) return st;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
     CombineParams cp;
     cp.o_part = p.o_part;
     cp.m_part = p.m_part;

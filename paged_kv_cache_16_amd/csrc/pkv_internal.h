@@ -12,6 +12,7 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 constexpr int kWaves = 4;           // wavefronts per workgroup of the split kernel
 constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
+constexpr int kMaxSlots = 512;      // partial slots per segment the stream combine handles
 constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
 
 struct AppendParams {
@@ -53,6 +54,12 @@ struct DecodeParams {
     int32_t num_splits;
     int32_t out_dtype;     // DType
     float qk_scale_log2;   // scale * log2(e)
+    // stream (persistent) kernel only
+    int32_t batch;
+    int32_t waves_total;   // waves launched
+    int32_t chunk_min;     // minimum units per wave
+    int32_t kmax;          // partial slots per (sequence, kv head) segment
+    int32_t* seg_count;    // [B*Hkv]: partials written for the segment; 0 = final row written
 };
 
 struct CombineParams {
@@ -70,6 +77,11 @@ struct CombineParams {
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s);
 hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const DecodeParams& p,
                          int batch, hipStream_t s);
+// Persistent stream kernel + its combine (the paged_decode_attention path). Events, when
+// non-null, are recorded around the stream kernel.
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, const DecodeParams& p, hipStream_t s,
+                                hipEvent_t ev_start, hipEvent_t ev_stop);
+int stream_blocks_per_cu(int dtype, int head_dim, int mode);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
 }  // namespace pkv

@@ -1,0 +1,427 @@
+// stream.hip — persistent ("stream-K") paged decode attention and its combine.
+//
+// The computation is the one described in decode.hip (softmax(q K^T * scale) V over the paged
+// cache, [TF] formula, [primer] §4.1 block table, [primer] §4.3 / [Novita] §關鍵技術 1 window,
+// [OVAL] §2.2/§3.3 page list); what differs is how the work is cut.
+//
+// All (sequence, kv head) segments of the batch are laid end to end as one flat list of
+// 16-token units, b-major then kv head then unit. The launch holds exactly the waves that
+// are resident on the GPU at once; wave w takes the contiguous units [w*C, (w+1)*C) with
+// C = max(ceil(N / waves), chunk_min), so every wave streams the same number of bytes no
+// matter how ragged the context lengths are, and no wave waits for a second launch round.
+// A wave keeps three units of K/V loads in flight (a 4-deep ring of register buffers) and
+// carries the pipeline across segment boundaries. At the end of its part of a segment it
+// writes either the finished, normalised row (when it holds the whole segment) or an
+// (o, m, l) partial into slot  w - first_wave(segment); the wave holding a segment's last
+// unit records how many partials the segment has. The combine kernel then merges them by
+// log-sum-exp ([Novita] §關鍵技術 2: partial softmax results merge through max and sum).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+#include "pkv_plan.h"
+
+namespace pkv {
+
+__device__ __forceinline__ float xor32_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+template <int MODE>
+__device__ __forceinline__ int seq_units(const DecodeParams& p, int b) {
+    return make_plan<MODE>(p, b).n_units;
+}
+
+// Position of a unit: sequence, kv head, unit index within the sequence.
+struct UnitPos {
+    int b, kvh, u, nu;
+};
+
+// Advances a position by k units (k >= 0), skipping sequences without units. Returns
+// b == batch when it runs off the end.
+template <int MODE>
+__device__ __forceinline__ UnitPos advance(const DecodeParams& p, UnitPos s, int k) {
+    while (s.b < p.batch) {
+        const int rem = s.nu - s.u;
+        if (k < rem) {
+            s.u += k;
+            return s;
+        }
+        k -= rem;
+        s.u = 0;
+        if (++s.kvh == p.kv_heads) {
+            s.kvh = 0;
+            do {
+                ++s.b;
+            } while (s.b < p.batch && (s.nu = seq_units<MODE>(p, s.b)) == 0);
+        }
+    }
+    return s;
+}
+
+template <class DT, int D>
+struct RingBuf {
+    static constexpr int NC = D / (4 * DT::kE);
+    u32x4 k[NC], v[NC];
+    int t0;
+};
+
+template <class DT, int D>
+__device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>& rb, int my_tok, unsigned my_off,
+                                          int k, int n, int lane) {
+    constexpr int NC = D / (4 * DT::kE);
+    const int t0 = k < n ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+    rb.t0 = t0;
+    if (t0 >= 0) {
+        const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
+        const char* kp = p.k_cache + off + lane * 16;
+        const char* vp = p.v_cache + off + lane * 16;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) rb.k[cc] = load16_stream(kp + cc * 1024);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) rb.v[cc] = load16_stream(vp + cc * 1024);
+    }
+}
+
+template <class DT, int D, int MODE>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_stream_kernel(DecodeParams p) {
+    using T = Tile<DT, D / (4 * DT::kE)>;
+    constexpr int NC = D / (4 * DT::kE);
+    constexpr int NACC = T::kAcc;
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane >> 4, c = lane & 15;
+    const int B = p.batch, Hkv = p.kv_heads, G = p.group;
+
+    // Total units N of the batch (uniform: kept in scalar registers).
+    int N = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        N += __builtin_amdgcn_readfirstlane(wave_sum(b < B ? seq_units<MODE>(p, b) : 0));
+    }
+    N *= Hkv;
+    const int W = p.waves_total;
+    int C = (N + W - 1) / W;
+    if (C < p.chunk_min) C = p.chunk_min;
+    if ((long long)wave * C >= N) return;
+    const int f_begin = wave * C;
+    const int f_end = (long long)f_begin + C < N ? f_begin + C : N;
+
+    // Locate the first unit: the sequence whose units (times Hkv) cover flat index f_begin.
+    UnitPos pos = {B, 0, 0, 0};
+    {
+        int cum = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int b = b0 + lane;
+            const int nu = b < B ? seq_units<MODE>(p, b) : 0;
+            const int cnt = nu * Hkv;
+            const int incl = wave_incl_scan(cnt, lane);
+            const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
+            if (cum + chunk_total > f_begin) {
+                const unsigned long long hit = __ballot(cum + incl > f_begin);
+                const int lf = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+                const int nu_b = __builtin_amdgcn_readlane(nu, lf);
+                const int before = cum + __builtin_amdgcn_readlane(incl, lf) - nu_b * Hkv;
+                const int rem = f_begin - before;
+                pos.b = b0 + lf;
+                pos.kvh = rem / nu_b;
+                pos.u = rem - pos.kvh * nu_b;
+                pos.nu = nu_b;
+                break;
+            }
+            cum += chunk_total;
+        }
+    }
+
+    // The wave's range, cut at segment boundaries into runs; each run is one (sequence,
+    // kv head) segment piece with its own query, softmax state and load pipeline.
+    const int qhead = c & 7;
+    const bool upper = c >= 8;
+    const float qk_scale = p.qk_scale_log2;
+    int f_run = f_begin;
+    while (f_run < f_end && pos.b < B) {
+        const int b = pos.b, kvh = pos.kvh, u0 = pos.u, nu = pos.nu;
+        const int cnt = f_end - f_run < nu - u0 ? f_end - f_run : nu - u0;
+        const int seg = b * Hkv + kvh;
+        const SeqPlan sp = make_plan<MODE>(p, b);
+
+        u32x4 q[NC];
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) q[kk] = u32x4{0u, 0u, 0u, 0u};
+        if (qhead < G) {
+            const char* qp = p.q + (((size_t)b * p.q_heads + kvh * G + qhead) * D + j * DT::kE) * DT::kBytes;
+#pragma unroll
+            for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qp + kk * 4 * DT::kE * DT::kBytes);
+        }
+        float m_run = kNegInf, l_run = 0.f;
+        f32x4 acc[NACC];
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[a] = zero4();
+
+        auto process = [&](RingBuf<DT, D>& rb) __attribute__((always_inline)) {
+            if (rb.t0 < 0) return;
+            f32x4 s = zero4();
+            T::qk(s, rb.k, q);
+            const unsigned keep = token_keep(sp, rb.t0, j);
+            float x[4];
+            float mx = kNegInf;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (keep >> i) & 1 ? s[i] * qk_scale : kNegInf;
+                mx = fmaxf(mx, x[i]);
+            }
+            mx = xor32_max(xor16_max(mx));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == kNegInf ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            f32x4 pr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+            l_run = l_run * alpha + ((pr.x + pr.y) + (pr.z + pr.w));
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+            if (!unit_full(sp, rb.t0)) T::mask_v(rb.v, keep);
+            T::pv(acc, rb.v, pr, upper);
+            m_run = m_new;
+        };
+
+        for (int ub = 0; ub < cnt; ub += 64) {
+            // Descriptor of the batch's unit k in lane k.
+            const int n = cnt - ub < 64 ? cnt - ub : 64;
+            int my_tok = -1;
+            unsigned my_off = 0;
+            if (lane < n) {
+                const int t0 = unit_token<MODE>(p, sp, b, u0 + ub + lane);
+                if (t0 >= 0) {
+                    const int phys = p.block_table[(size_t)b * p.max_blocks + t0 / p.block_size];
+                    if (phys >= 0 && phys < p.num_blocks) {
+                        const size_t elem = (((size_t)phys * Hkv + kvh) * p.block_size + (t0 % p.block_size)) * D;
+                        my_off = (unsigned)(elem * DT::kBytes / 16);
+                        my_tok = t0;
+                    }
+                }
+            }
+            RingBuf<DT, D> R0, R1, R2, R3;
+            ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane);
+            ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane);
+            ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane);
+            for (int k = 0; k < n; k += 4) {
+                ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane);
+                process(R0);
+                if (k + 1 >= n) break;
+                ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane);
+                process(R1);
+                if (k + 2 >= n) break;
+                ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane);
+                process(R2);
+                if (k + 3 >= n) break;
+                ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane);
+                process(R3);
+            }
+        }
+
+        // End of the run: the finished row, or a partial for the combine.
+        const float l_tot = xor32_sum(xor16_sum(l_run));
+        const int head = T::acc_head(c);
+        const bool writer = head < G && T::acc_owner(c);
+        const bool last = u0 + cnt == nu;
+        if (u0 == 0 && last) {
+            const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (writer) {
+#pragma unroll
+                for (int a = 0; a < NACC; ++a) {
+                    const int dim = T::acc_dim(a, j, c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) store_out(p.out, p.out_dtype, hrow * D + dim + i, acc[a][i] * inv);
+                }
+            }
+            if (j == 0 && c < 8 && head < G && p.lse)
+                p.lse[hrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+            if (lane == 0) p.seg_count[seg] = 0;
+        } else {
+            const int s_g = f_run - u0;  // flat index of the segment's unit 0
+            const int k_slot = wave - s_g / C;
+            if (k_slot < p.kmax) {
+                const size_t row = ((size_t)seg * p.kmax + k_slot) * G + head;
+                if (writer) {
+#pragma unroll
+                    for (int a = 0; a < NACC; ++a)
+                        *reinterpret_cast<f32x4*>(p.o_part + row * D + T::acc_dim(a, j, c)) = acc[a];
+                }
+                if (j == 0 && c < 8 && head < G) {
+                    p.m_part[row] = m_run;  // log2 units, read only by the stream combine
+                    p.l_part[row] = l_tot;
+                }
+                if (lane == 0 && last) p.seg_count[seg] = k_slot + 1;
+            }
+        }
+        f_run += cnt;
+        pos = advance<MODE>(p, pos, cnt);
+        pos.b = __builtin_amdgcn_readfirstlane(pos.b);
+        pos.kvh = __builtin_amdgcn_readfirstlane(pos.kvh);
+        pos.u = __builtin_amdgcn_readfirstlane(pos.u);
+        pos.nu = __builtin_amdgcn_readfirstlane(pos.nu);
+    }
+}
+
+// Merges a segment's partials: one workgroup per (sequence, kv head) segment. The slot
+// weights w = exp(m_k - M) are formed once in LDS, then every thread accumulates its
+// (head, dim) outputs with independent loads of the partial rows. Segments without units
+// get out = 0 and lse = -inf here; segments the stream kernel finished itself (count 0)
+// are skipped.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
+    __shared__ float s_w[kMaxSlots][kMaxGroup];
+    __shared__ float s_inv[kMaxGroup];
+    const int g = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
+    const int G = p.group;
+    const int nu = seq_units<MODE>(p, b);
+    int cnt = nu > 0 ? p.seg_count[g] : -1;
+    if (cnt == 0) return;
+    if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
+    if (cnt > kMaxSlots) cnt = kMaxSlots;
+    const size_t base = (size_t)g * p.kmax * G;  // partial row of (slot k, head h): base + k * G + h
+    if (cnt < 0) {
+        for (int idx = tid; idx < G * D; idx += 256) {
+            const int head = idx / D, x = idx - head * D;
+            const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
+            store_out(p.out, p.out_dtype, hrow * D + x, 0.f);
+            if (x == 0 && p.lse) p.lse[hrow] = kNegInf;
+        }
+        return;
+    }
+    for (int t = tid; t < cnt * G; t += 256) {
+        const float l = p.l_part[base + t];
+        s_w[t / G][t % G] = l > 0.f ? p.m_part[base + t] : kNegInf;  // log2 max of the slot
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = kNegInf;
+        for (int k = 0; k < cnt; ++k) M = fmaxf(M, s_w[k][tid]);
+        float Ls = 0.f;
+        for (int k = 0; k < cnt; ++k) {
+            const float mk = s_w[k][tid];
+            const float w = (M == kNegInf || mk == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+            s_w[k][tid] = w;
+            Ls += w * p.l_part[base + (size_t)k * G + tid];
+        }
+        s_inv[tid] = Ls > 0.f ? 1.f / Ls : 0.f;
+        if (p.lse) p.lse[(size_t)b * p.q_heads + kvh * G + tid] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int head = idx / D, x = idx - head * D;
+        float O = 0.f;
+        int k = 0;
+        for (; k + 4 <= cnt; k += 4) {
+            const float o0 = p.o_part[(base + (size_t)(k + 0) * G + head) * D + x];
+            const float o1 = p.o_part[(base + (size_t)(k + 1) * G + head) * D + x];
+            const float o2 = p.o_part[(base + (size_t)(k + 2) * G + head) * D + x];
+            const float o3 = p.o_part[(base + (size_t)(k + 3) * G + head) * D + x];
+            O += s_w[k][head] * o0 + s_w[k + 1][head] * o1 + s_w[k + 2][head] * o2 + s_w[k + 3][head] * o3;
+        }
+        for (; k < cnt; ++k) O += s_w[k][head] * p.o_part[(base + (size_t)k * G + head) * D + x];
+        store_out(p.out, p.out_dtype, ((size_t)b * p.q_heads + kvh * G + head) * D + x, O * s_inv[head]);
+    }
+}
+
+template <class DT, int D, int MODE>
+static hipError_t launch_stream_t(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const unsigned blocks = (unsigned)(p.waves_total / kWaves);
+    if (e0) {
+        hipError_t e = hipEventRecord(e0, s);
+        if (e != hipSuccess) return e;
+    }
+    decode_stream_kernel<DT, D, MODE><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (e1) {
+        err = hipEventRecord(e1, s);
+        if (err != hipSuccess) return err;
+    }
+    stream_combine_kernel<D, MODE><<<dim3((unsigned)(p.batch * p.kv_heads)), dim3(256), 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <class DT, int D>
+static hipError_t launch_stream_m(int mode, const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    switch (mode) {
+        case kWindow: return launch_stream_t<DT, D, kWindow>(p, s, e0, e1);
+        case kPages: return launch_stream_t<DT, D, kPages>(p, s, e0, e1);
+        default: return launch_stream_t<DT, D, kFull>(p, s, e0, e1);
+    }
+}
+
+template <class DT>
+static hipError_t launch_stream_d(int head_dim, int mode, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
+    return head_dim == 64 ? launch_stream_m<DT, 64>(mode, p, s, e0, e1) : launch_stream_m<DT, 128>(mode, p, s, e0, e1);
+}
+
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, const DecodeParams& p, hipStream_t s,
+                                hipEvent_t ev_start, hipEvent_t ev_stop) {
+    if (p.batch <= 0 || p.waves_total <= 0) return hipSuccess;
+    switch (dtype) {
+        case kF32: return launch_stream_d<F32>(head_dim, mode, p, s, ev_start, ev_stop);
+        case kF16: return launch_stream_d<F16>(head_dim, mode, p, s, ev_start, ev_stop);
+        default: return launch_stream_d<BF16>(head_dim, mode, p, s, ev_start, ev_stop);
+    }
+}
+
+template <class DT, int D, int MODE>
+static int occupancy_t() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE>, 64 * kWaves, 0) !=
+        hipSuccess)
+        return 1;
+    return n > 0 ? n : 1;
+}
+
+template <class DT>
+static int occupancy_d(int head_dim, int mode) {
+    if (head_dim == 64) {
+        return mode == kWindow ? occupancy_t<DT, 64, kWindow>()
+                               : mode == kPages ? occupancy_t<DT, 64, kPages>() : occupancy_t<DT, 64, kFull>();
+    }
+    return mode == kWindow ? occupancy_t<DT, 128, kWindow>()
+                           : mode == kPages ? occupancy_t<DT, 128, kPages>() : occupancy_t<DT, 128, kFull>();
+}
+
+int stream_blocks_per_cu(int dtype, int head_dim, int mode) {
+    switch (dtype) {
+        case kF32: return occupancy_d<F32>(head_dim, mode);
+        case kF16: return occupancy_d<F16>(head_dim, mode);
+        default: return occupancy_d<BF16>(head_dim, mode);
+    }
+}
+
+}  // namespace pkv
