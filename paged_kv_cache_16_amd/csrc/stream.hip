@@ -291,67 +291,77 @@ void decode_stream_kernel(DecodeParams p) {
     }
 }
 
-// Merges a segment's partials: one workgroup per (sequence, kv head) segment. The slot
-// weights w = exp(m_k - M) are formed once in LDS, then every thread accumulates its
-// (head, dim) outputs with independent loads of the partial rows. Segments without units
-// get out = 0 and lse = -inf here; segments the stream kernel finished itself (count 0)
-// are skipped.
+// Merges the partials of one (sequence, query head) row per 64-thread workgroup. The row's
+// slot count and its per-slot (m, l) are uniform, so they arrive through scalar loads; each
+// lane owns D/64 dims and fetches its slices of all partial rows in unrolled batches.
+// Rows of sequences without units get out = 0 and lse = -inf here; rows the stream kernel
+// finished itself (count 0) are skipped.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
-    __shared__ float s_w[kMaxSlots][kMaxGroup];
-    __shared__ float s_inv[kMaxGroup];
-    const int g = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
+__global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
+    constexpr int PER = D / 64;
+    const int r = blockIdx.x;
     const int G = p.group;
+    const int g = r / G, head = r - g * G;
+    const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
+    const int lane = threadIdx.x;
+    const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
     const int nu = seq_units<MODE>(p, b);
-    int cnt = nu > 0 ? p.seg_count[g] : -1;
-    if (cnt == 0) return;
-    if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
-    if (cnt > kMaxSlots) cnt = kMaxSlots;
-    const size_t base = (size_t)g * p.kmax * G;  // partial row of (slot k, head h): base + k * G + h
-    if (cnt < 0) {
-        for (int idx = tid; idx < G * D; idx += 256) {
-            const int head = idx / D, x = idx - head * D;
-            const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
-            store_out(p.out, p.out_dtype, hrow * D + x, 0.f);
-            if (x == 0 && p.lse) p.lse[hrow] = kNegInf;
-        }
+    int cnt = p.seg_count[g];
+    if (nu == 0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, 0.f);
+        if (lane == 0 && p.lse) p.lse[hrow] = kNegInf;
         return;
     }
-    for (int t = tid; t < cnt * G; t += 256) {
-        const float l = p.l_part[base + t];
-        s_w[t / G][t % G] = l > 0.f ? p.m_part[base + t] : kNegInf;  // log2 max of the slot
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = kNegInf;
-        for (int k = 0; k < cnt; ++k) M = fmaxf(M, s_w[k][tid]);
-        float Ls = 0.f;
-        for (int k = 0; k < cnt; ++k) {
-            const float mk = s_w[k][tid];
-            const float w = (M == kNegInf || mk == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-            s_w[k][tid] = w;
-            Ls += w * p.l_part[base + (size_t)k * G + tid];
+    if (cnt == 0) return;
+    if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
+    const size_t base = (size_t)g * p.kmax * G + head;  // partial row of slot k: base + k * G
+    const float* op = p.o_part + base * D + lane * PER;
+    const size_t stride = (size_t)G * D;
+    // Online merge over batches of 8 slots; every slot below kmax is addressable, so a batch
+    // is fetched whole and the slots past cnt are dropped by selection (their contents are
+    // stale, never multiplied in).
+    float M = kNegInf, Ls = 0.f;
+    float o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    for (int k = 0; k < cnt; k += 8) {
+        float lv[8], mv[8], v[8][PER];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = k + u < p.kmax;
+            const size_t rk = base + (size_t)(in ? k + u : 0) * G;
+            lv[u] = p.l_part[rk];
+            mv[u] = p.m_part[rk];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[u][i] = op[(size_t)(in ? k + u : 0) * stride + i];
         }
-        s_inv[tid] = Ls > 0.f ? 1.f / Ls : 0.f;
-        if (p.lse) p.lse[(size_t)b * p.q_heads + kvh * G + tid] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int head = idx / D, x = idx - head * D;
-        float O = 0.f;
-        int k = 0;
-        for (; k + 4 <= cnt; k += 4) {
-            const float o0 = p.o_part[(base + (size_t)(k + 0) * G + head) * D + x];
-            const float o1 = p.o_part[(base + (size_t)(k + 1) * G + head) * D + x];
-            const float o2 = p.o_part[(base + (size_t)(k + 2) * G + head) * D + x];
-            const float o3 = p.o_part[(base + (size_t)(k + 3) * G + head) * D + x];
-            O += s_w[k][head] * o0 + s_w[k + 1][head] * o1 + s_w[k + 2][head] * o2 + s_w[k + 3][head] * o3;
+        float bm = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool live = k + u < cnt && lv[u] > 0.f;
+            bm = fmaxf(bm, live ? mv[u] : kNegInf);
         }
-        for (; k < cnt; ++k) O += s_w[k][head] * p.o_part[(base + (size_t)k * G + head) * D + x];
-        store_out(p.out, p.out_dtype, ((size_t)b * p.q_heads + kvh * G + head) * D + x, O * s_inv[head]);
+        const float m_new = fmaxf(M, bm);
+        if (m_new == kNegInf) continue;
+        const float sc = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+        Ls *= sc;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] *= sc;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool live = k + u < cnt && lv[u] > 0.f;
+            const float w = live ? __builtin_amdgcn_exp2f(mv[u] - m_new) : 0.f;
+            Ls += live ? w * lv[u] : 0.f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] += live ? w * v[u][i] : 0.f;
+        }
+        M = m_new;
     }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, o[i] * inv);
+    if (lane == 0 && p.lse) p.lse[hrow] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
 }
 
 template <class DT, int D, int MODE>
@@ -368,7 +378,7 @@ static hipError_t launch_stream_t(const DecodeParams& p, hipStream_t s, hipEvent
         err = hipEventRecord(e1, s);
         if (err != hipSuccess) return err;
     }
-    stream_combine_kernel<D, MODE><<<dim3((unsigned)(p.batch * p.kv_heads)), dim3(256), 0, s>>>(p);
+    stream_combine_kernel<D, MODE><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
     return hipGetLastError();
 }
 

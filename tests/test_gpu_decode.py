@@ -346,3 +346,24 @@ def test_full_size_kvsparse_window_layer_sampled():
 
 def test_full_size_page_selected_sampled():
     _sampled_full_size("mha7b_pagesel_f16", samples=[0, 15], pages=16)
+
+
+def test_workspace_reuse():
+    """One workspace serves any number of calls, which all give the same result (its
+    contents on entry are ignored)."""
+    import paged_kv_cache_16_amd as pkv
+    lens = [1500, 333, 4000, 2, 0, 129]
+    c = make_case(48, B=6, Hq=16, Hkv=4, d=128, dtype="bf16", P=16, lens=lens)
+    n = pkv.workspace_size(c.gk, 6, 16, max(lens))
+    assert n > 0
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
+    ref = oracle_attend(c)
+    outs = []
+    for _ in range(3):
+        out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
+                                              workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
+    for got in outs:
+        assert_close(c, got, ref, "workspace reuse")
+        assert np.array_equal(got[0], outs[0][0])
