@@ -32,6 +32,36 @@ METRIC = "paged decode-attention KV GB/s and % of HBM peak; decode steps/s per l
 HBM_PEAK_GBS = 8000.0
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources of the library (names and contents, sorted by name)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_16_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")),
+                    key=os.path.basename):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, split_tokens: int):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3 --pmc summary,
+    or None when no summary matches the current kernel sources."""
+    if split_tokens:
+        return None
+    path = os.path.join(ROOT, "profiles", f"decode_stream_kernel_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(round(rec["traffic_bytes"]))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,7 +277,8 @@ def main():
             "bound": "hbm", "kernel": "decode_stream_kernel<BF16,128,full>" if args.split_tokens == 0
             else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, args.split_tokens), "traffic_unit": "bytes per launch",
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
             "p90_us": round(q(0.9) * 1e3, 3),
