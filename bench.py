@@ -176,6 +176,192 @@ def cpu_baseline(w, lens, seed, reps, seconds, dev):
                 seconds=round(total_s, 3))
 
 
+def _layer_caches(w, lens, P, seed, dev, tag, bt):
+    """One layer's K/V pools, prefilled with tokens [0, L_b - 1) of every sequence."""
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    d, Hkv = w.head_dim, w.kv_heads
+    nb = int(bt.max()) + 1
+    gk = torch.empty((nb, Hkv, P, d), dtype=synth.TORCH_DTYPE[w.dtype], device=dev)
+    gv = torch.empty_like(gk)
+    for b, L in enumerate(lens):
+        if L > 1:
+            kb = synth.normal((L - 1, Hkv, d), seed, w.name, tag, b, "k", dtype=w.dtype, device=dev)
+            vb = synth.normal((L - 1, Hkv, d), seed, w.name, tag, b, "v", dtype=w.dtype, device=dev)
+            pkv.kv_cache_append(gk, gv, kb, vb, synth.token_slots(bt[b:b + 1], [L - 1], P).to(dev))
+    return gk, gv
+
+
+def run_multilayer(w, args, dev):
+    """Decode steps over all layers: per layer, append of the batch's new tokens and attention
+    (window + sinks on the window layers); the context advances once per step after the last
+    layer. Qwen2.5-1.5B shape: 4096 cached tokens, then 32 steps (L = 4097..4128). KV-sparse
+    Llama-3-8B shape: one step, repeated for timing."""
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
+    if w.ctx_lo == w.ctx_hi:
+        base = [w.ctx_lo + 1] * B  # L at the first step
+    else:
+        base = synth.uniform_lengths(B, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
+    steps = w.steps
+    cap = [L + steps - 1 for L in base]
+    bt, nb = synth.block_tables(cap, P, args.seed, w.name)
+    gbt = bt.to(dev)
+    layers = []
+    for layer in range(w.layers):
+        gk, gv = _layer_caches(w, base, P, args.seed, dev, 1000 + layer, bt)
+        layers.append(dict(
+            k=gk, v=gv,
+            q=synth.normal((B, Hq, d), args.seed, w.name, layer, "q", dtype=w.dtype, device=dev),
+            kn=synth.normal((steps, B, Hkv, d), args.seed, w.name, layer, "kn", dtype=w.dtype, device=dev),
+            vn=synth.normal((steps, B, Hkv, d), args.seed, w.name, layer, "vn", dtype=w.dtype, device=dev),
+            window=w.window if layer in w.window_layers else 0))
+    lens_s = [torch.tensor([L + s for L in base], dtype=torch.int32, device=dev) for s in range(steps)]
+    slots_s = [torch.tensor([synth.slot_of(bt, b, L + s - 1, P) for b, L in enumerate(base)],
+                            dtype=torch.int32, device=dev) for s in range(steps)]
+    mcl = max(cap)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, max(pkv.workspace_size(layers[0]["k"], B, Hq, mcl, window=ly["window"],
+                                                     num_sinks=w.sinks) for ly in layers)),
+                     dtype=torch.uint8, device=dev)
+    hip = HipEvents()
+
+    def step(s, evs=None):
+        for li, ly in enumerate(layers):
+            pkv.kv_cache_append(ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], slots_s[s])
+            pkv.paged_decode_attention(ly["q"], ly["k"], ly["v"], gbt, lens_s[s], max_context_len=mcl,
+                                       window=ly["window"], num_sinks=w.sinks if ly["window"] else 0,
+                                       out=out, lse=lse, workspace=ws,
+                                       timing=None if evs is None else evs[li])
+
+    reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
+    for s in range(min(steps, 4)):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [[(hip.create(), hip.create()) for _ in layers] for _ in range(reps * steps)]
+    t0 = time.perf_counter()
+    i = 0
+    for _ in range(reps):
+        for s in range(steps):
+            step(s, evs[i])
+            i += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_steps = reps * steps
+    bytes_total = 0
+    full_us, win_us = [], []
+    for s_i in range(n_steps):
+        s = s_i % steps
+        for li, ly in enumerate(layers):
+            ms = hip.elapsed_ms(*evs[s_i][li])
+            if ly["window"]:
+                att = sum(min(L + s, ly["window"] + min(w.sinks, L + s)) for L in base)
+                win_us.append(ms * 1e3)
+            else:
+                att = sum(L + s for L in base)
+                full_us.append(ms * 1e3)
+            bytes_total += att * w.kv_bytes_per_token()
+    for e in evs:
+        for a, b in e:
+            hip.destroy(a)
+            hip.destroy(b)
+    step_ms = elapsed * 1e3 / n_steps
+    res = {
+        "metric": METRIC, "value": round(bytes_total / elapsed / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": n_steps, "warmup": min(steps, 4), "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "block_size": P, "layers": w.layers, "decode_steps": steps,
+                   "context_at_first_step": f"{min(base)}..{max(base)}",
+                   "window_layers": len(w.window_layers), "window": w.window, "sinks": w.sinks,
+                   "step": "per layer: append B tokens + paged_decode_attention",
+                   "parallelism": "single GPU"},
+        "full_steps_per_s": round(1e3 / step_ms, 2),
+        "layer_steps_per_s": round(1e3 / step_ms * w.layers, 1),
+        "attention_us_full_layer_mean": round(statistics.fmean(full_us), 2) if full_us else None,
+        "attention_us_window_layer_mean": round(statistics.fmean(win_us), 2) if win_us else None,
+        "hbm_frac_of_peak": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if full_us:
+        per_layer_bytes = sum(base) * w.kv_bytes_per_token()  # first step's full-layer bytes
+        res["attention_full_layer_GBps_at_step1"] = round(per_layer_bytes / (min(full_us) * 1e3), 1)
+    return res
+
+
+def run_page_selected(w, args, dev):
+    """Page-selected decode: every step appends the new token and attends to 16 pages of each
+    sequence (the newest page plus 15 distinct earlier ones), a fresh list per step."""
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
+    lens = [w.ctx_lo] * B
+    bt, nb = synth.block_tables(lens, P, args.seed, w.name)
+    gk, gv = _layer_caches(w, lens, P, args.seed, dev, "pages", bt)
+    n_lists = 64
+    lists = [synth.page_lists(lens, P, w.pages_per_step, args.seed, w.name, i).to(dev) for i in range(n_lists)]
+    q = synth.normal((B, Hq, d), args.seed, w.name, "q", dtype=w.dtype, device=dev)
+    kn = synth.normal((B, Hkv, d), args.seed, w.name, "kn", dtype=w.dtype, device=dev)
+    vn = synth.normal((B, Hkv, d), args.seed, w.name, "vn", dtype=w.dtype, device=dev)
+    slots = torch.tensor([synth.slot_of(bt, b, L - 1, P) for b, L in enumerate(lens)], dtype=torch.int32,
+                         device=dev)
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    gbt = bt.to(dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, pkv.workspace_size(gk, B, Hq, max(lens), page_list=lists[0])),
+                     dtype=torch.uint8, device=dev)
+    hip = HipEvents()
+
+    def step(i, ev=None):
+        pkv.kv_cache_append(gk, gv, kn, vn, slots)
+        pkv.paged_decode_attention(q, gk, gv, gbt, cl, max_context_len=max(lens), page_list=lists[i % n_lists],
+                                   out=out, lse=lse, workspace=ws, timing=ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = sorted(hip.elapsed_ms(a, b) for a, b in evs)
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    att_bytes = B * w.pages_per_step * P * w.kv_bytes_per_token()
+    step_ms = elapsed * 1e3 / args.steps
+    kmean = statistics.fmean(kern)
+    return {
+        "metric": METRIC, "value": round(att_bytes / (step_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "block_size": P, "context": lens[0], "pages_per_step": w.pages_per_step,
+                   "page_lists": n_lists, "pool_bytes": 2 * gk.numel() * gk.element_size(),
+                   "step": "append B tokens + paged_decode_attention over the step's page list",
+                   "parallelism": "single GPU"},
+        "hbm_frac_of_peak": round(att_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "steps_per_s_per_layer": round(1e3 / step_ms, 1),
+        "attention_kernel_us_mean": round(kmean * 1e3, 3),
+        "attention_kernel_GBps": round(att_bytes / (kmean * 1e-3) / 1e9, 2),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -195,10 +381,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
-    if w.layers != 1 or w.pages_per_step or w.window:
-        print(f"bench.py: workload {w.name} is a parity workload; the benchmark line is the "
-              "single-layer llama3_8b_layer_bf16 workload", file=sys.stderr)
-        sys.exit(2)
+    if w.layers > 1:
+        print(json.dumps(run_multilayer(w, args, dev)), flush=True)
+        return
+    if w.pages_per_step:
+        print(json.dumps(run_page_selected(w, args, dev)), flush=True)
+        return
     lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
     kv_bytes = sum(lens) * w.kv_bytes_per_token()
 

@@ -11,7 +11,9 @@ namespace {
 using namespace pkv;
 
 constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 256 CUs
-constexpr int kStreamChunkMin = 8;       // minimum units per wave in the persistent kernel
+constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persistent kernel: small
+                                         // problems spread over many waves (one wave streams only
+                                         // a few GB/s, so bandwidth comes from wave count)
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
