@@ -4,9 +4,8 @@
 Default workload: one Llama-3-8B-shaped attention layer at decode time — batch 32,
 32 query / 8 kv heads (GQA 4), head_dim 128, bf16 cache, 16-token blocks, context
 lengths drawn uniformly from [1024, 4096], random block tables. One step is the whole
-hot path over one batch: the append of the 32 new tokens (kv_cache_append), the split-K
-attention kernel and the log-sum-exp combine (exactly the two kernels
-paged_decode_attention launches). Several replica caches (own pools, tables, queries)
+hot path over one batch: paged_decode_append_attention, i.e. the append of the 32 new
+tokens fused into the persistent split-K attention kernel, then the log-sum-exp combine. Several replica caches (own pools, tables, queries)
 are cycled so that consecutive steps never find their K/V in the 256 MB last-level
 cache; every replica has the same context lengths, so the bytes per step are fixed.
 
@@ -236,11 +235,10 @@ def run_multilayer(w, args, dev):
 
     def step(s, evs=None):
         for li, ly in enumerate(layers):
-            pkv.kv_cache_append(ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], slots_s[s])
-            pkv.paged_decode_attention(ly["q"], ly["k"], ly["v"], gbt, lens_s[s], max_context_len=mcl,
-                                       window=ly["window"], num_sinks=w.sinks if ly["window"] else 0,
-                                       out=out, lse=lse, workspace=ws,
-                                       timing=None if evs is None else evs[li])
+            pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], slots_s[s],
+                                              gbt, lens_s[s], max_context_len=mcl, window=ly["window"],
+                                              num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
+                                              workspace=ws, timing=None if evs is None else evs[li])
 
     reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
     for s in range(min(steps, 4)):
@@ -283,7 +281,7 @@ def run_multilayer(w, args, dev):
                    "block_size": P, "layers": w.layers, "decode_steps": steps,
                    "context_at_first_step": f"{min(base)}..{max(base)}",
                    "window_layers": len(w.window_layers), "window": w.window, "sinks": w.sinks,
-                   "step": "per layer: append B tokens + paged_decode_attention",
+                   "step": "per layer: paged_decode_append_attention (append fused into attention)",
                    "parallelism": "single GPU"},
         "full_steps_per_s": round(1e3 / step_ms, 2),
         "layer_steps_per_s": round(1e3 / step_ms * w.layers, 1),
@@ -325,9 +323,9 @@ def run_page_selected(w, args, dev):
     hip = HipEvents()
 
     def step(i, ev=None):
-        pkv.kv_cache_append(gk, gv, kn, vn, slots)
-        pkv.paged_decode_attention(q, gk, gv, gbt, cl, max_context_len=max(lens), page_list=lists[i % n_lists],
-                                   out=out, lse=lse, workspace=ws, timing=ev)
+        pkv.paged_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
+                                          page_list=lists[i % n_lists], out=out, lse=lse, workspace=ws,
+                                          timing=ev)
 
     for i in range(args.warmup):
         step(i)
@@ -353,7 +351,7 @@ def run_page_selected(w, args, dev):
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "block_size": P, "context": lens[0], "pages_per_step": w.pages_per_step,
                    "page_lists": n_lists, "pool_bytes": 2 * gk.numel() * gk.element_size(),
-                   "step": "append B tokens + paged_decode_attention over the step's page list",
+                   "step": "paged_decode_append_attention over the step's page list",
                    "parallelism": "single GPU"},
         "hbm_frac_of_peak": round(att_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "steps_per_s_per_layer": round(1e3 / step_ms, 1),
@@ -410,10 +408,11 @@ def main():
     hip = HipEvents()
 
     def step(rep, ev=None):
-        pkv.kv_cache_append(rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"])
-        pkv.paged_decode_attention(rep["q"], rep["k"], rep["v"], rep["bt"], rep["cl"],
-                                   max_context_len=mcl, split_tokens=args.split_tokens, out=out,
-                                   lse=lse, workspace=workspace, timing=ev)
+        # one decode step of the layer: append of the 32 new tokens + attention, fused
+        pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
+                                          rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
+                                          split_tokens=args.split_tokens, out=out, lse=lse,
+                                          workspace=workspace, timing=ev)
 
     for i in range(args.warmup):
         step(reps[i % len(reps)])
@@ -455,15 +454,16 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
             "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
             "replicas": args.replicas, "split_tokens": args.split_tokens,
-            "step": "append 32 tokens + paged_decode_attention (persistent split kernel + LSE combine)",
+            "step": "paged_decode_append_attention: append of the 32 new tokens fused into the "
+                    "persistent split kernel, then the LSE combine",
             "parallelism": "single GPU",
         },
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": "decode_stream_kernel<BF16,128,full>" if args.split_tokens == 0
-            else "decode_split_kernel<BF16,128,full>",
+            "bound": "hbm", "kernel": "decode_stream_kernel<BF16,128,full,fused append>"
+            if args.split_tokens == 0 else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name, args.split_tokens), "traffic_unit": "bytes per launch",

@@ -180,6 +180,36 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc /* host */,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* paged_decode_append_attention — one decode step of one layer in one pass: the append of
+ * the batch's new tokens followed by attention over the updated cache ([primer] §2.2;
+ * [naive] §"KV cache的思想": each step writes the new token's K/V, then attends over all).
+ * Same result as kv_cache_append(desc, k_cache, v_cache, k_new, v_new, slot_mapping, batch)
+ * followed by paged_decode_attention(...) with the same arguments: the same cache contents
+ * and the same outputs. On the work-split path of paged_decode_attention both happen in one
+ * kernel (plus the combine): the cache write is spread over its wavefronts and the new token
+ * enters attention from k_new/v_new directly.
+ *   k_new, v_new:  [batch][num_kv_heads][head_dim], row b = sequence b's new token.
+ *   slot_mapping:  [batch] int32, the slot of position context_lens[b] - 1 of sequence b
+ *                  (block_table[b][(L-1)/P] * P + (L-1) % P); < 0 skips the write.
+ * Precondition: slot_mapping[b] >= 0 is that slot whenever context_lens[b] > 0 (with a
+ * negative slot the new token's values are still the ones attended). Other arguments as in
+ * paged_decode_attention; the workspace size is the same. */
+pkv_status paged_decode_append_attention(const pkv_cache_desc* desc /* host */,
+                                         void* k_cache, void* v_cache,
+                                         const void* k_new, const void* v_new,
+                                         const int32_t* slot_mapping,
+                                         const void* q,
+                                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens,
+                                         int32_t batch, int32_t num_q_heads,
+                                         int32_t max_context_len,
+                                         float scale,
+                                         const pkv_decode_opts* opts /* host, nullable */,
+                                         void* out, pkv_dtype out_dtype,
+                                         float* lse_out,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Bytes of workspace paged_decode_attention needs for these arguments (0 when
  * the call would need none). Returns 0 as well for arguments that the call
  * would reject; pure host function. */

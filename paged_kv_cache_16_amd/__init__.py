@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = [
-    "kv_cache_append", "paged_decode_attention", "paged_decode_attention_partial",
+    "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
+    "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
     "PagedKVError", "LIB_PATH",
 ]
@@ -57,6 +58,10 @@ _lib.kv_cache_append.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
 _lib.paged_decode_attention.restype = ctypes.c_int
 _lib.paged_decode_attention.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
                                         _P_OPTS, _vp, ctypes.c_int, _vp, _vp, _sz, _vp]
+_lib.paged_decode_append_attention.restype = ctypes.c_int
+_lib.paged_decode_append_attention.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                               _i32, _i32, _f32, _P_OPTS, _vp, ctypes.c_int, _vp, _vp, _sz,
+                                               _vp]
 _lib.paged_decode_attention_workspace_size.restype = _sz
 _lib.paged_decode_attention_workspace_size.argtypes = [_P_DESC, _i32, _i32, _i32, _P_OPTS]
 _lib.paged_decode_attention_num_splits.restype = _i32
@@ -181,6 +186,39 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
         _dev(q, "q", k_cache.dtype), _dev(block_table, "block_table", torch.int32),
         block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq,
         int(max_context_len), float(scale), ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
+        _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q)))
+    return out, lse
+
+
+def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table,
+                                  context_lens, *, max_context_len: int, scale: float = 0.0,
+                                  window: int = 0, num_sinks: int = 0, page_list=None,
+                                  split_tokens: int = 0, out=None, out_dtype=None, lse=None,
+                                  workspace=None, want_lse: bool = True, timing=None):
+    """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
+    slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse)."""
+    desc = cache_desc(k_cache)
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing)
+    ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
+                                                              ctypes.byref(o)))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if k_new.shape[0] != B or slot_mapping.numel() != B:
+        raise ValueError("one new token per sequence: k_new/v_new [B, Hkv, d], slot_mapping [B]")
+    _check("paged_decode_append_attention", _lib.paged_decode_append_attention(
+        ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", k_cache.dtype),
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, int(max_context_len), float(scale),
+        ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
         _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q)))
     return out, lse
 

@@ -262,12 +262,25 @@ int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc, int32_t ba
     return make_plan(desc, batch, max_context_len, -1, opts).num_splits;
 }
 
-pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
-                                  const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
-                                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-                                  int32_t max_context_len, float scale, const pkv_decode_opts* opts,
-                                  void* out, pkv_dtype out_dtype, float* lse_out, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct FusedAppend {
+    void* k_cache;
+    void* v_cache;
+    const void* k_new;
+    const void* v_new;
+    const int32_t* slots;
+};
+
+// paged_decode_attention, optionally preceded by the append of one new token per sequence
+// (fused into the persistent kernel on its path, a separate append launch otherwise).
+pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache, const void* q,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                       const pkv_decode_opts* opts, void* out, pkv_dtype out_dtype, float* lse_out,
+                       void* workspace, size_t workspace_bytes, void* stream, const FusedAppend* fa) {
     pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq,
                                       context_lens, batch, num_q_heads, max_context_len, opts);
     if (st != PKV_OK) return st;
@@ -288,14 +301,12 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
     const hipStream_t s = (hipStream_t)stream;
     hipEvent_t ev0 = opts ? (hipEvent_t)opts->timing_start : nullptr;
     hipEvent_t ev1 = opts ? (hipEvent_t)opts->timing_stop : nullptr;
-    if (pl.path == Plan::kDirect) {
-        if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
-        st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
-        if (st == PKV_OK && ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
-        return st;
+
+    // Validate the workspace and finish the launch parameters before anything is enqueued.
+    long long waves = 0;
+    if (pl.path != Plan::kDirect) {
+        if (!workspace || ((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
     }
-    if (!workspace) return PKV_ERR_WORKSPACE;
-    if (((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
     if (pl.path == Plan::kStream) {
         const int G = num_q_heads / desc->num_kv_heads;
         const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim);
@@ -306,7 +317,7 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
         if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
         const long long resident =
             (long long)device_cus(dev) * device_occupancy(dev, desc->dtype, desc->head_dim, pl.mode) * kWaves;
-        long long waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
+        waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
         if (waves > resident) waves = resident;
         waves = (waves + kWaves - 1) / kWaves * kWaves;
         p.o_part = (float*)((char*)workspace + wl.o_off);
@@ -317,13 +328,46 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
         p.waves_total = (int)waves;
         p.chunk_min = pl.chunk_min;
         p.kmax = pl.kmax;
-        return hip_status(launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, p, s, ev0, ev1));
+    } else if (pl.path == Plan::kPartitions) {
+        const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
+        if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
+        p.o_part = (float*)((char*)workspace + wl.o_off);
+        p.m_part = (float*)((char*)workspace + wl.m_off);
+        p.l_part = (float*)((char*)workspace + wl.l_off);
     }
-    const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
-    if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
-    p.o_part = (float*)((char*)workspace + wl.o_off);
-    p.m_part = (float*)((char*)workspace + wl.m_off);
-    p.l_part = (float*)((char*)workspace + wl.l_off);
+
+    if (fa && pl.path != Plan::kStream) {  // separate append launch ahead of attention
+        AppendParams ap;
+        ap.k_cache = fa->k_cache;
+        ap.v_cache = fa->v_cache;
+        ap.k_new = fa->k_new;
+        ap.v_new = fa->v_new;
+        ap.slots = fa->slots;
+        ap.num_tokens = batch;
+        ap.num_slots = (int64_t)desc->num_blocks * desc->block_size;
+        ap.block_size = desc->block_size;
+        ap.kv_heads = desc->num_kv_heads;
+        ap.head_dim = desc->head_dim;
+        st = hip_status(launch_append(desc->dtype, ap, s));
+        if (st != PKV_OK) return st;
+    }
+    if (pl.path == Plan::kDirect) {
+        if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
+        st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
+        if (st == PKV_OK && ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
+        return st;
+    }
+    if (pl.path == Plan::kStream) {
+        if (fa) {
+            p.k_cache_w = (char*)fa->k_cache;
+            p.v_cache_w = (char*)fa->v_cache;
+            p.k_new = (const char*)fa->k_new;
+            p.v_new = (const char*)fa->v_new;
+            p.new_slots = fa->slots;
+            p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
+        }
+        return hip_status(launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, fa != nullptr, p, s, ev0, ev1));
+    }
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
     st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch, s));
     if (st != PKV_OK) return st;
@@ -339,6 +383,38 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
     cp.head_dim = desc->head_dim;
     cp.out_dtype = out_dtype;
     return hip_status(launch_combine(cp, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_context_len, float scale, const pkv_decode_opts* opts,
+                                  void* out, pkv_dtype out_dtype, float* lse_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return decode_impl(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens, batch,
+                       num_q_heads, max_context_len, scale, opts, out, out_dtype, lse_out, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+pkv_status paged_decode_append_attention(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                                         const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                         const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                         int32_t max_context_len, float scale, const pkv_decode_opts* opts,
+                                         void* out, pkv_dtype out_dtype, float* lse_out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (batch > 0 && (!k_new || !v_new || !slot_mapping)) {
+        const pkv_status st = check_desc(desc);
+        return st != PKV_OK ? st : PKV_ERR_NULL;
+    }
+    const FusedAppend fa = {k_cache, v_cache, k_new, v_new, slot_mapping};
+    return decode_impl(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens, batch,
+                       num_q_heads, max_context_len, scale, opts, out, out_dtype, lse_out, workspace,
+                       workspace_bytes, stream, &fa);
 }
 
 pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void* k_cache,

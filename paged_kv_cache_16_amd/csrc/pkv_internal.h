@@ -60,6 +60,13 @@ struct DecodeParams {
     int32_t chunk_min;     // minimum units per wave
     int32_t kmax;          // partial slots per (sequence, kv head) segment
     int32_t* seg_count;    // [B*Hkv]: partials written for the segment; 0 = final row written
+    // fused decode step only: the batch's new rows ([B][Hkv][D]) and their slots ([B])
+    char* k_cache_w;
+    char* v_cache_w;
+    const char* k_new;
+    const char* v_new;
+    const int32_t* new_slots;
+    int64_t num_slots;
 };
 
 struct CombineParams {
@@ -79,8 +86,8 @@ hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const D
                          int batch, hipStream_t s);
 // Persistent stream kernel + its combine (the paged_decode_attention path). Events, when
 // non-null, are recorded around the stream kernel.
-hipError_t launch_decode_stream(int dtype, int head_dim, int mode, const DecodeParams& p, hipStream_t s,
-                                hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, const DecodeParams& p,
+                                hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 int stream_blocks_per_cu(int dtype, int head_dim, int mode);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

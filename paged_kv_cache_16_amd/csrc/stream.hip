@@ -108,7 +108,98 @@ __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>&
     }
 }
 
-template <class DT, int D, int MODE>
+// Cache write of the fused decode step, one new row (sequence b, kv head h) per call: stored
+// at slot new_slots[b] in the cache's lane-chunk order. The combine kernel does it after the
+// attention kernel, which took the new token from k_new/v_new directly; nothing reads the
+// slot in between.
+template <int ES, int D>
+__device__ __forceinline__ void write_new_row(const DecodeParams& p, int r, int lane) {
+    constexpr int E = 16 / ES, R = E / 4;
+    const int b = r / p.kv_heads, h = r - b * p.kv_heads;
+    const int64_t slot = p.new_slots[b];
+    if (slot < 0 || slot >= p.num_slots) return;
+    const int64_t blk = slot / p.block_size;
+    const int t = (int)(slot - blk * p.block_size);
+    const int tau = t & 15;
+    const size_t sub = (((size_t)blk * p.kv_heads + h) * p.block_size + (t - tau)) * D;
+    const size_t src = (size_t)r * D;
+    if (lane < D / E) {  // K: one whole 16-byte chunk per lane
+        const size_t chunk = (size_t)(lane >> 2) * 64 + (size_t)(lane & 3) * 16 + tau;
+        *reinterpret_cast<u32x4*>(p.k_cache_w + (sub + chunk * E) * ES) = load16(p.k_new + (src + lane * E) * ES);
+    }
+    for (int x = lane; x < D; x += 64) {  // V: element by element
+        const int n = x >> 4;
+        const size_t chunk = ((size_t)(n / R) * 4 + (tau >> 2)) * 16 + (x & 15);
+        const size_t pos = (size_t)(n % R) * 4 + (tau & 3);
+        if constexpr (ES == 2)
+            *reinterpret_cast<unsigned short*>(p.v_cache_w + (sub + chunk * E + pos) * 2) =
+                *reinterpret_cast<const unsigned short*>(p.v_new + (src + x) * 2);
+        else
+            *reinterpret_cast<unsigned*>(p.v_cache_w + (sub + chunk * E + pos) * 4) =
+                *reinterpret_cast<const unsigned*>(p.v_new + (src + x) * 4);
+    }
+}
+
+// The new token's values as lane (j, c) holds them in a tile: K chunks of token c (dims
+// kk*4E + j*E ..), and the V elements of dims 16n + c. Loaded once per run of the fused step.
+template <class DT, int D>
+struct NewRow {
+    static constexpr int NC = D / (4 * DT::kE);
+    static constexpr int NV = D / 16;  // V dims 16n + c, n < D/16
+    u32x4 k[NC];
+    unsigned v[NV];  // raw element bits (low 16 bits for 2-byte types)
+};
+
+template <class DT, int D>
+__device__ __forceinline__ void load_new_row(const DecodeParams& p, NewRow<DT, D>& nr, int b, int kvh, int j,
+                                             int c) {
+    constexpr int E = DT::kE, ES = DT::kBytes;
+    const size_t src = ((size_t)b * p.kv_heads + kvh) * D;
+#pragma unroll
+    for (int kk = 0; kk < NewRow<DT, D>::NC; ++kk) nr.k[kk] = load16(p.k_new + (src + kk * 4 * E + j * E) * ES);
+#pragma unroll
+    for (int n = 0; n < NewRow<DT, D>::NV; ++n) {
+        if constexpr (ES == 2)
+            nr.v[n] = *reinterpret_cast<const unsigned short*>(p.v_new + (src + 16 * n + c) * 2);
+        else
+            nr.v[n] = *reinterpret_cast<const unsigned*>(p.v_new + (src + 16 * n + c) * 4);
+    }
+}
+
+// Replaces token tau of a loaded tile by the new row (lanes that hold it).
+template <class DT, int D>
+__device__ __forceinline__ void patch_tile(u32x4 (&k)[D / (4 * DT::kE)], u32x4 (&v)[D / (4 * DT::kE)],
+                                          const NewRow<DT, D>& nr, int tau, int j, int c) {
+    constexpr int NC = D / (4 * DT::kE);
+    constexpr int R = DT::kE / 4;
+    if (c == tau) {
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) k[kk] = nr.k[kk];
+    }
+    if (j == (tau >> 2)) {
+        const int i = tau & 3;
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+            // token 4j+i of dim 16n + c is element (n % R) * 4 + i of chunk n / R
+            if constexpr (DT::kBytes == 2) {
+                const int target = (n % R) * 2 + (i >> 1);  // dword holding the element
+                const bool high = i & 1;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const unsigned wd = v[n / R][w];
+                    const unsigned upd = high ? ((wd & 0x0000ffffu) | (nr.v[n] << 16))
+                                              : ((wd & 0xffff0000u) | (nr.v[n] & 0xffffu));
+                    v[n / R][w] = w == target ? upd : wd;
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[n][w] = w == i ? nr.v[n] : v[n][w];
+            }
+        }
+    }
+}
+
+template <class DT, int D, int MODE, bool FUSED>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
     using T = Tile<DT, D / (4 * DT::kE)>;
@@ -183,9 +274,13 @@ void decode_stream_kernel(DecodeParams p) {
         f32x4 acc[NACC];
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[a] = zero4();
+        NewRow<DT, D> nrow;
+        const int t_new = sp.L - 1;  // the token this step appended
+        if (FUSED) load_new_row<DT, D>(p, nrow, b, kvh, j, c);
 
         auto process = [&](RingBuf<DT, D>& rb) __attribute__((always_inline)) {
             if (rb.t0 < 0) return;
+            if (FUSED && (unsigned)(t_new - rb.t0) < 16u) patch_tile<DT, D>(rb.k, rb.v, nrow, t_new - rb.t0, j, c);
             f32x4 s = zero4();
             T::qk(s, rb.k, q);
             const unsigned keep = token_keep(sp, rb.t0, j);
@@ -296,10 +391,11 @@ void decode_stream_kernel(DecodeParams p) {
 // lane owns D/64 dims and fetches its slices of all partial rows in unrolled batches.
 // Rows of sequences without units get out = 0 and lse = -inf here; rows the stream kernel
 // finished itself (count 0) are skipped.
-template <int D, int MODE>
+template <int D, int MODE, int ES>
 __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;
     const int r = blockIdx.x;
+    if (p.new_slots && r < p.batch * p.kv_heads) write_new_row<ES, D>(p, r, threadIdx.x);
     const int G = p.group;
     const int g = r / G, head = r - g * G;
     const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
@@ -365,52 +461,57 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
 }
 
 template <class DT, int D, int MODE>
-static hipError_t launch_stream_t(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+static hipError_t launch_stream_t(bool fused, const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const unsigned blocks = (unsigned)(p.waves_total / kWaves);
     if (e0) {
         hipError_t e = hipEventRecord(e0, s);
         if (e != hipSuccess) return e;
     }
-    decode_stream_kernel<DT, D, MODE><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
+    if (fused)
+        decode_stream_kernel<DT, D, MODE, true><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
+    else
+        decode_stream_kernel<DT, D, MODE, false><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (e1) {
         err = hipEventRecord(e1, s);
         if (err != hipSuccess) return err;
     }
-    stream_combine_kernel<D, MODE><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
+    stream_combine_kernel<D, MODE, DT::kBytes><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
     return hipGetLastError();
 }
 
 template <class DT, int D>
-static hipError_t launch_stream_m(int mode, const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+static hipError_t launch_stream_m(int mode, bool fused, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
     switch (mode) {
-        case kWindow: return launch_stream_t<DT, D, kWindow>(p, s, e0, e1);
-        case kPages: return launch_stream_t<DT, D, kPages>(p, s, e0, e1);
-        default: return launch_stream_t<DT, D, kFull>(p, s, e0, e1);
+        case kWindow: return launch_stream_t<DT, D, kWindow>(fused, p, s, e0, e1);
+        case kPages: return launch_stream_t<DT, D, kPages>(fused, p, s, e0, e1);
+        default: return launch_stream_t<DT, D, kFull>(fused, p, s, e0, e1);
     }
 }
 
 template <class DT>
-static hipError_t launch_stream_d(int head_dim, int mode, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
-                                  hipEvent_t e1) {
-    return head_dim == 64 ? launch_stream_m<DT, 64>(mode, p, s, e0, e1) : launch_stream_m<DT, 128>(mode, p, s, e0, e1);
+static hipError_t launch_stream_d(int head_dim, int mode, bool fused, const DecodeParams& p, hipStream_t s,
+                                  hipEvent_t e0, hipEvent_t e1) {
+    return head_dim == 64 ? launch_stream_m<DT, 64>(mode, fused, p, s, e0, e1)
+                          : launch_stream_m<DT, 128>(mode, fused, p, s, e0, e1);
 }
 
-hipError_t launch_decode_stream(int dtype, int head_dim, int mode, const DecodeParams& p, hipStream_t s,
-                                hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, const DecodeParams& p,
+                                hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     if (p.batch <= 0 || p.waves_total <= 0) return hipSuccess;
     switch (dtype) {
-        case kF32: return launch_stream_d<F32>(head_dim, mode, p, s, ev_start, ev_stop);
-        case kF16: return launch_stream_d<F16>(head_dim, mode, p, s, ev_start, ev_stop);
-        default: return launch_stream_d<BF16>(head_dim, mode, p, s, ev_start, ev_stop);
+        case kF32: return launch_stream_d<F32>(head_dim, mode, fused, p, s, ev_start, ev_stop);
+        case kF16: return launch_stream_d<F16>(head_dim, mode, fused, p, s, ev_start, ev_stop);
+        default: return launch_stream_d<BF16>(head_dim, mode, fused, p, s, ev_start, ev_stop);
     }
 }
 
 template <class DT, int D, int MODE>
 static int occupancy_t() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE>, 64 * kWaves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, true>, 64 * kWaves, 0) !=
         hipSuccess)
         return 1;
     return n > 0 ? n : 1;

@@ -367,3 +367,48 @@ def test_workspace_reuse():
     for got in outs:
         assert_close(c, got, ref, "workspace reuse")
         assert np.array_equal(got[0], outs[0][0])
+
+
+FUSED_CASES = [
+    dict(name="llama3-shape", B=4, Hq=32, Hkv=8, d=128, dtype="bf16", P=16, lens=[1500, 4096, 17, 2049], kw={}),
+    dict(name="g6-window", B=3, Hq=12, Hkv=2, d=128, dtype="bf16", P=16, lens=[4100, 600, 31],
+         kw=dict(window=512, num_sinks=4)),
+    dict(name="f16-pages", B=2, Hq=8, Hkv=8, d=128, dtype="f16", P=32, lens=[1000, 64], kw="pages"),
+    dict(name="f32-d64", B=2, Hq=4, Hkv=4, d=64, dtype="f32", P=16, lens=[300, 45], kw={}),
+    dict(name="tiny-direct", B=2, Hq=4, Hkv=2, d=128, dtype="bf16", P=16, lens=[100, 7], kw={}),
+    dict(name="partitions", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", P=16, lens=[900, 333], kw=dict(split_tokens=128)),
+]
+
+
+@pytest.mark.parametrize("fc", FUSED_CASES, ids=[f["name"] for f in FUSED_CASES])
+def test_fused_append_attention(fc):
+    """paged_decode_append_attention == kv_cache_append + paged_decode_attention: the cache
+    bytes match the oracle's append bit for bit and the outputs match the oracle."""
+    import paged_kv_cache_16_amd as pkv
+    lens = fc["lens"]
+    log(f"fused {fc['name']}")
+    c = make_case(60, B=fc["B"], Hq=fc["Hq"], Hkv=fc["Hkv"], d=fc["d"], dtype=fc["dtype"], P=fc["P"], lens=lens)
+    # GPU cache: prefill all but each sequence's last token; the fused call appends it
+    c.gk.fill_(float("nan"))
+    c.gv.fill_(float("nan"))
+    pre = synth.token_slots(c.bt, lens, c.P, last=[L - 1 for L in lens])
+    kp = torch.cat([c.K[b, :L - 1] for b, L in enumerate(lens)]).cuda()
+    vp = torch.cat([c.V[b, :L - 1] for b, L in enumerate(lens)]).cuda()
+    pkv.kv_cache_append(c.gk, c.gv, kp, vp, pre.cuda())
+    slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) for b, L in enumerate(lens)], dtype=torch.int32).cuda()
+    kn = torch.stack([c.K[b, L - 1] for b, L in enumerate(lens)]).cuda()
+    vn = torch.stack([c.V[b, L - 1] for b, L in enumerate(lens)]).cuda()
+    kw, okw = fc["kw"], {}
+    if kw == "pages":
+        pl = synth.page_lists(lens, c.P, 6, 60).numpy()
+        kw = dict(page_list=torch.as_tensor(pl).cuda())
+        okw = dict(page_list=pl)
+    elif "window" in kw:
+        okw = dict(window=kw["window"], sinks=kw["num_sinks"])
+    out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
+                                                 max_context_len=max(lens), **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bytes(c.gk), c.kpool.view(np.uint8))
+    assert np.array_equal(raw_bytes(c.gv), c.vpool.view(np.uint8))
+    got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    assert_close(c, got, oracle_attend(c, **okw), f"fused {fc['name']}")
