@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU baseline: run the oracle on whole sequences of the workload until "
                          "this much oracle time is spent (0 = skip)")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record the kernel's HIP events on every n-th call only: an event pair costs "
+                         "the step a few microseconds of queue work, so the step clock runs without most")
+    ap.add_argument("--no-graph", action="store_true", help="multi-layer modes: skip the HIP-graph timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -228,17 +232,21 @@ def run_multilayer(w, args, dev):
     mcl = max(cap)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, max(pkv.workspace_size(layers[0]["k"], B, Hq, mcl, window=ly["window"],
+    ws = torch.zeros(max(256, max(pkv.workspace_size(layers[0]["k"], B, Hq, mcl, window=ly["window"],
                                                      num_sinks=w.sinks) for ly in layers)),
                      dtype=torch.uint8, device=dev)
     hip = HipEvents()
 
-    def step(s, evs=None):
+    every = max(1, args.event_every)
+
+    def step(s, evs=None, s_i=0):
+        # events on the layers with (s_i + layer) % every == 0, so the sample rotates over layers
         for li, ly in enumerate(layers):
+            ev = evs[li] if evs is not None and (s_i + li) % every == 0 else None
             pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], slots_s[s],
                                               gbt, lens_s[s], max_context_len=mcl, window=ly["window"],
                                               num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
-                                              workspace=ws, timing=None if evs is None else evs[li])
+                                              workspace=ws, timing=ev)
 
     reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
     for s in range(min(steps, 4)):
@@ -249,7 +257,7 @@ def run_multilayer(w, args, dev):
     i = 0
     for _ in range(reps):
         for s in range(steps):
-            step(s, evs[i])
+            step(s, evs[i], i)
             i += 1
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -259,19 +267,40 @@ def run_multilayer(w, args, dev):
     for s_i in range(n_steps):
         s = s_i % steps
         for li, ly in enumerate(layers):
-            ms = hip.elapsed_ms(*evs[s_i][li])
             if ly["window"]:
                 att = sum(min(L + s, ly["window"] + min(w.sinks, L + s)) for L in base)
-                win_us.append(ms * 1e3)
             else:
                 att = sum(L + s for L in base)
-                full_us.append(ms * 1e3)
             bytes_total += att * w.kv_bytes_per_token()
+            if (s_i + li) % every:
+                continue
+            us = hip.elapsed_ms(*evs[s_i][li]) * 1e3
+            (win_us if ly["window"] else full_us).append(us)
     for e in evs:
         for a, b in e:
             hip.destroy(a)
             hip.destroy(b)
     step_ms = elapsed * 1e3 / n_steps
+    graph_ms = None
+    if not args.no_graph:
+        # The same steps replayed from HIP graphs: one graph per decode step holding every layer.
+        graphs = []
+        for s in range(steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs[:4]:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for g in graphs:
+                g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / n_steps
+        del graphs
     res = {
         "metric": METRIC, "value": round(bytes_total / elapsed / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": n_steps, "warmup": min(steps, 4), "ms_per_step": round(step_ms, 4),
@@ -285,6 +314,8 @@ def run_multilayer(w, args, dev):
                    "parallelism": "single GPU"},
         "full_steps_per_s": round(1e3 / step_ms, 2),
         "layer_steps_per_s": round(1e3 / step_ms * w.layers, 1),
+        "graph_full_steps_per_s": round(1e3 / graph_ms, 2) if graph_ms else None,
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "attention_us_full_layer_mean": round(statistics.fmean(full_us), 2) if full_us else None,
         "attention_us_window_layer_mean": round(statistics.fmean(win_us), 2) if win_us else None,
         "hbm_frac_of_peak": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBS, 4),
@@ -318,7 +349,7 @@ def run_page_selected(w, args, dev):
     gbt = bt.to(dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, pkv.workspace_size(gk, B, Hq, max(lens), page_list=lists[0])),
+    ws = torch.zeros(max(256, pkv.workspace_size(gk, B, Hq, max(lens), page_list=lists[0])),
                      dtype=torch.uint8, device=dev)
     hip = HipEvents()
 
@@ -330,10 +361,11 @@ def run_page_selected(w, args, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    evs = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = sorted(hip.elapsed_ms(a, b) for a, b in evs)
@@ -404,7 +436,7 @@ def main():
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens)
-    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # arrival counters start at 0
     hip = HipEvents()
 
     def step(rep, ev=None):
@@ -418,12 +450,14 @@ def main():
         step(reps[i % len(reps)])
     torch.cuda.synchronize()
 
-    # HIP events recorded by the library on the launch stream, right around the main kernel.
-    events = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    # HIP events recorded by the library on the launch stream, right around the main kernel,
+    # on every event_every-th step of the timed region.
+    every = max(1, args.event_every)
+    events = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(reps[i % len(reps)], events[i])
+        step(reps[i % len(reps)], events[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -469,7 +503,7 @@ def main():
             "traffic": measured_traffic(w.name, args.split_tokens), "traffic_unit": "bytes per launch",
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
-            "p90_us": round(q(0.9) * 1e3, 3),
+            "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),
         },
     }
     if args.cpu_seconds > 0:

@@ -349,21 +349,29 @@ def test_full_size_page_selected_sampled():
 
 
 def test_workspace_reuse():
-    """One workspace serves any number of calls, which all give the same result (its
-    contents on entry are ignored)."""
+    """One workspace serves any number of calls, which all give the same result: its
+    contents on entry are ignored, also between calls whose plans differ (full and window
+    attention sharing one workspace, as the layers of one model do)."""
     import paged_kv_cache_16_amd as pkv
     lens = [1500, 333, 4000, 2, 0, 129]
     c = make_case(48, B=6, Hq=16, Hkv=4, d=128, dtype="bf16", P=16, lens=lens)
     n = pkv.workspace_size(c.gk, 6, 16, max(lens))
-    assert n > 0
-    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
+    n_w = pkv.workspace_size(c.gk, 6, 16, max(lens), window=300, num_sinks=4)
+    assert n > 0 and n_w > 0
+    ws = torch.full((max(n, n_w),), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
     ref = oracle_attend(c)
+    ref_w = oracle_attend(c, window=300, sinks=4)
     outs = []
     for _ in range(3):
         out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
                                               workspace=ws)
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
+        out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
+                                              window=300, num_sinks=4, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(c, (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)), ref_w,
+                     "workspace reuse, window")
     for got in outs:
         assert_close(c, got, ref, "workspace reuse")
         assert np.array_equal(got[0], outs[0][0])
@@ -412,3 +420,48 @@ def test_fused_append_attention(fc):
     assert np.array_equal(raw_bytes(c.gv), c.vpool.view(np.uint8))
     got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
     assert_close(c, got, oracle_attend(c, **okw), f"fused {fc['name']}")
+
+
+def test_graph_replay_fused_step():
+    """The fused decode step captured in a HIP graph: every replay, with eager calls and
+    synchronisations in between, reproduces the eager result bit for bit (the work split
+    and the merge order are fixed by the arguments, not by timing), and the eager result
+    matches the oracle."""
+    import paged_kv_cache_16_amd as pkv
+    lens = [1500, 333, 4000, 2, 0, 129]
+    B, Hq, Hkv = 6, 16, 4
+    c = make_case(49, B=B, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", P=16, lens=lens)
+    # the new row of each sequence is its last token, already in the cache: rewriting it is a no-op
+    slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) if L > 0 else -1 for b, L in enumerate(lens)],
+                         dtype=torch.int32).cuda()
+    kn = torch.stack([c.K[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    vn = torch.stack([c.V[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    ws = torch.empty(pkv.workspace_size(c.gk, B, Hq, max(lens)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl, max_context_len=max(lens),
+                                          out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    assert_close(c, (ref[0].cpu().numpy().astype(np.float64), ref[1].cpu().numpy().astype(np.float64)),
+                 oracle_attend(c), "graph: eager step")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    ws2 = torch.empty(pkv.workspace_size(c.gk, B, Hq, max(lens), window=300, num_sinks=4), dtype=torch.uint8,
+                      device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {i} differs from the eager step"
+        # eager work between replays, on another workspace and with another plan
+        pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens), window=300,
+                                   num_sinks=4, workspace=ws2)
+        torch.cuda.synchronize()
