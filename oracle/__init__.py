@@ -82,6 +82,9 @@ class Oracle:
         L.oracle_decode_attention_split.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _P, _I, _I,
                                                     _P, _I, _P, _D, _I, _I, _P, _I, _I, _I, _P,
                                                     _P, _P, _P, _P]
+        L.oracle_decode_scores.restype = _I
+        L.oracle_decode_scores.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P, _D, _I,
+                                           _I, _P, _I, _P, _I64]
         L.oracle_bruteforce.restype = _I
         L.oracle_bruteforce.argtypes = [_I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _D, _I, _I, _I,
                                         _P, _I, _P, _P]
@@ -138,6 +141,23 @@ class Oracle:
             mb, _ptr(cl), float(scale), int(window), int(sinks), _ptr(pl), pps, _ptr(out),
             _ptr(lse)), "decode_attention")
         return out, lse
+
+    def decode_scores(self, dtype, kpool, q, block_table, context_lens, *, P, Hkv, d, stride,
+                      scale=0.0, window=0, sinks=0, page_list=None, score=None):
+        """Adds one step's scores into `score` ([B][Hkv][stride] float64, zeros when None) and
+        returns it."""
+        kpool, _, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
+            dtype, kpool, kpool, q, block_table, context_lens, P, Hkv, d, page_list)
+        if score is None:
+            score = np.zeros((B, Hkv, stride), np.float64)
+        score = np.ascontiguousarray(score, dtype=np.float64)
+        if score.shape != (B, Hkv, stride):
+            raise ValueError(f"score must be [{B}][{Hkv}][{stride}], got {score.shape}")
+        self._check(self.lib.oracle_decode_scores(
+            DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool), _ptr(q), B, Hq, _ptr(bt), mb, _ptr(cl),
+            float(scale), int(window), int(sinks), _ptr(pl), pps, _ptr(score), int(stride)),
+            "decode_scores")
+        return score
 
     def decode_attention_split(self, dtype, kpool, vpool, q, block_table, context_lens, *, P,
                                Hkv, d, units, max_splits, scale=0.0, window=0, sinks=0,
@@ -211,6 +231,10 @@ def decode_attention(*a, **k):
 
 def decode_attention_split(*a, **k):
     return default().decode_attention_split(*a, **k)
+
+
+def decode_scores(*a, **k):
+    return default().decode_scores(*a, **k)
 
 
 def bruteforce(*a, **k):

@@ -17,7 +17,8 @@
  *   [OVAL]   "OVAL — Output-Aware Local Page Bases for KV Cache Retrieval" (2kiu.com):
  *            §2.2/§3.3 per-step page base indices; §3.2 window clamps.
  *   [Novita] "How KV Sparsity Achieves 1.5x Acceleration for vLLM": §關鍵技術 1 per-layer
- *            full cache or sliding window; §關鍵技術 2 online softmax keeping rowmax and l.
+ *            full cache or sliding window; §關鍵技術 2 online softmax keeping rowmax and l,
+ *            and the per-token sparsification score built from them.
  *   [TF]     "Transformer模型中的KV Cache优化推理策略": §"为什么传统推理方式难以为继？"
  *            Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V.
  *
@@ -28,7 +29,9 @@
  *     "sink" tokens, each token once; W >= L is full attention;
  *   - page_list entries are logical page ids per sequence, shared by all heads,
  *     translated through the block table; entries < 0 are padding;
- *   - L == 0 gives out = 0 and lse = -inf.
+ *   - L == 0 gives out = 0 and lse = -inf;
+ *   - a token's score sums the softmax probabilities of the query heads that share its
+ *     kv head (the cache is per kv head), one query per head per decode step.
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms,
  * invariants, brute force, the primer's worked KV-size values); none is unpinned.
@@ -244,6 +247,56 @@ int oracle_decode_attention(int dt, int64_t num_blocks, int P, int Hkv, int d,
             }
             for (int x = 0; x < d; ++x) o[x] /= z;
             lse[(size_t)b * Hq + h] = m + log(z);
+        }
+        free(logits);
+        free(toks);
+    }
+    return ORC_OK;
+}
+
+/* Decode-time KV scores ([Novita] §關鍵技術 2: the sparsification score of a token in a
+ * head is the sum, over recent queries, of its softmax probability
+ * p = exp(q.k - rowmax) / l, which the attention pass already has the rowmax and l for).
+ * One decode step contributes its single query per head: for every sequence b, kv head
+ * kvh and attended token t,
+ *     score[b][kvh][t] += sum over the G query heads h of kvh of softmax_h(t),
+ * with softmax_h the attention weights of oracle_decode_attention. Tokens that are not
+ * attended are left as they are, so a caller accumulates over steps by passing the same
+ * array again. score: [B][Hkv][stride] doubles; every attended t must be < stride. */
+int oracle_decode_scores(int dt, int64_t num_blocks, int P, int Hkv, int d,
+                         const void* kpool, const void* q, int B, int Hq,
+                         const int32_t* block_table, int max_blocks,
+                         const int32_t* context_lens, double scale,
+                         int window, int sinks, const int32_t* page_list, int pps,
+                         double* score, int64_t stride) {
+    if (!common_args_ok(dt, num_blocks, P, Hkv, d, B, Hq, max_blocks, window, sinks,
+                        page_list, pps) || stride < 0)
+        return ORC_ERR_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        int L = context_lens[b];
+        if (L < 0) return ORC_ERR_PRECONDITION;
+        const int32_t* pages = page_list ? page_list + (size_t)b * pps : NULL;
+        if (pages && !pages_ok(pages, pps)) return ORC_ERR_PRECONDITION;
+        double* logits = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+        if (!logits || !toks) { free(logits); free(toks); return ORC_ERR_NOMEM; }
+        for (int h = 0; h < Hq; ++h) {
+            int64_t cnt = gather_logits(dt, num_blocks, P, Hkv, d, kpool, q, Hq, b, h,
+                                        block_table + (size_t)b * max_blocks, max_blocks, L,
+                                        scale, window, sinks, pages, pps, logits, toks);
+            if (cnt < 0) { free(logits); free(toks); return ORC_ERR_PRECONDITION; }
+            if (cnt == 0) continue;
+            double m = logits[0];
+            for (int64_t k = 1; k < cnt; ++k) if (logits[k] > m) m = logits[k];
+            double z = 0.0;
+            for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);
+            double* row = score + ((size_t)b * Hkv + h / G) * (size_t)stride;
+            for (int64_t k = 0; k < cnt; ++k) {
+                if (toks[k] >= stride) { free(logits); free(toks); return ORC_ERR_PRECONDITION; }
+                row[toks[k]] += exp(logits[k] - m) / z;
+            }
         }
         free(logits);
         free(toks);

@@ -313,6 +313,65 @@ def pin_split_combine(o):
             assert np.all(np.isneginf(mp[~live]))
 
 
+def scores(o, pr, stride, score=None, **kw):
+    return o.decode_scores(pr.dtype, pr.kpool, synth.raw_numpy(pr.q), pr.bt.numpy(),
+                           np.array(pr.lens, np.int32), P=pr.P, Hkv=pr.Hkv, d=pr.d, stride=stride,
+                           score=score, **kw)
+
+
+def pin_scores(o):
+    """Decode-time KV scores: per (sequence, kv head) they sum to G (one softmax per query
+    head); weighting V by them reproduces the sum of the group's attention outputs (with
+    linearly independent V rows this fixes every score); tokens that are not attended keep
+    the value they had, and attended ones are added to it."""
+    rng = np.random.default_rng(21)
+    for case in range(9):
+        dtype = ("f32", "f16", "bf16")[case % 3]
+        G = (1, 2, 3)[(case // 3) % 3]
+        Hkv = 1 + case % 2
+        d, P = 64, (16, 32)[case % 2]
+        B = 2
+        lens = [int(x) for x in rng.integers(1, 41, size=B)]
+        if case == 4:
+            lens[1] = 0
+        pr = build(o, 300 + case, B=B, Hq=G * Hkv, Hkv=Hkv, d=d, dtype=dtype, P=P, lens=lens)
+        stride = max(lens) + 3
+        pl = np.full((B, 2), -1, np.int32)
+        for b, L in enumerate(lens):
+            npg = (L + P - 1) // P
+            if npg:
+                pl[b, 0] = int(rng.integers(0, npg))
+        for kw in (dict(), dict(window=7, sinks=2), dict(page_list=pl)):
+            init = rng.standard_normal((B, Hkv, stride))
+            got = scores(o, pr, stride, score=init.copy(), **kw)
+            new = got - init
+            out, _ = attend(o, pr, **kw)
+            Vd = to_f64(pr.V)
+            for b, L in enumerate(lens):
+                for h in range(Hkv):
+                    sb = new[b, h]
+                    if L == 0:
+                        assert np.abs(sb).max() <= TOL
+                        continue
+                    assert abs(sb.sum() - G) <= 1e-12, (case, kw, b, h)
+                    mix = (sb[:L, None] * Vd[b, :L, h]).sum(0)
+                    ref = out[b, h * G:(h + 1) * G].sum(0)
+                    assert np.abs(mix - ref).max() <= 1e-11, (case, kw, b, h)
+                    att = scores(o, pr, stride, score=np.zeros((B, Hkv, stride)), **kw)[b, h] != 0
+                    assert np.abs(sb[~att]).max(initial=0.0) <= TOL, (case, kw)
+    # closed forms: one token gets all of every head's mass; identical keys share it equally
+    pr = build(o, 310, B=1, Hq=3, Hkv=1, d=64, dtype="bf16", P=16, lens=[1])
+    s1 = scores(o, pr, 4)
+    assert abs(s1[0, 0, 0] - 3.0) <= TOL and np.abs(s1[0, 0, 1:]).max() <= TOL
+    L = 45
+    K = synth.normal((1, 1, 1, 64), 3, "k", dtype="bf16").expand(1, L, 1, 64).contiguous()
+    pr = build(o, 311, B=1, Hq=2, Hkv=1, d=64, dtype="bf16", P=16, lens=[L], K=K)
+    s2 = scores(o, pr, L, window=10, sinks=2)[0, 0]
+    toks = [0, 1] + list(range(35, 45))
+    assert np.abs(s2[toks] - 2.0 / len(toks)).max() <= TOL
+    assert np.abs(np.delete(s2, toks)).max() <= TOL
+
+
 def pin_empty(o):
     pr = build(o, 14, B=2, Hq=2, Hkv=1, d=64, dtype="f16", P=16, lens=[0, 3])
     out, lse = attend(o, pr)
@@ -322,7 +381,7 @@ def pin_empty(o):
 PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundtrip,
         pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
         pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
-        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_empty]
+        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_empty]
 
 
 if __name__ == "__main__":

@@ -35,6 +35,10 @@ MUTATIONS = [
     ("append skips last head", "for (int h = 0; h < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src",
      "for (int h = 0; h + 1 < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src"),
     ("paged rounding dropped", "if (block_size > 0) seq =", "if (block_size < 0) seq ="),
+    ("score not normalised", "row[toks[k]] += exp(logits[k] - m) / z;", "row[toks[k]] += exp(logits[k] - m);"),
+    ("score row per head, not per group", "double* row = score + ((size_t)b * Hkv + h / G) * (size_t)stride;",
+     "double* row = score + ((size_t)b * Hkv + h % Hkv) * (size_t)stride;"),
+    ("score overwritten, not added", "row[toks[k]] += exp(logits[k] - m) / z;", "row[toks[k]] = exp(logits[k] - m) / z;"),
 ]
 
 
