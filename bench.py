@@ -77,6 +77,9 @@ def parse():
                     help="record the kernel's HIP events on every n-th call only: an event pair costs "
                          "the step a few microseconds of queue work, so the step clock runs without most")
     ap.add_argument("--no-graph", action="store_true", help="multi-layer modes: skip the HIP-graph timing")
+    ap.add_argument("--scores", action="store_true",
+                    help="default workload: every step also exports the decode-time KV scores "
+                         "(softmax probability per token and kv head, accumulated over steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -435,8 +438,9 @@ def main():
     mcl = max(lens)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens)
-    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # arrival counters start at 0
+    ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens, scores=args.scores)
+    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scores = torch.zeros((B, w.kv_heads, mcl), dtype=torch.float32, device=dev) if args.scores else None
     hip = HipEvents()
 
     def step(rep, ev=None):
@@ -444,7 +448,7 @@ def main():
         pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
                                           rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
                                           split_tokens=args.split_tokens, out=out, lse=lse,
-                                          workspace=workspace, timing=ev)
+                                          workspace=workspace, timing=ev, scores=scores)
 
     for i in range(args.warmup):
         step(reps[i % len(reps)])
@@ -489,7 +493,8 @@ def main():
             "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
             "replicas": args.replicas, "split_tokens": args.split_tokens,
             "step": "paged_decode_append_attention: append of the 32 new tokens fused into the "
-                    "persistent split kernel, then the LSE combine",
+                    "persistent split kernel, then the LSE combine"
+                    + (", plus the decode-time KV score export" if args.scores else ""),
             "parallelism": "single GPU",
         },
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
@@ -500,7 +505,8 @@ def main():
             if args.split_tokens == 0 else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, args.split_tokens), "traffic_unit": "bytes per launch",
+            "traffic": None if args.scores else measured_traffic(w.name, args.split_tokens),
+            "traffic_unit": "bytes per launch",
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
             "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),

@@ -107,7 +107,21 @@ typedef struct {
  *            distinct and ascending. Pages starting at or past L contribute nothing
  *            and their block-table entries are never read.
  * window > 0 together with page_list is PKV_ERR_MODE. num_sinks is ignored
- * unless window > 0. */
+ * unless window > 0.
+ *
+ * Score export ([Novita] §關鍵技術 2: a token's sparsification score is its softmax
+ * probability p = exp(q.k - rowmax) / l, summed over recent queries; the attention pass
+ * already holds rowmax and l). With score_acc != NULL the call also does, for every
+ * sequence b, kv head h and attended token t:
+ *     score_acc[b][h][t] += sum over the query heads g of kv head h of softmax_g(t),
+ * with softmax_g the attention weights of this call. Tokens that are not attended are left
+ * unchanged, so passing the same array on every step accumulates scores over steps (the
+ * caller zeroes or decays it as its policy wants). score_acc is a [batch][num_kv_heads]
+ * [score_stride] fp32 device array with score_stride >= min(max_context_len,
+ * max_blocks_per_seq * block_size) (else PKV_ERR_SHAPE). Score export always uses the
+ * work-split path; it needs split_tokens == 0 (else PKV_ERR_MODE) and is not available
+ * to paged_decode_attention_partial (PKV_ERR_MODE). Every token's update is made by one
+ * thread, in a fixed order: results do not depend on timing. */
 typedef struct {
     int32_t window;          /* <= 0: no window */
     int32_t num_sinks;       /* >= 0 */
@@ -118,6 +132,8 @@ typedef struct {
                                 rounded up to a multiple of 16 and clamped to [16, 4096]. */
     void* timing_start;      /* nullable hipEvent_t: recorded on the stream right before the */
     void* timing_stop;       /* main attention kernel, and right after it (profiling hook) */
+    float* score_acc;        /* nullable: score export, see above (device) */
+    int32_t score_stride;    /* row length of score_acc */
 } pkv_decode_opts;
 
 /* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";

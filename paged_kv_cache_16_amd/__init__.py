@@ -47,7 +47,7 @@ class CacheDesc(ctypes.Structure):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("window", _i32), ("num_sinks", _i32), ("page_list", _vp),
                 ("pages_per_seq", _i32), ("split_tokens", _i32), ("timing_start", _vp),
-                ("timing_stop", _vp)]
+                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32)]
 
 
 _P_DESC = ctypes.POINTER(CacheDesc)
@@ -117,13 +117,19 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(nb, P, hkv, d, DTYPE_CODE[k_cache.dtype])
 
 
-def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None) -> DecodeOpts:
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None)
+def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None) -> DecodeOpts:
+    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None, None, 0)
     if timing is not None:
         o.timing_start, o.timing_stop = int(timing[0]), int(timing[1])
     if page_list is not None:
         o.page_list = _dev(page_list, "page_list", torch.int32)
         o.pages_per_seq = page_list.shape[1]
+    if scores is not None:
+        # [B, Hkv, stride] fp32, accumulated in place
+        if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_contiguous():
+            raise ValueError("scores must be a contiguous [batch, num_kv_heads, stride] float32 tensor")
+        o.score_acc = _dev(scores, "scores", torch.float32)
+        o.score_stride = scores.shape[2]
     return o
 
 
@@ -140,12 +146,15 @@ def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
 
 
 def workspace_size(k_cache, batch: int, num_q_heads: int, max_context_len: int, *, window=0,
-                   num_sinks=0, page_list=None, split_tokens=0) -> int:
+                   num_sinks=0, page_list=None, split_tokens=0, scores=False) -> int:
+    """scores: True (or the score tensor) when the calls export scores."""
     desc = cache_desc(k_cache)
     o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens))
     if page_list is not None:
         o.page_list = ctypes.c_void_p(1)  # only its presence matters to the size
         o.pages_per_seq = page_list.shape[1]
+    if scores is not None and scores is not False:
+        o.score_acc = ctypes.c_void_p(1)
     return int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), batch, num_q_heads,
                                                           max_context_len, ctypes.byref(o)))
 
@@ -164,17 +173,19 @@ def num_splits(k_cache, batch: int, max_context_len: int, *, window=0, num_sinks
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, max_context_len: int,
                            scale: float = 0.0, window: int = 0, num_sinks: int = 0, page_list=None,
                            split_tokens: int = 0, out=None, out_dtype=None, lse=None, workspace=None,
-                           want_lse: bool = True, timing=None):
+                           want_lse: bool = True, timing=None, scores=None):
     """One decode query per sequence over its paged cache. Returns (out, lse).
 
-    timing: optional pair of raw hipEvent_t handles recorded around the main kernel."""
+    timing: optional pair of raw hipEvent_t handles recorded around the main kernel.
+    scores: optional [B, Hkv, stride] float32 tensor; every attended token's softmax
+    probability, summed over the query heads of its kv head, is added into it."""
     desc = cache_desc(k_cache)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
@@ -194,16 +205,17 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
                                   context_lens, *, max_context_len: int, scale: float = 0.0,
                                   window: int = 0, num_sinks: int = 0, page_list=None,
                                   split_tokens: int = 0, out=None, out_dtype=None, lse=None,
-                                  workspace=None, want_lse: bool = True, timing=None):
+                                  workspace=None, want_lse: bool = True, timing=None, scores=None):
     """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
-    slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse)."""
+    slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
+    scores: as in paged_decode_attention."""
     desc = cache_desc(k_cache)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:

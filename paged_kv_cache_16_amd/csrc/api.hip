@@ -53,9 +53,10 @@ struct Plan {
 
 // Path selection for paged_decode_attention (the partial call always uses partitions).
 void choose_path(Plan& pl, const pkv_decode_opts* o) {
+    const bool scores = o && o->score_acc;
     if (o && o->split_tokens > 0) {
         pl.path = pl.num_splits > 1 ? Plan::kPartitions : Plan::kDirect;
-    } else if (pl.units_bound <= kDirectMaxUnits) {
+    } else if (pl.units_bound <= kDirectMaxUnits && !scores) {
         pl.path = Plan::kDirect;
         pl.num_splits = 1;
         pl.units_per_split = kDirectMaxUnits;
@@ -98,6 +99,8 @@ pkv_status check_opts(const pkv_decode_opts* o) {
     if (o->num_sinks < 0 || o->split_tokens < 0) return PKV_ERR_MODE;
     if (o->page_list && o->window > 0) return PKV_ERR_MODE;
     if (o->page_list && o->pages_per_seq <= 0) return PKV_ERR_MODE;
+    if (o->score_acc && o->split_tokens > 0) return PKV_ERR_MODE;
+    if (o->score_acc && o->score_stride < 0) return PKV_ERR_SHAPE;
     return PKV_OK;
 }
 
@@ -145,17 +148,26 @@ struct WsLayout {
 };
 
 struct StreamWs {
-    size_t o_off, m_off, l_off, cnt_off, total;
+    size_t o_off, m_off, l_off, cnt_off, logits_off, lse2_off, total;
 };
 
-StreamWs stream_ws(int batch, int kv_heads, int group, int kmax, int head_dim) {
+// Stream-path workspace: partial slots and per-segment counts; with score export also the
+// masked logits of every attended unit ([B*Hkv][units_bound][G][16] fp32) and the rows'
+// log2 normalisers ([B][Hq]).
+StreamWs stream_ws(int batch, int kv_heads, int group, int kmax, int head_dim, bool scores, int units_bound) {
     StreamWs w;
     const size_t rows = (size_t)batch * kv_heads * kmax * group;
     w.o_off = 0;
     w.m_off = align_up(rows * head_dim * sizeof(float));
     w.l_off = w.m_off + align_up(rows * sizeof(float));
     w.cnt_off = w.l_off + align_up(rows * sizeof(float));
-    w.total = w.cnt_off + align_up((size_t)batch * kv_heads * sizeof(int32_t));
+    w.logits_off = w.cnt_off + align_up((size_t)batch * kv_heads * sizeof(int32_t));
+    w.lse2_off = w.logits_off;
+    w.total = w.logits_off;
+    if (scores) {
+        w.lse2_off = w.logits_off + align_up((size_t)batch * kv_heads * units_bound * group * 16 * sizeof(float));
+        w.total = w.lse2_off + align_up((size_t)batch * kv_heads * group * sizeof(float));
+    }
     return w;
 }
 
@@ -250,7 +262,8 @@ size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc, int32_t
     if (pl.path == Plan::kDirect) return 0;
     if (pl.path == Plan::kStream) {
         if (num_q_heads % desc->num_kv_heads) return 0;
-        return stream_ws(batch, desc->num_kv_heads, num_q_heads / desc->num_kv_heads, pl.kmax, desc->head_dim)
+        return stream_ws(batch, desc->num_kv_heads, num_q_heads / desc->num_kv_heads, pl.kmax, desc->head_dim,
+                         opts && opts->score_acc, pl.units_bound)
             .total;
     }
     return ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim).total;
@@ -303,13 +316,16 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     hipEvent_t ev1 = opts ? (hipEvent_t)opts->timing_stop : nullptr;
 
     // Validate the workspace and finish the launch parameters before anything is enqueued.
+    const bool scores = opts && opts->score_acc;
+    if (scores && opts->score_stride < run.len_cap) return PKV_ERR_SHAPE;
+    if (scores && (pl.units_bound + 63) / 64 > 65535) return PKV_ERR_UNSUPPORTED;  // score grid's y extent
     long long waves = 0;
     if (pl.path != Plan::kDirect) {
         if (!workspace || ((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
     }
     if (pl.path == Plan::kStream) {
         const int G = num_q_heads / desc->num_kv_heads;
-        const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim);
+        const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim, scores, pl.units_bound);
         if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
         const long long n_bound = (long long)batch * desc->num_kv_heads * pl.units_bound;
         if (n_bound > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
@@ -328,6 +344,13 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.waves_total = (int)waves;
         p.chunk_min = pl.chunk_min;
         p.kmax = pl.kmax;
+        if (scores) {
+            p.logits = (float*)((char*)workspace + wl.logits_off);
+            p.row_lse2 = (float*)((char*)workspace + wl.lse2_off);
+            p.score = opts->score_acc;
+            p.score_stride = opts->score_stride;
+            p.units_bound = pl.units_bound;
+        }
     } else if (pl.path == Plan::kPartitions) {
         const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
         if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
@@ -366,7 +389,8 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
             p.new_slots = fa->slots;
             p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
         }
-        return hip_status(launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, fa != nullptr, p, s, ev0, ev1));
+        return hip_status(
+            launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, fa != nullptr, scores, p, s, ev0, ev1));
     }
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
     st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch, s));
@@ -426,6 +450,7 @@ pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void
     pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq,
                                       context_lens, batch, num_q_heads, max_context_len, opts);
     if (st != PKV_OK) return st;
+    if (opts && opts->score_acc) return PKV_ERR_MODE;  // score export is not part of the partial call
     const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
     if (num_splits != pl.num_splits) return PKV_ERR_SHAPE;
     if (batch == 0) return PKV_OK;

@@ -67,6 +67,13 @@ struct DecodeParams {
     const char* v_new;
     const int32_t* new_slots;
     int64_t num_slots;
+    // score export only: masked log2-domain logits [B*Hkv][units_bound][G][16], the rows'
+    // log2 normalisers [B][Hq] (m + log2 l), and the caller's [B][Hkv][score_stride] sums
+    float* logits;
+    float* row_lse2;
+    float* score;
+    int32_t score_stride;
+    int32_t units_bound;
 };
 
 struct CombineParams {
@@ -86,8 +93,8 @@ hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const D
                          int batch, hipStream_t s);
 // Persistent stream kernel + its combine (the paged_decode_attention path). Events, when
 // non-null, are recorded around the stream kernel.
-hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, const DecodeParams& p,
-                                hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, bool scores,
+                                const DecodeParams& p, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 int stream_blocks_per_cu(int dtype, int head_dim, int mode);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

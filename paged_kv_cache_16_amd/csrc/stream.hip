@@ -89,14 +89,16 @@ struct RingBuf {
     static constexpr int NC = D / (4 * DT::kE);
     u32x4 k[NC], v[NC];
     int t0;
+    int u;  // unit index within the segment
 };
 
 template <class DT, int D>
 __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>& rb, int my_tok, unsigned my_off,
-                                          int k, int n, int lane) {
+                                          int k, int n, int lane, int u_base) {
     constexpr int NC = D / (4 * DT::kE);
     const int t0 = k < n ? __builtin_amdgcn_readlane(my_tok, k) : -1;
     rb.t0 = t0;
+    rb.u = u_base + k;
     if (t0 >= 0) {
         const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
         const char* kp = p.k_cache + off + lane * 16;
@@ -199,7 +201,12 @@ __device__ __forceinline__ void patch_tile(u32x4 (&k)[D / (4 * DT::kE)], u32x4 (
     }
 }
 
-template <class DT, int D, int MODE, bool FUSED>
+// Score export: each wave stages the logits of its current run in 4 KiB of LDS and stores
+// them in contiguous full-wave bursts (a 16-lane store per unit cost about three times
+// as much at the benchmark shape).
+constexpr int kLgFloats = 1024;
+
+template <class DT, int D, int MODE, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
     using T = Tile<DT, D / (4 * DT::kE)>;
@@ -254,6 +261,8 @@ void decode_stream_kernel(DecodeParams p) {
     // kv head) segment piece with its own query, softmax state and load pipeline.
     const int qhead = c & 7;
     const bool upper = c >= 8;
+    __shared__ float lg_stage[kWaves * (SCORES ? kLgFloats : 1)];
+    float* lgb = lg_stage + (SCORES ? (threadIdx.x >> 6) * kLgFloats : 0);
     const float qk_scale = p.qk_scale_log2;
     int f_run = f_begin;
     while (f_run < f_end && pos.b < B) {
@@ -278,7 +287,24 @@ void decode_stream_kernel(DecodeParams p) {
         const int t_new = sp.L - 1;  // the token this step appended
         if (FUSED) load_new_row<DT, D>(p, nrow, b, kvh, j, c);
 
+        // score export: the run's logits are staged in LDS and stored in contiguous bursts
+        int lg_n = 0, lg_u0 = u0;
+        auto flush = [&]() __attribute__((always_inline)) {
+            const int nf = lg_n * G * 16;
+            float* dst = p.logits + ((size_t)seg * p.units_bound + lg_u0) * G * 16;
+            for (int i = lane * 4; i < nf; i += 256)
+                *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(lgb + i);
+            lg_u0 += lg_n;
+            lg_n = 0;
+        };
         auto process = [&](RingBuf<DT, D>& rb) __attribute__((always_inline)) {
+            if constexpr (SCORES) {
+                if ((lg_n + 1) * G * 16 > kLgFloats) flush();
+                if (rb.t0 < 0) {
+                    ++lg_n;
+                    return;
+                }
+            }
             if (rb.t0 < 0) return;
             if (FUSED && (unsigned)(t_new - rb.t0) < 16u) patch_tile<DT, D>(rb.k, rb.v, nrow, t_new - rb.t0, j, c);
             f32x4 s = zero4();
@@ -290,6 +316,11 @@ void decode_stream_kernel(DecodeParams p) {
             for (int i = 0; i < 4; ++i) {
                 x[i] = (keep >> i) & 1 ? s[i] * qk_scale : kNegInf;
                 mx = fmaxf(mx, x[i]);
+            }
+            if constexpr (SCORES) {
+                // score export: the unit's masked logits of head c (tokens 4j .. 4j+3)
+                if (c < G) *reinterpret_cast<f32x4*>(lgb + (lg_n * G + c) * 16 + 4 * j) = f32x4{x[0], x[1], x[2], x[3]};
+                ++lg_n;
             }
             mx = xor32_max(xor16_max(mx));
             const float m_new = fmaxf(m_run, mx);
@@ -323,24 +354,25 @@ void decode_stream_kernel(DecodeParams p) {
                 }
             }
             RingBuf<DT, D> R0, R1, R2, R3;
-            ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane);
-            ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane);
-            ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane);
+            ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
+            ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
+            ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
             for (int k = 0; k < n; k += 4) {
-                ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane);
+                ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
                 process(R0);
                 if (k + 1 >= n) break;
-                ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane);
+                ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
                 process(R1);
                 if (k + 2 >= n) break;
-                ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane);
+                ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
                 process(R2);
                 if (k + 3 >= n) break;
-                ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane);
+                ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
                 process(R3);
             }
         }
 
+        if constexpr (SCORES) flush();
         // End of the run: the finished row, or a partial for the combine.
         const float l_tot = xor32_sum(xor16_sum(l_run));
         const int head = T::acc_head(c);
@@ -359,6 +391,9 @@ void decode_stream_kernel(DecodeParams p) {
             }
             if (j == 0 && c < 8 && head < G && p.lse)
                 p.lse[hrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+            if constexpr (SCORES) {
+                if (j == 0 && c < 8 && head < G) p.row_lse2[hrow] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
+            }
             if (lane == 0) p.seg_count[seg] = 0;
         } else {
             const int s_g = f_run - u0;  // flat index of the segment's unit 0
@@ -407,6 +442,7 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, 0.f);
         if (lane == 0 && p.lse) p.lse[hrow] = kNegInf;
+        if (lane == 0 && p.row_lse2) p.row_lse2[hrow] = kNegInf;
         return;
     }
     if (cnt == 0) return;
@@ -458,19 +494,69 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, o[i] * inv);
     if (lane == 0 && p.lse) p.lse[hrow] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
+    if (lane == 0 && p.row_lse2) p.row_lse2[hrow] = Ls > 0.f ? M + __log2f(Ls) : kNegInf;
+}
+
+// Score export ([Novita] §關鍵技術 2: a token's score is its softmax probability
+// p = exp(q.k - rowmax) / l, which needs only the row's max and sum besides the logit).
+// Grid: (sequence, kv head) segments x chunks of kScoreUnits units. A thread owns four
+// consecutive tokens of one unit: it reads their logits for each of the G query heads as
+// one 16-byte load per head, and adds sum_g 2^(x_g - (m_g + log2 l_g)) to score[t] for the
+// tokens that are attended. Each token has one owner and the heads are summed in order, so
+// the result does not depend on timing.
+constexpr int kScoreUnits = 64;  // units per workgroup (256 threads x 4 tokens)
+
+template <int MODE>
+__global__ __launch_bounds__(256) void score_kernel(DecodeParams p) {
+    const int seg = blockIdx.x;
+    const int u = blockIdx.y * kScoreUnits + (threadIdx.x >> 2);
+    const int b = seg / p.kv_heads, kvh = seg - b * p.kv_heads;
+    const int G = p.group;
+    const SeqPlan sp = make_plan<MODE>(p, b);
+    if (u >= sp.n_units) return;
+    const int t0 = unit_token<MODE>(p, sp, b, u);
+    if (t0 < 0) return;
+    const int q4 = (threadIdx.x & 3) * 4;  // first token of the thread within the unit
+    const float* lg = p.logits + (((size_t)seg * p.units_bound + u) * G) * 16 + q4;
+    const float* lse2 = p.row_lse2 + (size_t)b * p.q_heads + kvh * G;
+    f32x4 mass = zero4();
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+        if (g < G) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16);
+            const float l2 = lse2[g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mass[i] += __builtin_amdgcn_exp2f(x[i] - l2);
+        }
+    }
+    float* row = p.score + (size_t)seg * p.score_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + q4 + i;
+        if (t < sp.L && (t < sp.e0 || t >= sp.s1)) row[t] += mass[i];  // attended tokens only
+    }
 }
 
 template <class DT, int D, int MODE>
-static hipError_t launch_stream_t(bool fused, const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
     const unsigned blocks = (unsigned)(p.waves_total / kWaves);
     if (e0) {
         hipError_t e = hipEventRecord(e0, s);
         if (e != hipSuccess) return e;
     }
-    if (fused)
-        decode_stream_kernel<DT, D, MODE, true><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
-    else
-        decode_stream_kernel<DT, D, MODE, false><<<dim3(blocks), dim3(64 * kWaves), 0, s>>>(p);
+    const dim3 grid(blocks), block(64 * kWaves);
+    if (scores) {
+        if (fused)
+            decode_stream_kernel<DT, D, MODE, true, true><<<grid, block, 0, s>>>(p);
+        else
+            decode_stream_kernel<DT, D, MODE, false, true><<<grid, block, 0, s>>>(p);
+    } else {
+        if (fused)
+            decode_stream_kernel<DT, D, MODE, true, false><<<grid, block, 0, s>>>(p);
+        else
+            decode_stream_kernel<DT, D, MODE, false, false><<<grid, block, 0, s>>>(p);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (e1) {
@@ -478,42 +564,51 @@ static hipError_t launch_stream_t(bool fused, const DecodeParams& p, hipStream_t
         if (err != hipSuccess) return err;
     }
     stream_combine_kernel<D, MODE, DT::kBytes><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
+    err = hipGetLastError();
+    if (err != hipSuccess || !scores) return err;
+    score_kernel<MODE><<<dim3((unsigned)(p.batch * p.kv_heads), (unsigned)((p.units_bound + kScoreUnits - 1) / kScoreUnits)),
+                         dim3(256), 0, s>>>(p);
     return hipGetLastError();
 }
 
 template <class DT, int D>
-static hipError_t launch_stream_m(int mode, bool fused, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
-                                  hipEvent_t e1) {
+static hipError_t launch_stream_m(int mode, bool fused, bool scores, const DecodeParams& p, hipStream_t s,
+                                  hipEvent_t e0, hipEvent_t e1) {
     switch (mode) {
-        case kWindow: return launch_stream_t<DT, D, kWindow>(fused, p, s, e0, e1);
-        case kPages: return launch_stream_t<DT, D, kPages>(fused, p, s, e0, e1);
-        default: return launch_stream_t<DT, D, kFull>(fused, p, s, e0, e1);
+        case kWindow: return launch_stream_t<DT, D, kWindow>(fused, scores, p, s, e0, e1);
+        case kPages: return launch_stream_t<DT, D, kPages>(fused, scores, p, s, e0, e1);
+        default: return launch_stream_t<DT, D, kFull>(fused, scores, p, s, e0, e1);
     }
 }
 
 template <class DT>
-static hipError_t launch_stream_d(int head_dim, int mode, bool fused, const DecodeParams& p, hipStream_t s,
-                                  hipEvent_t e0, hipEvent_t e1) {
-    return head_dim == 64 ? launch_stream_m<DT, 64>(mode, fused, p, s, e0, e1)
-                          : launch_stream_m<DT, 128>(mode, fused, p, s, e0, e1);
+static hipError_t launch_stream_d(int head_dim, int mode, bool fused, bool scores, const DecodeParams& p,
+                                  hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    return head_dim == 64 ? launch_stream_m<DT, 64>(mode, fused, scores, p, s, e0, e1)
+                          : launch_stream_m<DT, 128>(mode, fused, scores, p, s, e0, e1);
 }
 
-hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, const DecodeParams& p,
-                                hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, bool scores,
+                                const DecodeParams& p, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     if (p.batch <= 0 || p.waves_total <= 0) return hipSuccess;
     switch (dtype) {
-        case kF32: return launch_stream_d<F32>(head_dim, mode, fused, p, s, ev_start, ev_stop);
-        case kF16: return launch_stream_d<F16>(head_dim, mode, fused, p, s, ev_start, ev_stop);
-        default: return launch_stream_d<BF16>(head_dim, mode, fused, p, s, ev_start, ev_stop);
+        case kF32: return launch_stream_d<F32>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
+        case kF16: return launch_stream_d<F16>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
+        default: return launch_stream_d<BF16>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
     }
 }
 
 template <class DT, int D, int MODE>
 static int occupancy_t() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, true>, 64 * kWaves, 0) !=
-        hipSuccess)
+    // the least occupancy of the variants, so that every launch fits at once
+    int m = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, true, false>, 64 * kWaves,
+                                                     0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_stream_kernel<DT, D, MODE, true, true>, 64 * kWaves,
+                                                     0) != hipSuccess)
         return 1;
+    n = m < n ? m : n;
     return n > 0 ? n : 1;
 }
 

@@ -105,3 +105,31 @@ def test_validation_precedes_any_launch(pkv):
     assert call(*args(opts=ctypes.byref(many), mcl=4096)) == 5   # needs a workspace, none given
     assert lib.paged_decode_combine(None, None, None, 2, 4, 3, 128, None, 0, None, None) == 1
     assert lib.paged_decode_combine(fake, fake, fake, 2, 4, 0, 128, fake, 0, None, None) == 2
+
+
+def test_score_export_validation(pkv):
+    """Score export: sizing grows by the logits buffer; invalid combinations are rejected on
+    the host before anything is enqueued."""
+    lib = pkv._lib
+    d = _desc(pkv)
+    fake = ctypes.c_void_p(256)  # never dereferenced
+    plain = pkv.DecodeOpts(0, 0, None, 0, 0)
+    scored = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 4096)
+    ws0 = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(plain))
+    ws1 = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(scored))
+    # logits of every unit and head: 32 seq x 8 kv heads x 256 units x 4 heads x 16 tokens x 4 B
+    assert ws1 - ws0 >= 32 * 8 * 256 * 4 * 16 * 4
+    # scores force the work-split path, so even a tiny problem needs a workspace
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(plain)) == 0
+    small = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 20)
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(small)) > 0
+    call = lib.paged_decode_attention
+    args = lambda opts, mcl=100: (ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, mcl, 0.0, opts, fake, 2,
+                                  None, None, 0, None)
+    split = pkv.DecodeOpts(0, 0, None, 0, 64, None, None, fake, 4096)
+    assert call(*args(ctypes.byref(split))) == 4        # scores with fixed partitions
+    short = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 99)
+    assert call(*args(ctypes.byref(short))) == 2        # stride below the context bound
+    part = lib.paged_decode_attention_partial
+    assert part(ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, 100, 0.0, ctypes.byref(scored),
+                fake, fake, fake, 1, None) == 4         # the partial call exports no scores
