@@ -84,7 +84,9 @@ class Oracle:
                                                     _P, _P, _P, _P]
         L.oracle_decode_scores.restype = _I
         L.oracle_decode_scores.argtypes = [_I, _I64, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P, _D, _I,
-                                           _I, _P, _I, _P, _I64]
+                                           _I, _P, _I, _P, _I64, _I]
+        L.oracle_select_pages.restype = _I
+        L.oracle_select_pages.argtypes = [_P, _I, _I64, _P, _I, _I, _I, _I, _P]
         L.oracle_bruteforce.restype = _I
         L.oracle_bruteforce.argtypes = [_I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _D, _I, _I, _I,
                                         _P, _I, _P, _P]
@@ -143,9 +145,9 @@ class Oracle:
         return out, lse
 
     def decode_scores(self, dtype, kpool, q, block_table, context_lens, *, P, Hkv, d, stride,
-                      scale=0.0, window=0, sinks=0, page_list=None, score=None):
+                      scale=0.0, window=0, sinks=0, page_list=None, score=None, block=1):
         """Adds one step's scores into `score` ([B][Hkv][stride] float64, zeros when None) and
-        returns it."""
+        returns it. block: tokens per score entry."""
         kpool, _, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
             dtype, kpool, kpool, q, block_table, context_lens, P, Hkv, d, page_list)
         if score is None:
@@ -155,9 +157,21 @@ class Oracle:
             raise ValueError(f"score must be [{B}][{Hkv}][{stride}], got {score.shape}")
         self._check(self.lib.oracle_decode_scores(
             DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool), _ptr(q), B, Hq, _ptr(bt), mb, _ptr(cl),
-            float(scale), int(window), int(sinks), _ptr(pl), pps, _ptr(score), int(stride)),
+            float(scale), int(window), int(sinks), _ptr(pl), pps, _ptr(score), int(stride), int(block)),
             "decode_scores")
         return score
+
+    def select_pages(self, scores, context_lens, *, P, k, recent=1):
+        """scores: [B][H][stride] float32 page weights. Returns the [B][k] int32 page lists."""
+        sc = np.ascontiguousarray(scores, dtype=np.float32)
+        if sc.ndim != 3:
+            raise ValueError("scores must be [B][H][stride]")
+        cl = _i32(context_lens).reshape(-1)
+        B, H, stride = sc.shape
+        out = np.full((B, k), -7, np.int32)
+        self._check(self.lib.oracle_select_pages(_ptr(sc), H, stride, _ptr(cl), B, int(P), int(k), int(recent),
+                                                 _ptr(out)), "select_pages")
+        return out
 
     def decode_attention_split(self, dtype, kpool, vpool, q, block_table, context_lens, *, P,
                                Hkv, d, units, max_splits, scale=0.0, window=0, sinks=0,
@@ -235,6 +249,10 @@ def decode_attention_split(*a, **k):
 
 def decode_scores(*a, **k):
     return default().decode_scores(*a, **k)
+
+
+def select_pages(*a, **k):
+    return default().select_pages(*a, **k)
 
 
 def bruteforce(*a, **k):

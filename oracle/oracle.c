@@ -15,7 +15,8 @@
  *            (cf-1.com): §2.2 decode = append the new token's K/V, then attend over all
  *            cached tokens; §3.1 KV-size formula; §4.1 block table; §4.3 sliding window.
  *   [OVAL]   "OVAL — Output-Aware Local Page Bases for KV Cache Retrieval" (2kiu.com):
- *            §2.2/§3.3 per-step page base indices; §3.2 window clamps.
+ *            §2.2/§3.3 per-step page base indices, the top-k pages by weight; §3.2 window
+ *            clamps.
  *   [Novita] "How KV Sparsity Achieves 1.5x Acceleration for vLLM": §關鍵技術 1 per-layer
  *            full cache or sliding window; §關鍵技術 2 online softmax keeping rowmax and l,
  *            and the per-token sparsification score built from them.
@@ -259,18 +260,20 @@ int oracle_decode_attention(int dt, int64_t num_blocks, int P, int Hkv, int d,
  * p = exp(q.k - rowmax) / l, which the attention pass already has the rowmax and l for).
  * One decode step contributes its single query per head: for every sequence b, kv head
  * kvh and attended token t,
- *     score[b][kvh][t] += sum over the G query heads h of kvh of softmax_h(t),
- * with softmax_h the attention weights of oracle_decode_attention. Tokens that are not
- * attended are left as they are, so a caller accumulates over steps by passing the same
- * array again. score: [B][Hkv][stride] doubles; every attended t must be < stride. */
+ *     score[b][kvh][t / block] += sum over the G query heads h of kvh of softmax_h(t),
+ * with softmax_h the attention weights of oracle_decode_attention. An entry gathers the
+ * scores of `block` consecutive tokens (block = 1: per token; block = the page size: per
+ * page). Entries without attended tokens are left as they are, so a caller accumulates over
+ * steps by passing the same array again. score: [B][Hkv][stride] doubles; every attended
+ * t / block must be < stride. */
 int oracle_decode_scores(int dt, int64_t num_blocks, int P, int Hkv, int d,
                          const void* kpool, const void* q, int B, int Hq,
                          const int32_t* block_table, int max_blocks,
                          const int32_t* context_lens, double scale,
                          int window, int sinks, const int32_t* page_list, int pps,
-                         double* score, int64_t stride) {
+                         double* score, int64_t stride, int block) {
     if (!common_args_ok(dt, num_blocks, P, Hkv, d, B, Hq, max_blocks, window, sinks,
-                        page_list, pps) || stride < 0)
+                        page_list, pps) || stride < 0 || block < 1)
         return ORC_ERR_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     int G = Hq / Hkv;
@@ -294,12 +297,67 @@ int oracle_decode_scores(int dt, int64_t num_blocks, int P, int Hkv, int d,
             for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);
             double* row = score + ((size_t)b * Hkv + h / G) * (size_t)stride;
             for (int64_t k = 0; k < cnt; ++k) {
-                if (toks[k] >= stride) { free(logits); free(toks); return ORC_ERR_PRECONDITION; }
-                row[toks[k]] += exp(logits[k] - m) / z;
+                int64_t e = toks[k] / block;
+                if (e >= stride) { free(logits); free(toks); return ORC_ERR_PRECONDITION; }
+                row[e] += exp(logits[k] - m) / z;
             }
         }
         free(logits);
         free(toks);
+    }
+    return ORC_OK;
+}
+
+/* Page selection ([OVAL] §3.3: each step keeps the k pages of highest weight and hands
+ * their ids to attention; the config this path is measured on always keeps the page of the
+ * newest token). For sequence b with context length L and n = ceil(L / P) pages:
+ *   - the weight of page p is sum over h = 0 .. H-1 (in that order) of
+ *     scores[b][h][p], accumulated in fp32 (float), so that a caller comparing against a
+ *     kernel that sums in the same order sees the same weights bit for bit;
+ *   - the newest min(recent, n) pages [n - recent, n) are always taken;
+ *   - of the older pages [0, n - recent), the k - recent with the largest weight are
+ *     taken; equal weights go to the lower page id;
+ *   - out[b] lists the taken ids ascending, then -1 up to k entries.
+ * L == 0 gives a row of -1. Preconditions: 0 <= recent <= k, n <= stride, finite scores. */
+int oracle_select_pages(const float* scores, int H, int64_t stride, const int32_t* context_lens,
+                        int B, int P, int k, int recent, int32_t* out) {
+    if (!scores || H <= 0 || stride < 0 || B < 0 || P <= 0 || k <= 0 || recent < 0 ||
+        recent > k)
+        return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b) {
+        int32_t* row = out + (size_t)b * k;
+        for (int i = 0; i < k; ++i) row[i] = -1;
+        int L = context_lens[b];
+        if (L < 0) return ORC_ERR_PRECONDITION;
+        int64_t n = ((int64_t)L + P - 1) / P;
+        if (n > stride) return ORC_ERR_PRECONDITION;
+        if (n == 0) continue;
+        int64_t first_recent = n - recent > 0 ? n - recent : 0;
+        float* w = (float*)malloc(sizeof(float) * (size_t)(first_recent > 0 ? first_recent : 1));
+        char* taken = (char*)calloc((size_t)(first_recent > 0 ? first_recent : 1), 1);
+        if (!w || !taken) { free(w); free(taken); return ORC_ERR_NOMEM; }
+        for (int64_t p = 0; p < first_recent; ++p) {
+            float acc = 0.0f;
+            for (int h = 0; h < H; ++h) acc += scores[((size_t)b * H + h) * (size_t)stride + p];
+            if (!isfinite(acc)) { free(w); free(taken); return ORC_ERR_PRECONDITION; }
+            w[p] = acc;
+        }
+        /* k - recent rounds of "best remaining page": largest weight, then lowest id */
+        int cnt = 0;
+        int64_t want = k - recent;
+        for (int64_t r = 0; r < want && r < first_recent; ++r) {
+            int64_t best = -1;
+            for (int64_t p = 0; p < first_recent; ++p) {
+                if (taken[p]) continue;
+                if (best < 0 || w[p] > w[best]) best = p;  /* ascending p: ties keep the lower id */
+            }
+            taken[best] = 1;
+        }
+        for (int64_t p = 0; p < first_recent; ++p)
+            if (taken[p]) row[cnt++] = (int32_t)p;
+        for (int64_t p = first_recent; p < n; ++p) row[cnt++] = (int32_t)p;
+        free(w);
+        free(taken);
     }
     return ORC_OK;
 }

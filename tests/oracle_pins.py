@@ -313,10 +313,10 @@ def pin_split_combine(o):
             assert np.all(np.isneginf(mp[~live]))
 
 
-def scores(o, pr, stride, score=None, **kw):
+def scores(o, pr, stride, score=None, block=1, **kw):
     return o.decode_scores(pr.dtype, pr.kpool, synth.raw_numpy(pr.q), pr.bt.numpy(),
                            np.array(pr.lens, np.int32), P=pr.P, Hkv=pr.Hkv, d=pr.d, stride=stride,
-                           score=score, **kw)
+                           score=score, block=block, **kw)
 
 
 def pin_scores(o):
@@ -372,6 +372,67 @@ def pin_scores(o):
     assert np.abs(np.delete(s2, toks)).max() <= TOL
 
 
+def pin_scores_block(o):
+    """Score entries of `block` consecutive tokens hold the sums of the (pinned) per-token
+    scores of their tokens, in every mode and for blocks that do and do not divide P."""
+    pr = build(o, 320, B=2, Hq=6, Hkv=2, d=64, dtype="bf16", P=16, lens=[70, 33])
+    pl = np.array([[0, 3, -1], [1, -1, -1]], np.int32)
+    for kw in (dict(), dict(window=20, sinks=3), dict(page_list=pl)):
+        tok = scores(o, pr, 70, **kw)
+        for block in (16, 5, 1000):
+            n = (70 + block - 1) // block
+            got = scores(o, pr, n, block=block, **kw)
+            ref = np.zeros_like(got)
+            for t in range(70):
+                ref[:, :, t // block] += tok[:, :, t]
+            assert np.abs(got - ref).max() <= 1e-12, (kw, block)
+
+
+def _f32_weights(sc):
+    """Page weights in float32, heads added in index order."""
+    B, H, n = sc.shape
+    w = np.zeros((B, n), np.float32)
+    for h in range(H):
+        w = (w + sc[:, h]).astype(np.float32)
+    return w
+
+
+def pin_select_pages(o):
+    """Page selection: the hand-worked cases of tests/golden/page_select.json ([OVAL] §3.3),
+    and on random inputs with many ties the properties that define the result: ids ascending
+    and distinct; the newest pages present; min(k, n) ids; every older page taken weighs at
+    least as much as every older page left out, and where they weigh the same the taken id is
+    the lower."""
+    with open(os.path.join(GOLDEN, "page_select.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        got = o.select_pages(np.array(c["scores"], np.float32), np.array(c["lens"], np.int32), P=c["P"],
+                             k=c["k"], recent=c["recent"])
+        assert got.tolist() == c["expect"], (c["what"], got.tolist())
+    rng = np.random.default_rng(33)
+    for case in range(40):
+        B, H, P = 3, int(rng.integers(1, 4)), int(rng.choice([16, 32]))
+        k, recent = int(rng.integers(1, 9)), 0
+        recent = int(rng.integers(0, k + 1))
+        lens = rng.integers(0, 20 * P, size=B)
+        stride = int((lens.max() + P - 1) // P) + 2
+        sc = rng.integers(0, 4, size=(B, H, stride)).astype(np.float32) * 0.5  # small integers: many ties
+        got = o.select_pages(sc, lens, P=P, k=k, recent=recent)
+        w = _f32_weights(sc)
+        for b in range(B):
+            n = int((lens[b] + P - 1) // P)
+            row = [int(x) for x in got[b] if x >= 0]
+            assert all(x == -1 for x in got[b][len(row):]), (case, got[b])
+            assert row == sorted(set(row)) and len(row) == min(k, n), (case, row)
+            newest = list(range(max(0, n - recent), n))
+            assert set(newest) <= set(row), (case, row, newest)
+            older = [x for x in row if x < n - recent]
+            rest = [x for x in range(max(0, n - recent)) if x not in older]
+            for a in older:
+                for r in rest:
+                    assert w[b, a] > w[b, r] or (w[b, a] == w[b, r] and a < r), (case, a, r)
+
+
 def pin_empty(o):
     pr = build(o, 14, B=2, Hq=2, Hkv=1, d=64, dtype="f16", P=16, lens=[0, 3])
     out, lse = attend(o, pr)
@@ -381,7 +442,8 @@ def pin_empty(o):
 PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundtrip,
         pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
         pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
-        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_empty]
+        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_scores_block, pin_select_pages,
+        pin_empty]
 
 
 if __name__ == "__main__":

@@ -35,10 +35,15 @@ MUTATIONS = [
     ("append skips last head", "for (int h = 0; h < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src",
      "for (int h = 0; h + 1 < Hkv; ++h)\n            for (int x = 0; x < d; ++x) {\n                size_t src"),
     ("paged rounding dropped", "if (block_size > 0) seq =", "if (block_size < 0) seq ="),
-    ("score not normalised", "row[toks[k]] += exp(logits[k] - m) / z;", "row[toks[k]] += exp(logits[k] - m);"),
+    ("score not normalised", "row[e] += exp(logits[k] - m) / z;", "row[e] += exp(logits[k] - m);"),
     ("score row per head, not per group", "double* row = score + ((size_t)b * Hkv + h / G) * (size_t)stride;",
      "double* row = score + ((size_t)b * Hkv + h % Hkv) * (size_t)stride;"),
-    ("score overwritten, not added", "row[toks[k]] += exp(logits[k] - m) / z;", "row[toks[k]] = exp(logits[k] - m) / z;"),
+    ("score overwritten, not added", "row[e] += exp(logits[k] - m) / z;", "row[e] = exp(logits[k] - m) / z;"),
+    ("score entry by token, not block", "int64_t e = toks[k] / block;", "int64_t e = toks[k] / (block > 1 ? block - 1 : 1);"),
+    ("page ties to the higher id", "if (best < 0 || w[p] > w[best]) best = p;", "if (best < 0 || w[p] >= w[best]) best = p;"),
+    ("page weights in double", "float acc = 0.0f;", "double acc = 0.0;"),
+    ("newest page not forced", "for (int64_t p = first_recent; p < n; ++p) row[cnt++] = (int32_t)p;", ";"),
+    ("k pages besides the newest", "int64_t want = k - recent;", "int64_t want = k;"),
 ]
 
 
