@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--scores", action="store_true",
                     help="default workload: every step also exports the decode-time KV scores "
                          "(softmax probability per token and kv head, accumulated over steps)")
+    ap.add_argument("--loop", action="store_true",
+                    help="page-selected workload: close the loop; each step exports per-page scores and "
+                         "paged_select_pages picks the next step's pages from them (newest page kept)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -96,6 +99,11 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev: int, stream: int) -> None:
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self) -> int:
         h = self._ct.c_void_p()
@@ -356,23 +364,46 @@ def run_page_selected(w, args, dev):
                      dtype=torch.uint8, device=dev)
     hip = HipEvents()
 
-    def step(i, ev=None):
+    loop = args.loop
+    if loop:
+        # closed loop: per-page scores accumulate over steps and pick the next step's pages
+        n_pages = (max(lens) + P - 1) // P
+        gscores = torch.zeros((B, Hkv, n_pages), dtype=torch.float32, device=dev)
+        plist = lists[0].clone()
+        ws = torch.zeros(max(256, pkv.workspace_size(gk, B, Hq, max(lens), page_list=lists[0], scores=True)),
+                         dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i, ev=None, sev=None):
+        if not loop:
+            pkv.paged_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
+                                              page_list=lists[i % n_lists], out=out, lse=lse, workspace=ws,
+                                              timing=ev)
+            return
         pkv.paged_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
-                                          page_list=lists[i % n_lists], out=out, lse=lse, workspace=ws,
-                                          timing=ev)
+                                          page_list=plist, out=out, lse=lse, workspace=ws, timing=ev,
+                                          scores=gscores, score_block=P)
+        if sev is not None:
+            hip.record(sev[0], stream)
+        pkv.select_pages(gscores, cl, block_size=P, k=w.pages_per_step, recent=1, page_list=plist)
+        if sev is not None:
+            hip.record(sev[1], stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     every = max(1, args.event_every)
     evs = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)]
+    sevs = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)] if loop else None
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i // every] if i % every == 0 else None)
+        on = i % every == 0
+        step(i, evs[i // every] if on else None, sevs[i // every] if on and loop else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = sorted(hip.elapsed_ms(a, b) for a, b in evs)
-    for a, b in evs:
+    sel = sorted(hip.elapsed_ms(a, b) for a, b in sevs) if loop else []
+    for a, b in evs + (sevs or []):
         hip.destroy(a)
         hip.destroy(b)
     att_bytes = B * w.pages_per_step * P * w.kv_bytes_per_token()
@@ -386,12 +417,16 @@ def run_page_selected(w, args, dev):
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "block_size": P, "context": lens[0], "pages_per_step": w.pages_per_step,
                    "page_lists": n_lists, "pool_bytes": 2 * gk.numel() * gk.element_size(),
-                   "step": "paged_decode_append_attention over the step's page list",
+                   "step": "paged_decode_append_attention over the step's page list"
+                           + (", per-page score export, paged_select_pages for the next step" if loop else ""),
                    "parallelism": "single GPU"},
         "hbm_frac_of_peak": round(att_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "steps_per_s_per_layer": round(1e3 / step_ms, 1),
         "attention_kernel_us_mean": round(kmean * 1e3, 3),
         "attention_kernel_GBps": round(att_bytes / (kmean * 1e-3) / 1e9, 2),
+        **({"closed_loop": "per-page score export + paged_select_pages each step",
+            "select_pages_us_mean": round(statistics.fmean(sel) * 1e3, 3),
+            "select_pages_us_p50": round(sel[len(sel) // 2] * 1e3, 3)} if loop else {}),
     }
 
 

@@ -112,16 +112,17 @@ typedef struct {
  * Score export ([Novita] §關鍵技術 2: a token's sparsification score is its softmax
  * probability p = exp(q.k - rowmax) / l, summed over recent queries; the attention pass
  * already holds rowmax and l). With score_acc != NULL the call also does, for every
- * sequence b, kv head h and attended token t:
- *     score_acc[b][h][t] += sum over the query heads g of kv head h of softmax_g(t),
- * with softmax_g the attention weights of this call. Tokens that are not attended are left
- * unchanged, so passing the same array on every step accumulates scores over steps (the
- * caller zeroes or decays it as its policy wants). score_acc is a [batch][num_kv_heads]
- * [score_stride] fp32 device array with score_stride >= min(max_context_len,
- * max_blocks_per_seq * block_size) (else PKV_ERR_SHAPE). Score export always uses the
- * work-split path; it needs split_tokens == 0 (else PKV_ERR_MODE) and is not available
- * to paged_decode_attention_partial (PKV_ERR_MODE). Every token's update is made by one
- * thread, in a fixed order: results do not depend on timing. */
+ * sequence b, kv head h and attended token t, with B = max(score_block, 1):
+ *     score_acc[b][h][t / B] += sum over the query heads g of kv head h of softmax_g(t),
+ * with softmax_g the attention weights of this call: per token for B = 1, per page for
+ * B = block_size. Entries without attended tokens are left unchanged, so passing the same
+ * array on every step accumulates scores over steps (the caller zeroes or decays it as its
+ * policy wants). score_acc is a [batch][num_kv_heads][score_stride] fp32 device array with
+ * score_stride >= ceil(min(max_context_len, max_blocks_per_seq * block_size) / B) (else
+ * PKV_ERR_SHAPE). Score export always uses the work-split path; it needs split_tokens == 0
+ * (else PKV_ERR_MODE) and is not available to paged_decode_attention_partial
+ * (PKV_ERR_MODE). Every entry's update is made by one thread, in a fixed order: results do
+ * not depend on timing. */
 typedef struct {
     int32_t window;          /* <= 0: no window */
     int32_t num_sinks;       /* >= 0 */
@@ -134,6 +135,7 @@ typedef struct {
     void* timing_stop;       /* main attention kernel, and right after it (profiling hook) */
     float* score_acc;        /* nullable: score export, see above (device) */
     int32_t score_stride;    /* row length of score_acc */
+    int32_t score_block;     /* tokens per score entry; 0 or 1: one entry per token */
 } pkv_decode_opts;
 
 /* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";
@@ -284,6 +286,29 @@ pkv_status paged_decode_combine(const float* o_part, const float* m_part, const 
                                 int32_t head_dim,
                                 void* out, pkv_dtype out_dtype, float* lse_out,
                                 void* stream);
+
+/* paged_select_pages — the next step's page list from page scores ([OVAL] §3.3: each
+ * step keeps the k pages of highest weight and passes their ids to attention; the newest
+ * pages, which hold the tokens just appended, are always kept). For sequence b with
+ * context length L and n = ceil(L / block_size) pages:
+ *   weight(p) = sum over h = 0 .. heads-1, in that order, of scores[b][h][p], in fp32;
+ *   the newest min(recent, n) pages [n - recent, n) are always taken; of the older pages
+ *   the k - recent of largest weight are taken, equal weights going to the lower id;
+ *   page_list[b] = the taken ids ascending, then -1 up to k entries (L == 0: all -1).
+ * The result is exactly that of the definition (weights summed in the stated order), so it
+ * is deterministic and can be compared bit for bit. The rows are valid page_list rows for
+ * paged_decode_attention with pages_per_seq = k.
+ *   scores:        [batch][heads][stride] fp32, device: e.g. the score_acc array of a
+ *                  decode call with score_block == block_size.
+ *   context_lens:  [batch] int32, device.
+ *   page_list:     [batch][k] int32, device, written.
+ * Limits: 1 <= k <= 64, 0 <= recent <= k, 1 <= heads, 0 <= stride <= 15360, batch <= 65535
+ * (else PKV_ERR_SHAPE / PKV_ERR_UNSUPPORTED). Preconditions: n <= stride for every
+ * sequence (pages at or past stride are never read: such a sequence is treated as having
+ * stride pages), finite scores. */
+pkv_status paged_select_pages(const float* scores, int32_t heads, int32_t stride,
+                              const int32_t* context_lens, int32_t batch, int32_t block_size,
+                              int32_t k, int32_t recent, int32_t* page_list, void* stream);
 
 /* KV-cache size in bytes by the formula of [primer] §3.1,
  *   2 x batch x layers x kv_heads x head_dim x seq_len x dtype_bytes,

@@ -21,6 +21,7 @@ __all__ = [
     "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
+    "select_pages",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -47,7 +48,7 @@ class CacheDesc(ctypes.Structure):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("window", _i32), ("num_sinks", _i32), ("page_list", _vp),
                 ("pages_per_seq", _i32), ("split_tokens", _i32), ("timing_start", _vp),
-                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32)]
+                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32), ("score_block", _i32)]
 
 
 _P_DESC = ctypes.POINTER(CacheDesc)
@@ -71,6 +72,8 @@ _lib.paged_decode_attention_partial.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _i3
                                                 _f32, _P_OPTS, _vp, _vp, _vp, _i32, _vp]
 _lib.paged_decode_combine.restype = ctypes.c_int
 _lib.paged_decode_combine.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, ctypes.c_int, _vp, _vp]
+_lib.paged_select_pages.restype = ctypes.c_int
+_lib.paged_select_pages.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
 _lib.pkv_kv_cache_bytes.restype = ctypes.c_uint64
 _lib.pkv_kv_cache_bytes.argtypes = [_i64] * 7
 _lib.pkv_status_string.restype = ctypes.c_char_p
@@ -117,8 +120,10 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(nb, P, hkv, d, DTYPE_CODE[k_cache.dtype])
 
 
-def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None) -> DecodeOpts:
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None, None, 0)
+def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None,
+          score_block=1) -> DecodeOpts:
+    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None, None, 0,
+                   int(score_block))
     if timing is not None:
         o.timing_start, o.timing_stop = int(timing[0]), int(timing[1])
     if page_list is not None:
@@ -173,19 +178,20 @@ def num_splits(k_cache, batch: int, max_context_len: int, *, window=0, num_sinks
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, max_context_len: int,
                            scale: float = 0.0, window: int = 0, num_sinks: int = 0, page_list=None,
                            split_tokens: int = 0, out=None, out_dtype=None, lse=None, workspace=None,
-                           want_lse: bool = True, timing=None, scores=None):
+                           want_lse: bool = True, timing=None, scores=None, score_block: int = 1):
     """One decode query per sequence over its paged cache. Returns (out, lse).
 
     timing: optional pair of raw hipEvent_t handles recorded around the main kernel.
     scores: optional [B, Hkv, stride] float32 tensor; every attended token's softmax
-    probability, summed over the query heads of its kv head, is added into it."""
+    probability, summed over the query heads of its kv head, is added into entry
+    t // score_block (score_block = 1: per token; = the page size: per page)."""
     desc = cache_desc(k_cache)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
@@ -205,7 +211,8 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
                                   context_lens, *, max_context_len: int, scale: float = 0.0,
                                   window: int = 0, num_sinks: int = 0, page_list=None,
                                   split_tokens: int = 0, out=None, out_dtype=None, lse=None,
-                                  workspace=None, want_lse: bool = True, timing=None, scores=None):
+                                  workspace=None, want_lse: bool = True, timing=None, scores=None,
+                                  score_block: int = 1):
     """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
     slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
     scores: as in paged_decode_attention."""
@@ -215,7 +222,7 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
@@ -272,6 +279,21 @@ def paged_decode_combine(o_part, m_part, l_part, *, out=None, out_dtype=torch.fl
         _dev(l_part, "l_part", torch.float32), B, Hq, S, d, _dev(out, "out"), DTYPE_CODE[out.dtype],
         _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(o_part)))
     return out, lse
+
+
+def select_pages(scores, context_lens, *, block_size: int, k: int, recent: int = 1, page_list=None):
+    """Next step's page lists [B, k] int32 from page scores [B, heads, stride] float32: the
+    newest `recent` pages plus the k - recent older pages of largest weight (sum over heads),
+    ascending, -1 padded."""
+    if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous [batch, heads, stride] float32 tensor")
+    B, H, stride = scores.shape
+    if page_list is None:
+        page_list = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    _check("paged_select_pages", _lib.paged_select_pages(
+        _dev(scores, "scores", torch.float32), H, stride, _dev(context_lens, "context_lens", torch.int32), B,
+        int(block_size), int(k), int(recent), _dev(page_list, "page_list", torch.int32), _stream(scores)))
+    return page_list
 
 
 def kv_cache_bytes(batch, layers, kv_heads, head_dim, seq_len, dtype_bytes, block_size=0) -> int:

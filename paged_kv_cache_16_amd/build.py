@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["append.hip", "decode.hip", "stream.hip", "api.hip"]
+SOURCES = ["append.hip", "decode.hip", "stream.hip", "select.hip", "api.hip"]
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     # packed-fp32 VALU forms are kept out of the generated code

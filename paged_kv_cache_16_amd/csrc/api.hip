@@ -317,7 +317,10 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
 
     // Validate the workspace and finish the launch parameters before anything is enqueued.
     const bool scores = opts && opts->score_acc;
-    if (scores && opts->score_stride < run.len_cap) return PKV_ERR_SHAPE;
+    const int score_block = scores && opts->score_block > 1 ? opts->score_block : 1;
+    if (scores && opts->score_block < 0) return PKV_ERR_SHAPE;
+    if (scores && opts->score_stride < ((long long)run.len_cap + score_block - 1) / score_block) return PKV_ERR_SHAPE;
+    if (scores && ((long long)run.len_cap + score_block - 1) / score_block > 65535LL * 256) return PKV_ERR_UNSUPPORTED;
     if (scores && (pl.units_bound + 63) / 64 > 65535) return PKV_ERR_UNSUPPORTED;  // score grid's y extent
     long long waves = 0;
     if (pl.path != Plan::kDirect) {
@@ -350,6 +353,7 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
             p.score = opts->score_acc;
             p.score_stride = opts->score_stride;
             p.units_bound = pl.units_bound;
+            p.score_block = score_block;
         }
     } else if (pl.path == Plan::kPartitions) {
         const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);
@@ -511,3 +515,24 @@ const char* pkv_status_string(pkv_status s) {
 }
 
 }  // extern "C"
+
+extern "C" pkv_status paged_select_pages(const float* scores, int32_t heads, int32_t stride,
+                                         const int32_t* context_lens, int32_t batch, int32_t block_size,
+                                         int32_t k, int32_t recent, int32_t* page_list, void* stream) {
+    if (batch < 0 || heads <= 0 || stride < 0 || block_size <= 0) return PKV_ERR_SHAPE;
+    if (k <= 0 || recent < 0 || recent > k) return PKV_ERR_SHAPE;
+    if (k > kSelectMaxK || stride > kSelectMaxPages || batch > 65535) return PKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PKV_OK;
+    if (!scores || !context_lens || !page_list) return PKV_ERR_NULL;
+    SelectParams p;
+    p.scores = scores;
+    p.context_lens = context_lens;
+    p.page_list = page_list;
+    p.heads = heads;
+    p.stride = stride;
+    p.batch = batch;
+    p.block_size = block_size;
+    p.k = k;
+    p.recent = recent;
+    return hip_status(launch_select(p, (hipStream_t)stream));
+}

@@ -74,6 +74,19 @@ struct DecodeParams {
     float* score;
     int32_t score_stride;
     int32_t units_bound;
+    int32_t score_block;   // tokens per score entry (>= 1)
+};
+
+struct SelectParams {
+    const float* scores;   // [batch][heads][stride]
+    const int32_t* context_lens;
+    int32_t* page_list;    // [batch][k]
+    int32_t heads;
+    int32_t stride;
+    int32_t batch;
+    int32_t block_size;
+    int32_t k;
+    int32_t recent;
 };
 
 struct CombineParams {
@@ -97,5 +110,8 @@ hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, b
                                 const DecodeParams& p, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 int stream_blocks_per_cu(int dtype, int head_dim, int mode);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+constexpr int kSelectMaxK = 64;
+constexpr int kSelectMaxPages = 15360;  // page weights held in LDS (60 KiB)
 
 }  // namespace pkv

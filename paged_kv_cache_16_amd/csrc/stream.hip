@@ -537,6 +537,130 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeParams p) {
     }
 }
 
+// Score export with entries of B > 1 tokens (e.g. one per page): thread e owns entry e of
+// a (sequence, kv head) segment and walks its tokens [e*B, (e+1)*B) in 16-token chunks
+// aligned to units. For a chunk whose unit was attended, the stored logits of all G heads
+// (G x 16 floats, contiguous) arrive as 16-byte loads issued together; each token's mass
+// sums its heads in order, and the masses of the entry's attended tokens are added in
+// token order. Entries without attended tokens are not written.
+template <int MODE>
+__global__ __launch_bounds__(256) void score_block_kernel(DecodeParams p) {
+    const int seg = blockIdx.x;
+    const int e = blockIdx.y * 256 + threadIdx.x;
+    const int b = seg / p.kv_heads, kvh = seg - b * p.kv_heads;
+    const int G = p.group, B = p.score_block;
+    // The plan's context length, the page list and the row normalisers are independent
+    // loads: all are issued before any of them is used.
+    const SeqPlan sp = make_plan<MODE>(p, b);
+    float lse2[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) lse2[g] = g < G ? p.row_lse2[(size_t)b * p.q_heads + kvh * G + g] : 0.f;
+    // page-list mode: the sequence's list in LDS, so that finding a page's place in the
+    // list is a scan of LDS (entries beyond kListLds are looked up in memory)
+    constexpr int kListLds = 256;
+    __shared__ int list[MODE == kPages ? kListLds : 1];
+    if (MODE == kPages) {
+        for (int i = threadIdx.x; i < p.pages_per_seq && i < kListLds; i += 256)
+            list[i] = p.page_list[(size_t)b * p.pages_per_seq + i];
+        __syncthreads();
+    }
+    const long long t_lo = (long long)e * B;
+    if (t_lo >= sp.L) return;
+    const int t_hi = (long long)(e + 1) * B < sp.L ? (e + 1) * B : sp.L;
+    const int per = p.block_size >> 4;  // units per page (page-list mode)
+    float acc = 0.f;
+    bool any = false;
+    for (int c0 = (int)(t_lo & ~15LL); c0 < t_hi; c0 += 16) {
+        const int cu = c0 >> 4;  // the chunk's unit position t / 16
+        int u = -1;              // its index among the enumerated units, -1: not enumerated
+        if (MODE == kPages) {
+            const int pg = c0 / p.block_size;
+            for (int kk = 0; kk < p.pages_per_seq; ++kk) {
+                const int v = kk < kListLds ? list[kk] : p.page_list[(size_t)b * p.pages_per_seq + kk];
+                if (v == pg) {
+                    u = kk * per + (cu - pg * per);
+                    break;
+                }
+            }
+        } else if (MODE == kWindow) {
+            if (cu < sp.n0) u = cu;
+            else if (cu >= sp.u1a) u = sp.n0 + (cu - sp.u1a);
+        } else {
+            u = cu;
+        }
+        if (u < 0) continue;
+        const float* lg = p.logits + ((size_t)seg * p.units_bound + u) * G * 16;
+        float m[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m[i] = 0.f;
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            if (g < G) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16 + v4 * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += __builtin_amdgcn_exp2f(x[i] - lse2[g]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = c0 + i;
+            const bool att = t >= t_lo && t < t_hi && (MODE != kWindow || t < sp.e0 || t >= sp.s1);
+            if (att) {
+                acc += m[i];
+                any = true;
+            }
+        }
+    }
+    if (any) p.score[(size_t)seg * p.score_stride + e] += acc;
+}
+
+// Page-list mode with one score entry per page: thread (segment, kk) owns list entry kk,
+// so only listed pages are visited and no search is needed; its page's units are
+// kk * P/16 .. (kk + 1) * P/16 - 1 and its entry is the page id. Same arithmetic and order
+// as score_block_kernel.
+__global__ __launch_bounds__(256) void score_page_kernel(DecodeParams p) {
+    const int seg = blockIdx.x;
+    const int kk = blockIdx.y * 256 + threadIdx.x;
+    if (kk >= p.pages_per_seq) return;
+    const int b = seg / p.kv_heads, kvh = seg - b * p.kv_heads;
+    const int G = p.group;
+    const int pg = p.page_list[(size_t)b * p.pages_per_seq + kk];
+    int L = p.context_lens[b];
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+    float lse2[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) lse2[g] = g < G ? p.row_lse2[(size_t)b * p.q_heads + kvh * G + g] : 0.f;
+    if (pg < 0 || (long long)pg * p.block_size >= L) return;
+    const int per = p.block_size >> 4;
+    float acc = 0.f;
+    for (int c = 0; c < per; ++c) {
+        const int c0 = pg * p.block_size + 16 * c;
+        if (c0 >= L) break;
+        const float* lg = p.logits + ((size_t)seg * p.units_bound + kk * per + c) * G * 16;
+        float m[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m[i] = 0.f;
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            if (g < G) {
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16 + v4 * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += __builtin_amdgcn_exp2f(x[i] - lse2[g]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (c0 + i < L) acc += m[i];
+    }
+    p.score[(size_t)seg * p.score_stride + pg] += acc;
+}
+
 template <class DT, int D, int MODE>
 static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
                                   hipEvent_t e1) {
@@ -566,8 +690,19 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
     stream_combine_kernel<D, MODE, DT::kBytes><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess || !scores) return err;
-    score_kernel<MODE><<<dim3((unsigned)(p.batch * p.kv_heads), (unsigned)((p.units_bound + kScoreUnits - 1) / kScoreUnits)),
-                         dim3(256), 0, s>>>(p);
+    if (MODE == kPages && p.score_block == p.block_size) {
+        score_page_kernel<<<dim3((unsigned)(p.batch * p.kv_heads), (unsigned)((p.pages_per_seq + 255) / 256)),
+                            dim3(256), 0, s>>>(p);
+    } else if (p.score_block > 1) {
+        const long long entries = ((long long)p.len_cap + p.score_block - 1) / p.score_block;
+        if (entries > 0)
+            score_block_kernel<MODE>
+                <<<dim3((unsigned)(p.batch * p.kv_heads), (unsigned)((entries + 255) / 256)), dim3(256), 0, s>>>(p);
+    } else if (p.units_bound > 0) {
+        score_kernel<MODE><<<dim3((unsigned)(p.batch * p.kv_heads),
+                                  (unsigned)((p.units_bound + kScoreUnits - 1) / kScoreUnits)),
+                             dim3(256), 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

@@ -133,3 +133,22 @@ def test_score_export_validation(pkv):
     part = lib.paged_decode_attention_partial
     assert part(ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, 100, 0.0, ctypes.byref(scored),
                 fake, fake, fake, 1, None) == 4         # the partial call exports no scores
+
+
+def test_select_pages_validation(pkv):
+    """paged_select_pages rejects bad shapes and limits on the host (no launch)."""
+    sel = pkv._lib.paged_select_pages
+    fake = ctypes.c_void_p(256)  # never dereferenced
+    assert sel(fake, 4, 100, fake, 2, 16, 65, 1, fake, None) == 3      # k above 64
+    assert sel(fake, 4, 100, fake, 2, 16, 4, 5, fake, None) == 2       # recent above k
+    assert sel(fake, 4, 15361, fake, 2, 16, 4, 1, fake, None) == 3     # pages beyond the LDS table
+    assert sel(fake, 0, 100, fake, 2, 16, 4, 1, fake, None) == 2       # no heads
+    assert sel(None, 4, 100, fake, 2, 16, 4, 1, fake, None) == 1       # missing scores
+    assert sel(None, 4, 100, None, 0, 16, 4, 1, None, None) == 0       # empty batch
+    d = _desc(pkv)
+    call = pkv._lib.paged_decode_attention
+    args = lambda opts: (ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, 100, 0.0, opts, fake, 2,
+                         None, None, 0, None)
+    # per-page entries: 100 tokens in pages of 16 need 7 entries
+    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 6, 16)))) == 2
+    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 7, -2)))) == 2
