@@ -20,7 +20,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "i8bf16": 3, "i8f16": 4}
+# INT8 caches: the pool is raw bytes (int8 data plane, then the fp32 scale plane); their
+# inputs (q, appended rows) are of the named 16-bit type.
+INPUT_DTYPE = {"i8bf16": "bf16", "i8f16": "f16"}
+
+
+def pool_elems(nb, Hkv, P, d, dtype):
+    """Length of a flat pool array (elements for float dtypes, bytes for INT8 ones)."""
+    return nb * Hkv * P * (d + 4) if dtype in INPUT_DTYPE else nb * Hkv * P * d
 
 
 def compile_oracle(src: str, so: str) -> str:
@@ -53,11 +61,26 @@ def _ptr(a):
 
 
 def _raw(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Input arrays (q, rows): raw bits of the input dtype."""
+    dtype = INPUT_DTYPE.get(dtype, dtype)
     want = np.float32 if dtype == "f32" else np.uint16
     a = np.ascontiguousarray(a)
     if a.dtype != want:
         raise TypeError(f"{dtype} data must be passed as {np.dtype(want).name}, got {a.dtype}")
     return a
+
+
+def _raw_pool(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype in INPUT_DTYPE:
+        a = np.ascontiguousarray(a)
+        if a.dtype != np.uint8:
+            raise TypeError(f"{dtype} pools must be passed as uint8 bytes, got {a.dtype}")
+        return a
+    return _raw(a, dtype)
+
+
+def _nb(pool, Hkv, P, d, dtype):
+    return pool.size // (Hkv * P * (d + 4 if dtype in INPUT_DTYPE else d))
 
 
 def _i32(a) -> np.ndarray:
@@ -90,6 +113,8 @@ class Oracle:
         L.oracle_bruteforce.restype = _I
         L.oracle_bruteforce.argtypes = [_I, _P, _P, _I, _P, _I, _I, _I, _I, _P, _D, _I, _I, _I,
                                         _P, _I, _P, _P]
+        L.oracle_quantise_rows.restype = _I
+        L.oracle_quantise_rows.argtypes = [_P, _I, _I, _P, _P]
         L.oracle_kv_cache_bytes.restype = ctypes.c_uint64
         L.oracle_kv_cache_bytes.argtypes = [_I64] * 7
         self.lib = L
@@ -110,17 +135,17 @@ class Oracle:
         for a in (kpool, vpool):
             if not (isinstance(a, np.ndarray) and a.flags.c_contiguous):
                 raise TypeError("pools must be C-contiguous numpy arrays (written in place)")
-        kpool, vpool = _raw(kpool, dtype), _raw(vpool, dtype)
+        kpool, vpool = _raw_pool(kpool, dtype), _raw_pool(vpool, dtype)
         k_new, v_new = _raw(k_new, dtype), _raw(v_new, dtype)
         slots = _i32(slots)
-        nb = kpool.size // (Hkv * P * d)
+        nb = _nb(kpool, Hkv, P, d, dtype)
         self._check(self.lib.oracle_kv_append(DTYPE_CODE[dtype], nb, P, Hkv, d, _ptr(kpool),
                                               _ptr(vpool), _ptr(k_new), _ptr(v_new),
                                               _ptr(slots), slots.size), "kv_append")
         return kpool, vpool
 
     def _common(self, dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list):
-        kpool, vpool, q = _raw(kpool, dtype), _raw(vpool, dtype), _raw(q, dtype)
+        kpool, vpool, q = _raw_pool(kpool, dtype), _raw_pool(vpool, dtype), _raw(q, dtype)
         bt = _i32(block_table)
         cl = _i32(context_lens).reshape(-1)
         B = cl.size
@@ -128,7 +153,7 @@ class Oracle:
         mb = bt.shape[1] if bt.ndim == 2 else 0
         pl = None if page_list is None else _i32(page_list)
         pps = 0 if pl is None else pl.shape[1]
-        nb = kpool.size // (Hkv * P * d)
+        nb = _nb(kpool, Hkv, P, d, dtype)
         return kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb
 
     def decode_attention(self, dtype, kpool, vpool, q, block_table, context_lens, *, P, Hkv, d,
@@ -209,6 +234,15 @@ class Oracle:
             "bruteforce")
         return out, lse
 
+    def quantise_rows(self, x):
+        """x: [n][d] float32 rows -> (int8 [n][d], float32 scales [n])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        n, d = x.shape
+        q = np.zeros((n, d), np.int8)
+        sc = np.zeros(n, np.float32)
+        self._check(self.lib.oracle_quantise_rows(_ptr(x), n, d, _ptr(q), _ptr(sc)), "quantise_rows")
+        return q, sc
+
     def kv_cache_bytes(self, batch, layers, heads, head_dim, seq_len, dtype_bytes,
                        block_size=0) -> int:
         return int(self.lib.oracle_kv_cache_bytes(batch, layers, heads, head_dim, seq_len,
@@ -257,6 +291,10 @@ def select_pages(*a, **k):
 
 def bruteforce(*a, **k):
     return default().bruteforce(*a, **k)
+
+
+def quantise_rows(*a, **k):
+    return default().quantise_rows(*a, **k)
 
 
 def kv_cache_bytes(*a, **k):

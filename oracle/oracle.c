@@ -42,10 +42,19 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+/* ORC_I8_BF16 / ORC_I8_F16: an INT8 cache ([primer] §4.2 and §5.2's int8 KV cache dtype,
+ * which halves the bytes per token) whose inputs (q, new K/V rows) are bf16 / fp16. Such a
+ * pool holds an int8 data plane [num_blocks][Hkv][P][d] in the same lane-chunk order as
+ * the other dtypes (16 elements per 16-byte chunk), followed by an fp32 scale plane
+ * [num_blocks][Hkv][P]: one scale per (token, kv head) row. Element value = int8 * scale. */
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_I8_BF16 = 3, ORC_I8_F16 = 4 };
 enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_PRECONDITION = 2, ORC_ERR_NOMEM = 3 };
 
-static size_t elem_size(int dt) { return dt == ORC_F32 ? 4u : 2u; }
+static int is_q8(int dt) { return dt == ORC_I8_BF16 || dt == ORC_I8_F16; }
+/* dtype of q and of the rows handed to append */
+static int in_dt(int dt) { return dt == ORC_I8_BF16 ? ORC_BF16 : dt == ORC_I8_F16 ? ORC_F16 : dt; }
+/* bytes of one cache element */
+static size_t elem_size(int dt) { return dt == ORC_F32 ? 4u : is_q8(dt) ? 1u : 2u; }
 
 /* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
 static double decode_f16(uint16_t h) {
@@ -105,10 +114,55 @@ static size_t v_index(size_t blk, int h, int t, int x, int Hkv, int P, int d, in
 }
 
 static int shape_ok(int dt, int P, int d) {
-    if (dt != ORC_F32 && dt != ORC_F16 && dt != ORC_BF16) return 0;
+    if (dt < ORC_F32 || dt > ORC_I8_F16) return 0;
     if (P <= 0 || P % 16 != 0) return 0;
     int E = (int)(16 / elem_size(dt));
     return d > 0 && d % (4 * E) == 0 && d % 16 == 0;
+}
+
+/* Value of cache element (blk, h, t, x) of a K (is_v = 0) or V pool. */
+static double load_cache(const void* pool, int64_t num_blocks, size_t blk, int h, int t, int x,
+                         int Hkv, int P, int d, int dt, int is_v) {
+    size_t idx = is_v ? v_index(blk, h, t, x, Hkv, P, d, dt) : k_index(blk, h, t, x, Hkv, P, d, dt);
+    if (!is_q8(dt)) return load_elem(pool, idx, dt);
+    int8_t q;
+    memcpy(&q, (const char*)pool + idx, 1);
+    float sc;
+    size_t plane = (size_t)num_blocks * Hkv * (size_t)P * d;
+    memcpy(&sc, (const char*)pool + plane + (((size_t)blk * Hkv + h) * P + t) * 4, 4);
+    return (double)q * (double)sc;
+}
+
+/* Quantisation of one row of d values for an INT8 cache (symmetric, one scale per
+ * (token, kv head) row, so appending a token never changes earlier ones): with
+ * amax = max |x| in fp32, scale = amax / 127 and q = rint(x * (127 / amax)) clamped to
+ * [-127, 127], both divisions and the product in fp32 (round to nearest even); a zero row
+ * gets scale 0 and q = 0. */
+static float quantise_row(const float* x, int d, int8_t* q) {
+    float amax = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int i = 0; i < d; ++i) q[i] = 0;
+        return 0.0f;
+    }
+    float inv = 127.0f / amax;
+    for (int i = 0; i < d; ++i) {
+        float r = rintf(x[i] * inv);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+    return amax / 127.0f;
+}
+
+/* Exposed for the quantisation pins: quantises `n` rows of d fp32 values. */
+int oracle_quantise_rows(const float* x, int n, int d, int8_t* q, float* scales) {
+    if (!x || !q || !scales || n < 0 || d <= 0) return ORC_ERR_ARG;
+    for (int r = 0; r < n; ++r) scales[r] = quantise_row(x + (size_t)r * d, d, q + (size_t)r * d);
+    return ORC_OK;
 }
 
 /* Exposed so the tests can check the layout against hand-computed positions. */
@@ -127,6 +181,34 @@ int oracle_kv_append(int dt, int64_t num_blocks, int P, int Hkv, int d,
                      void* kpool, void* vpool, const void* knew, const void* vnew,
                      const int32_t* slots, int64_t n) {
     if (!shape_ok(dt, P, d) || Hkv <= 0 || num_blocks < 0 || n < 0) return ORC_ERR_ARG;
+    if (is_q8(dt)) { /* quantise each (token, head) row of K and of V, then store it */
+        float* row = (float*)malloc(sizeof(float) * (size_t)d);
+        int8_t* q = (int8_t*)malloc((size_t)d);
+        if (!row || !q) { free(row); free(q); return ORC_ERR_NOMEM; }
+        size_t plane = (size_t)num_blocks * Hkv * (size_t)P * d;
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t s = slots[i];
+            if (s < 0) continue;
+            if (s >= num_blocks * (int64_t)P) { free(row); free(q); return ORC_ERR_PRECONDITION; }
+            int64_t blk = s / P;
+            int t = (int)(s % P);
+            for (int h = 0; h < Hkv; ++h)
+                for (int is_v = 0; is_v < 2; ++is_v) {
+                    const void* src = is_v ? vnew : knew;
+                    char* pool = (char*)(is_v ? vpool : kpool);
+                    for (int x = 0; x < d; ++x)
+                        row[x] = (float)load_elem(src, ((size_t)i * Hkv + h) * d + x, in_dt(dt));
+                    float sc = quantise_row(row, d, q);
+                    for (int x = 0; x < d; ++x)
+                        pool[is_v ? v_index(blk, h, t, x, Hkv, P, d, dt) : k_index(blk, h, t, x, Hkv, P, d, dt)] =
+                            (char)q[x];
+                    memcpy(pool + plane + (((size_t)blk * Hkv + h) * P + t) * 4, &sc, 4);
+                }
+        }
+        free(row);
+        free(q);
+        return ORC_OK;
+    }
     size_t es = elem_size(dt);
     for (int64_t i = 0; i < n; ++i) {
         int64_t s = slots[i];
@@ -196,8 +278,8 @@ static int64_t gather_logits(int dt, int64_t num_blocks, int P, int Hkv, int d,
         if (blk < 0 || blk >= num_blocks) return -1;
         double dot = 0.0;
         for (int x = 0; x < d; ++x)
-            dot += load_elem(q, ((size_t)b * Hq + h) * d + x, dt) *
-                   load_elem(kpool, k_index(blk, kvh, t % P, x, Hkv, P, d, dt), dt);
+            dot += load_elem(q, ((size_t)b * Hq + h) * d + x, in_dt(dt)) *
+                   load_cache(kpool, num_blocks, (size_t)blk, kvh, t % P, x, Hkv, P, d, dt, 0);
         logits[cnt] = scale * dot;
         toks[cnt] = t;
         ++cnt;
@@ -244,7 +326,7 @@ int oracle_decode_attention(int dt, int64_t num_blocks, int P, int Hkv, int d,
                 int64_t t = toks[k];
                 int64_t blk = block_table[(size_t)b * max_blocks + t / P];
                 for (int x = 0; x < d; ++x)
-                    o[x] += w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);
+                    o[x] += w * load_cache(vpool, num_blocks, (size_t)blk, kvh, (int)(t % P), x, Hkv, P, d, dt, 1);
             }
             for (int x = 0; x < d; ++x) o[x] /= z;
             lse[(size_t)b * Hq + h] = m + log(z);
@@ -426,7 +508,7 @@ int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, in
                 int64_t blk = block_table[(size_t)b * max_blocks + t / P];
                 for (int x = 0; x < d; ++x)
                     po[(size_t)s * d + x] +=
-                        w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);
+                        w * load_cache(vpool, num_blocks, (size_t)blk, kvh, (int)(t % P), x, Hkv, P, d, dt, 1);
             }
             size_t bh = (size_t)b * Hq + h;
             if (o_part) memcpy(o_part + bh * max_splits * d, po, sizeof(double) * (size_t)max_splits * d);

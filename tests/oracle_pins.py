@@ -17,6 +17,7 @@ from types import SimpleNamespace
 import numpy as np
 import torch
 
+import oracle
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -433,6 +434,82 @@ def pin_select_pages(o):
                     assert w[b, a] > w[b, r] or (w[b, a] == w[b, r] and a < r), (case, a, r)
 
 
+def pin_int8_quantise(o):
+    """INT8 rows: the hand-worked cases of tests/golden/int8_rows.json, and on random rows the
+    properties of symmetric rounding quantisation: |q| <= 127, the largest |x| maps to +-127,
+    and every x is within half a step of q * scale."""
+    with open(os.path.join(GOLDEN, "int8_rows.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        q, sc = o.quantise_rows(np.array([c["x"]], np.float32))
+        assert q[0].tolist() == c["q"], (c["what"], q[0].tolist())
+        if "scale" in c:
+            assert float(sc[0]) == c["scale"], c["what"]
+        else:
+            assert abs(float(sc[0]) - c["scale_approx"]) <= c["scale_approx"] * 2.0 ** -23, c["what"]
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((64, 128)) * rng.uniform(0.01, 30, size=(64, 1))).astype(np.float32)
+    q, sc = o.quantise_rows(x)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    amax_pos = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(64), amax_pos]) == 127)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * sc[:, None].astype(np.float64))
+    assert np.all(err <= sc[:, None] * (0.5 + 1e-5)), err.max()
+
+
+def _int8_problem(o, seed, B, Hq, Hkv, d, P, lens):
+    """K/V rows whose largest |value| is 127 * 2^-k (k per row, 5..7) and the rest smaller
+    bf16 values: every scale is 2^-k and every dequantised value rint(x * 2^k) * 2^-k is exact
+    in fp32. Returns the INT8 problem and the fp32 problem holding the dequantised values."""
+    rng = np.random.default_rng(seed)
+    Lmax = max(lens + [1])
+
+    def rows(tag):
+        k = rng.integers(5, 8, size=(B, Lmax, Hkv, 1)).astype(np.float64)
+        amax = 127.0 * 2.0 ** -k
+        x = rng.uniform(-0.95, 0.95, size=(B, Lmax, Hkv, d)) * amax
+        x[..., 0] = amax[..., 0] * np.where(rng.random((B, Lmax, Hkv)) < 0.5, -1.0, 1.0)
+        xb = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+        deq = np.rint(xb.to(torch.float64).numpy() * 2.0 ** k) * 2.0 ** -k
+        return xb, torch.tensor(deq, dtype=torch.float32)
+
+    K, Kd = rows("k")
+    V, Vd = rows("v")
+    q = synth.normal((B, Hq, d), seed, "q", dtype="bf16")
+    lens = [int(x) for x in lens]
+    bt, nb = synth.block_tables(lens, P, seed, spare_blocks=1)
+    slots = synth.token_slots(bt, lens, P)
+    out = []
+    for dtype, KK, VV, qq in (("i8bf16", K, V, q), ("f32", Kd, Vd, q.to(torch.float32))):
+        if dtype == "i8bf16":
+            kpool = np.zeros(nb * Hkv * P * (d + 4), np.uint8)
+            vpool = np.zeros_like(kpool)
+        else:
+            kpool = np.full(nb * Hkv * P * d, np.float32(np.nan), np.float32)
+            vpool = np.full_like(kpool, np.float32(np.nan))
+        kn = torch.cat([KK[b, :L] for b, L in enumerate(lens)])
+        vn = torch.cat([VV[b, :L] for b, L in enumerate(lens)])
+        o.kv_append(dtype, kpool, vpool, synth.raw_numpy(kn), synth.raw_numpy(vn), slots.numpy(), P=P, Hkv=Hkv, d=d)
+        out.append(SimpleNamespace(q=qq, bt=bt, nb=nb, lens=lens, kpool=kpool, vpool=vpool, P=P, Hkv=Hkv, Hq=Hq,
+                                   d=d, dtype=dtype, B=B))
+    return out
+
+
+def pin_int8_attention(o):
+    """Attention (and scores) over an INT8 cache equal attention over an fp32 cache holding
+    the same dequantised values (rows built so that they are exact): int8 plane layout, scale
+    plane and dequantisation, in every mode."""
+    pr8, pr32 = _int8_problem(o, 500, B=3, Hq=4, Hkv=2, d=64, P=16, lens=[70, 33, 1])
+    pl = np.array([[0, 3, -1], [1, 2, -1], [0, -1, -1]], np.int32)
+    for kw in (dict(), dict(window=20, sinks=3), dict(page_list=pl)):
+        a8 = attend(o, pr8, **kw)
+        a32 = attend(o, pr32, **kw)
+        assert np.abs(a8[0] - a32[0]).max() <= 1e-12 and np.abs(a8[1] - a32[1]).max() <= 1e-12, kw
+        s8 = scores(o, pr8, 70, **kw)
+        s32 = scores(o, pr32, 70, **kw)
+        assert np.abs(s8 - s32).max() <= 1e-12, kw
+
+
 def pin_empty(o):
     pr = build(o, 14, B=2, Hq=2, Hkv=1, d=64, dtype="f16", P=16, lens=[0, 3])
     out, lse = attend(o, pr)
@@ -443,7 +520,7 @@ PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundt
         pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
         pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
         pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_scores_block, pin_select_pages,
-        pin_empty]
+        pin_int8_quantise, pin_int8_attention, pin_empty]
 
 
 if __name__ == "__main__":

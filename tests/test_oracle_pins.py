@@ -44,6 +44,11 @@ MUTATIONS = [
     ("page weights in double", "float acc = 0.0f;", "double acc = 0.0;"),
     ("newest page not forced", "for (int64_t p = first_recent; p < n; ++p) row[cnt++] = (int32_t)p;", ";"),
     ("k pages besides the newest", "int64_t want = k - recent;", "int64_t want = k;"),
+    ("int8 rounding truncates", "float r = rintf(x[i] * inv);", "float r = truncf(x[i] * inv);"),
+    ("int8 scale not applied", "return (double)q * (double)sc;", "return (double)q;"),
+    ("int8 scale per tile, not per row", "memcpy(&sc, (const char*)pool + plane + (((size_t)blk * Hkv + h) * P + t) * 4, 4);",
+     "memcpy(&sc, (const char*)pool + plane + (((size_t)blk * Hkv + h) * P) * 4, 4);"),
+    ("int8 amax from the first element", "if (a > amax) amax = a;", "if (i == 0) amax = a;"),
 ]
 
 
