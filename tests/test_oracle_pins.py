@@ -19,8 +19,8 @@ MUTATIONS = [
      "(size_t)(x / (4 * E)) * 16 + (size_t)((x / E) % 4) * 64 + tau"),
     ("V token split transposed", "int n = x / 16, c = x % 16, j = tau / 4, i = tau % 4;",
      "int n = x / 16, c = x % 16, j = tau % 4, i = tau / 4;"),
-    ("V read from K pool", "o[x] += w * load_elem(vpool, v_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);",
-     "o[x] += w * load_elem(kpool, k_index(blk, kvh, (int)(t % P), x, Hkv, P, d, dt), dt);"),
+    ("V read from K pool", "o[x] += w * load_cache(vpool, num_blocks, (size_t)blk, kvh, (int)(t % P), x, Hkv, P, d, dt, 1);",
+     "o[x] += w * load_cache(kpool, num_blocks, (size_t)blk, kvh, (int)(t % P), x, Hkv, P, d, dt, 0);"),
     ("normaliser not shifted", "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);",
      "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k]);"),
     ("block index uses offset", "int64_t blk = bt_row[t / P];", "int64_t blk = bt_row[t % P];"),
