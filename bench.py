@@ -12,7 +12,7 @@ cache; every replica has the same context lengths, so the bytes per step are fix
 Prints one JSON line. value = algorithmic KV bytes per step (the attended tokens' K and
 V rows, sum(L) * 2 * Hkv * d * 2 bytes) / wall time per step. roofline = the split
 kernel alone: the same bytes / its mean duration from HIP events recorded on the
-launch stream around every timed launch.
+launch stream around every 8th timed launch (--event-every).
 """
 from __future__ import annotations
 
@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--scores", action="store_true",
                     help="default workload: every step also exports the decode-time KV scores "
                          "(softmax probability per token and kv head, accumulated over steps)")
+    ap.add_argument("--kv-dtype", default=None, choices=[None, "int8"],
+                    help="default workload: keep the cache in INT8 (per-row scales); bytes count the int8 "
+                         "data plus the scales actually read")
     ap.add_argument("--loop", action="store_true",
                     help="page-selected workload: close the loop; each step exports per-page scores and "
                          "paged_select_pages picks the next step's pages from them (newest page kept)")
@@ -121,7 +124,9 @@ class HipEvents:
         self.lib.hipEventDestroy(h)
 
 
-def build_replica(w, lens, seed, r, dev):
+def build_replica(w, lens, seed, r, dev, kv_dtype=None):
+    """One replica of the workload's caches and step inputs. kv_dtype "int8": an INT8 cache
+    filled by the quantising append from the same rows."""
     import torch
 
     import paged_kv_cache_16_amd as pkv
@@ -130,7 +135,7 @@ def build_replica(w, lens, seed, r, dev):
     B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
     tdt = synth.TORCH_DTYPE[w.dtype]
     bt, nb = synth.block_tables(lens, P, seed, w.name, r)
-    gk = torch.empty((nb, Hkv, P, d), dtype=tdt, device=dev)
+    gk = pkv.new_cache(nb, Hkv, P, d, torch.int8 if kv_dtype == "int8" else tdt, device=dev)
     gv = torch.empty_like(gk)
     for b, L in enumerate(lens):  # prefill: tokens [0, L-1) of every sequence
         if L > 1:
@@ -467,7 +472,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    reps = [build_replica(w, lens, args.seed, r, dev) for r in range(args.replicas)]
+    reps = [build_replica(w, lens, args.seed, r, dev, args.kv_dtype) for r in range(args.replicas)]
+    if args.kv_dtype == "int8":  # K and V: d int8 bytes + one fp32 scale per token and kv head
+        kv_bytes = sum(lens) * 2 * w.kv_heads * (w.head_dim + 4)
     torch.cuda.synchronize()
     B, Hq, d = w.batch, w.q_heads, w.head_dim
     mcl = max(lens)
@@ -527,27 +534,31 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
             "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
             "replicas": args.replicas, "split_tokens": args.split_tokens,
-            "step": "paged_decode_append_attention: append of the 32 new tokens fused into the "
-                    "persistent split kernel, then the LSE combine"
+            "step": ("paged_decode_append_attention: append of the 32 new tokens fused into the "
+                     "persistent split kernel, then the LSE combine" if args.kv_dtype != "int8" else
+                     "paged_decode_append_attention on an INT8 cache: quantising append of the 32 new "
+                     "tokens, then the persistent split kernel and the LSE combine")
                     + (", plus the decode-time KV score export" if args.scores else ""),
+            "kv_dtype": args.kv_dtype or w.dtype,
             "parallelism": "single GPU",
         },
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": "decode_stream_kernel<BF16,128,full,fused append>"
+            "bound": "hbm", "kernel": ("decode_stream_kernel<I8B,128,full>" if args.kv_dtype == "int8" else
+                                       "decode_stream_kernel<BF16,128,full,fused append>")
             if args.split_tokens == 0 else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if args.scores else measured_traffic(w.name, args.split_tokens),
+            "traffic": None if (args.scores or args.kv_dtype) else measured_traffic(w.name, args.split_tokens),
             "traffic_unit": "bytes per launch",
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
             "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),
         },
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.kv_dtype:
         res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_seconds, dev)
     print(json.dumps(res), flush=True)
 

@@ -80,17 +80,30 @@ typedef enum {
     PKV_ERR_HIP = 6          /* the HIP runtime reported a launch error */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
 
 /* Shape of one layer's cache (one K pool and one V pool, same shape and dtype).
- * Supported: dtype in {F32, F16, BF16}; head_dim in {64, 128};
- * block_size a multiple of 16 in [16, 256]. */
+ * Supported: dtype in {F32, F16, BF16, I8}; head_dim in {64, 128};
+ * block_size a multiple of 16 in [16, 256].
+ *
+ * INT8 caches ([primer] §4.2 and §5.2: an int8 KV cache dtype halves the bytes per
+ * token). A PKV_I8 pool is one buffer: an int8 data plane of num_blocks x num_kv_heads x
+ * block_size x head_dim bytes in the lane-chunk order below (E = 16), followed by an fp32
+ * scale plane [num_blocks][num_kv_heads][block_size], one scale per (token, kv head) row:
+ * element value = int8 * scale. kv_cache_append quantises each appended row
+ * symmetrically: amax = max |x| (fp32), scale = amax / 127, q = rint(x * (127 / amax))
+ * clamped to [-127, 127], both divisions correctly rounded in fp32 (round to nearest
+ * even); a zero row gets scale 0. Rows are never re-quantised. q, k_new and v_new of an
+ * INT8 cache are of input_dtype (BF16 or F16). Attention over an INT8 cache always uses
+ * the work-split path (split_tokens must be 0, else PKV_ERR_UNSUPPORTED), and the partial
+ * call does not accept it (PKV_ERR_UNSUPPORTED). */
 typedef struct {
     int32_t num_blocks;   /* physical blocks in each pool */
     int32_t block_size;   /* tokens per block (page size P) */
     int32_t num_kv_heads; /* Hkv */
     int32_t head_dim;     /* d */
-    pkv_dtype dtype;      /* element type of the pools, of k_new/v_new and of q */
+    pkv_dtype dtype;      /* element type of the pools, and of k_new/v_new and q unless I8 */
+    pkv_dtype input_dtype; /* PKV_I8 only: type of q, k_new, v_new (BF16 or F16) */
 } pkv_cache_desc;
 
 /* Which cached tokens one decode step attends to, and a tuning knob.

@@ -21,7 +21,7 @@ __all__ = [
     "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
-    "select_pages",
+    "select_pages", "new_cache",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -42,7 +42,7 @@ _sz = ctypes.c_size_t
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("num_kv_heads", _i32),
-                ("head_dim", _i32), ("dtype", ctypes.c_int)]
+                ("head_dim", _i32), ("dtype", ctypes.c_int), ("input_dtype", ctypes.c_int)]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -111,13 +111,37 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+def cache_desc(k_cache: torch.Tensor, input_dtype=None) -> CacheDesc:
+    """Descriptor of a cache tensor. An INT8 cache is a torch.int8 tensor
+    [num_blocks, num_kv_heads, block_size, head_dim + 4] holding the int8 data plane followed
+    by the fp32 scale plane (see new_cache); input_dtype is then the type of q and of the
+    appended rows (bf16 by default)."""
     if k_cache.dim() != 4:
         raise ValueError("cache tensors are [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, P, d = k_cache.shape
+    if k_cache.dtype == torch.int8:
+        ind = DTYPE_CODE.get(input_dtype or torch.bfloat16)
+        if ind not in (1, 2):
+            raise ValueError("an INT8 cache takes bf16 or fp16 inputs")
+        return CacheDesc(nb, P, hkv, d - 4, 3, ind)
     if k_cache.dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
-    nb, hkv, P, d = k_cache.shape
-    return CacheDesc(nb, P, hkv, d, DTYPE_CODE[k_cache.dtype])
+    return CacheDesc(nb, P, hkv, d, DTYPE_CODE[k_cache.dtype], 0)
+
+
+def input_dtype_of(k_cache: torch.Tensor, other: torch.Tensor | None = None):
+    """Type of q / appended rows for this cache (the cache's own, or other's for INT8)."""
+    if k_cache.dtype == torch.int8:
+        return other.dtype if other is not None else torch.bfloat16
+    return k_cache.dtype
+
+
+def new_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype, device="cuda"):
+    """An uninitialised cache tensor. dtype torch.int8 gives an INT8 cache: int8 data plane
+    plus fp32 scale plane, shaped [num_blocks, num_kv_heads, block_size, head_dim + 4]."""
+    if dtype == torch.int8:
+        return torch.empty((num_blocks, num_kv_heads, block_size, head_dim + 4), dtype=torch.int8, device=device)
+    return torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
 
 
 def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None,
@@ -140,13 +164,13 @@ def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, sc
 
 def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
     """Scatter k_new/v_new [N, Hkv, d] into the pools at slot_mapping[N] (int32, <0 = skip)."""
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, k_new.dtype)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
     n = slot_mapping.numel()
     _check("kv_cache_append", _lib.kv_cache_append(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
+        _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
         _dev(slot_mapping, "slot_mapping", torch.int32), n, _stream(k_cache)))
 
 
@@ -185,7 +209,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
     scores: optional [B, Hkv, stride] float32 tensor; every attended token's softmax
     probability, summed over the query heads of its kv head, is added into entry
     t // score_block (score_block = 1: per token; = the page size: per page)."""
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, q.dtype)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
@@ -200,7 +224,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("paged_decode_attention", _lib.paged_decode_attention(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(q, "q", k_cache.dtype), _dev(block_table, "block_table", torch.int32),
+        _dev(q, "q", input_dtype_of(k_cache, q)), _dev(block_table, "block_table", torch.int32),
         block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq,
         int(max_context_len), float(scale), ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
         _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q)))
@@ -216,7 +240,7 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
     """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
     slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
     scores: as in paged_decode_attention."""
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, q.dtype)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
@@ -233,8 +257,8 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         raise ValueError("one new token per sequence: k_new/v_new [B, Hkv, d], slot_mapping [B]")
     _check("paged_decode_append_attention", _lib.paged_decode_append_attention(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
-        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", k_cache.dtype),
+        _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
+        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", input_dtype_of(k_cache, q)),
         _dev(block_table, "block_table", torch.int32), block_table.shape[1],
         _dev(context_lens, "context_lens", torch.int32), B, Hq, int(max_context_len), float(scale),
         ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
@@ -247,7 +271,7 @@ def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_len
                                    window: int = 0, num_sinks: int = 0, page_list=None,
                                    o_part=None, m_part=None, l_part=None):
     """Split-K partials (o [B,Hq,S,d], m [B,Hq,S], l [B,Hq,S], fp32) over explicit partitions."""
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, q.dtype)
     B, Hq, d = q.shape
     o = _opts(window, num_sinks, page_list, split_tokens)
     S = int(_lib.paged_decode_attention_num_splits(ctypes.byref(desc), B, max_context_len, ctypes.byref(o)))
@@ -259,7 +283,7 @@ def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_len
         l_part = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _check("paged_decode_attention_partial", _lib.paged_decode_attention_partial(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(q, "q", k_cache.dtype), _dev(block_table, "block_table", torch.int32),
+        _dev(q, "q", input_dtype_of(k_cache, q)), _dev(block_table, "block_table", torch.int32),
         block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq,
         int(max_context_len), float(scale), ctypes.byref(o), _dev(o_part, "o_part", torch.float32),
         _dev(m_part, "m_part", torch.float32), _dev(l_part, "l_part", torch.float32), S, _stream(q)))

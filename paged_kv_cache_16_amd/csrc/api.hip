@@ -21,13 +21,22 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : 2; }
+int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : t == PKV_I8 ? 1 : 2; }
 
-bool dtype_ok(int t) { return t == PKV_F32 || t == PKV_F16 || t == PKV_BF16; }
+bool dtype_ok(int t) { return t == PKV_F32 || t == PKV_F16 || t == PKV_BF16 || t == PKV_I8; }
+
+// Library-internal element code of a cache (INT8 caches by their input type).
+int kdt(const pkv_cache_desc* d) {
+    if (d->dtype == PKV_I8) return d->input_dtype == PKV_F16 ? kI8H : kI8B;
+    return (int)d->dtype;
+}
+// The type of q and of the outputs other than fp32.
+pkv_dtype io_dtype(const pkv_cache_desc* d) { return d->dtype == PKV_I8 ? d->input_dtype : d->dtype; }
 
 pkv_status check_desc(const pkv_cache_desc* d) {
     if (!d) return PKV_ERR_NULL;
     if (!dtype_ok(d->dtype)) return PKV_ERR_UNSUPPORTED;
+    if (d->dtype == PKV_I8 && d->input_dtype != PKV_BF16 && d->input_dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
     if (d->num_blocks < 0 || d->num_kv_heads <= 0 || d->block_size <= 0) return PKV_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (d->block_size % 16 != 0 || d->block_size > 256) return PKV_ERR_UNSUPPORTED;
@@ -49,14 +58,16 @@ struct Plan {
     enum Path { kDirect, kPartitions, kStream } path = kDirect;
     int kmax = 0;       // stream path: partial slots per segment
     int chunk_min = 0;  // stream path: minimum units per wave
+    bool q8 = false;    // INT8 cache: the stream path only
 };
 
 // Path selection for paged_decode_attention (the partial call always uses partitions).
 void choose_path(Plan& pl, const pkv_decode_opts* o) {
-    const bool scores = o && o->score_acc;
+    // score export and INT8 caches exist on the stream path only
+    const bool stream_only = (o && o->score_acc) || pl.q8;
     if (o && o->split_tokens > 0) {
         pl.path = pl.num_splits > 1 ? Plan::kPartitions : Plan::kDirect;
-    } else if (pl.units_bound <= kDirectMaxUnits && !scores) {
+    } else if (pl.units_bound <= kDirectMaxUnits && !stream_only) {
         pl.path = Plan::kDirect;
         pl.num_splits = 1;
         pl.units_per_split = kDirectMaxUnits;
@@ -72,7 +83,7 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
 
 struct DeviceInfo {
     int cus = 0;
-    int occupancy[3][2][3] = {};  // [dtype][head_dim 64/128][mode] workgroups per CU
+    int occupancy[5][2][3] = {};  // [internal dtype][head_dim 64/128][mode] workgroups per CU
 };
 DeviceInfo g_dev[64];
 
@@ -108,6 +119,7 @@ pkv_status check_opts(const pkv_decode_opts* o) {
 Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_blocks,
                const pkv_decode_opts* o) {
     Plan pl;
+    pl.q8 = d->dtype == PKV_I8;
     const int P = d->block_size;
     long long cap = max_context_len;
     if (max_blocks >= 0 && (long long)max_blocks * P < cap) cap = (long long)max_blocks * P;
@@ -250,7 +262,7 @@ pkv_status kv_cache_append(const pkv_cache_desc* desc, void* k_cache, void* v_ca
     p.block_size = desc->block_size;
     p.kv_heads = desc->num_kv_heads;
     p.head_dim = desc->head_dim;
-    return hip_status(launch_append(desc->dtype, p, (hipStream_t)stream));
+    return hip_status(launch_append(kdt(desc), p, (hipStream_t)stream));
 }
 
 size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
@@ -297,7 +309,8 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq,
                                       context_lens, batch, num_q_heads, max_context_len, opts);
     if (st != PKV_OK) return st;
-    if (out_dtype != PKV_F32 && out_dtype != desc->dtype) return PKV_ERR_UNSUPPORTED;
+    if (out_dtype != PKV_F32 && out_dtype != io_dtype(desc)) return PKV_ERR_UNSUPPORTED;
+    if (desc->dtype == PKV_I8 && opts && opts->split_tokens > 0) return PKV_ERR_UNSUPPORTED;
     if (batch == 0) return PKV_OK;
     if (!out) return PKV_ERR_NULL;
     // The plan (and so the workspace size) ignores max_blocks_per_seq so that the size
@@ -335,7 +348,7 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
         const long long resident =
-            (long long)device_cus(dev) * device_occupancy(dev, desc->dtype, desc->head_dim, pl.mode) * kWaves;
+            (long long)device_cus(dev) * device_occupancy(dev, kdt(desc), desc->head_dim, pl.mode) * kWaves;
         waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
         if (waves > resident) waves = resident;
         waves = (waves + kWaves - 1) / kWaves * kWaves;
@@ -363,7 +376,8 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.l_part = (float*)((char*)workspace + wl.l_off);
     }
 
-    if (fa && pl.path != Plan::kStream) {  // separate append launch ahead of attention
+    const bool fuse = fa && pl.path == Plan::kStream && desc->dtype != PKV_I8;
+    if (fa && !fuse) {  // separate append launch ahead of attention
         AppendParams ap;
         ap.k_cache = fa->k_cache;
         ap.v_cache = fa->v_cache;
@@ -375,17 +389,17 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         ap.block_size = desc->block_size;
         ap.kv_heads = desc->num_kv_heads;
         ap.head_dim = desc->head_dim;
-        st = hip_status(launch_append(desc->dtype, ap, s));
+        st = hip_status(launch_append(kdt(desc), ap, s));
         if (st != PKV_OK) return st;
     }
     if (pl.path == Plan::kDirect) {
         if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
-        st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, true, p, batch, s));
+        st = hip_status(launch_decode(kdt(desc), desc->head_dim, pl.mode, true, p, batch, s));
         if (st == PKV_OK && ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
         return st;
     }
     if (pl.path == Plan::kStream) {
-        if (fa) {
+        if (fuse) {
             p.k_cache_w = (char*)fa->k_cache;
             p.v_cache_w = (char*)fa->v_cache;
             p.k_new = (const char*)fa->k_new;
@@ -394,10 +408,10 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
             p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
         }
         return hip_status(
-            launch_decode_stream(desc->dtype, desc->head_dim, pl.mode, fa != nullptr, scores, p, s, ev0, ev1));
+            launch_decode_stream(kdt(desc), desc->head_dim, pl.mode, fuse, scores, p, s, ev0, ev1));
     }
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return PKV_ERR_HIP;
-    st = hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch, s));
+    st = hip_status(launch_decode(kdt(desc), desc->head_dim, pl.mode, false, p, batch, s));
     if (st != PKV_OK) return st;
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return PKV_ERR_HIP;
     CombineParams cp;
@@ -455,6 +469,7 @@ pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void
                                       context_lens, batch, num_q_heads, max_context_len, opts);
     if (st != PKV_OK) return st;
     if (opts && opts->score_acc) return PKV_ERR_MODE;  // score export is not part of the partial call
+    if (desc->dtype == PKV_I8) return PKV_ERR_UNSUPPORTED;
     const Plan pl = make_plan(desc, batch, max_context_len, -1, opts);
     if (num_splits != pl.num_splits) return PKV_ERR_SHAPE;
     if (batch == 0) return PKV_OK;
@@ -466,7 +481,7 @@ pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
-    return hip_status(launch_decode(desc->dtype, desc->head_dim, pl.mode, false, p, batch,
+    return hip_status(launch_decode(kdt(desc), desc->head_dim, pl.mode, false, p, batch,
                                     (hipStream_t)stream));
 }
 

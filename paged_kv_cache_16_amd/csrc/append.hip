@@ -64,7 +64,88 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     }
 }
 
+// INT8 cache ([primer] §4.2: the int8 KV cache halves the bytes per token). One wavefront
+// quantises one (token, kv head) row of K and of V: amax = max |x| in fp32 (a wave-wide
+// max), scale = amax / 127, q = rint(x * (127 / amax)) clamped to [-127, 127], both
+// divisions correctly rounded in fp32, a zero row giving scale 0 and q = 0 (symmetric, one
+// scale per row, so no earlier token is ever re-quantised). The bytes go to the row's
+// lane-chunk positions (16 elements per chunk) and the scale to the pool's fp32 scale
+// plane [num_blocks][Hkv][P], which follows the data plane.
+template <class In>
+__device__ __forceinline__ float in_f32(const void* base, size_t idx) {
+    const unsigned short h = reinterpret_cast<const unsigned short*>(base)[idx];
+    if constexpr (__is_same(In, BF16))
+        return __uint_as_float((unsigned)h << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+template <class In, int D>
+__global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
+    constexpr int PER = D / 64;  // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= p.num_tokens * p.kv_heads) return;
+    const int64_t i = row / p.kv_heads;
+    const int h = (int)(row - i * p.kv_heads);
+    const int64_t slot = p.slots[i];
+    if (slot < 0 || slot >= p.num_slots) return;
+    const int64_t blk = slot / p.block_size;
+    const int t = (int)(slot - blk * p.block_size);
+    const int tau = t & 15;
+    const size_t sub = (((size_t)blk * p.kv_heads + h) * p.block_size + (t - tau)) * (size_t)D;
+    const size_t plane = (size_t)p.num_slots * p.kv_heads * D;  // bytes of the data plane
+    const size_t srow = ((size_t)blk * p.kv_heads + h) * p.block_size + t;
+#pragma unroll
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        const void* src = is_v ? p.v_new : p.k_new;
+        char* pool = (char*)(is_v ? p.v_cache : p.k_cache);
+        float x[PER];
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            x[e] = in_f32<In>(src, (size_t)row * D + lane + 64 * e);
+            amax = fmaxf(amax, fabsf(x[e]));
+        }
+        amax = wave_max(amax);
+        const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            float r = amax > 0.f ? rintf(x[e] * inv) : 0.f;
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            const int xd = lane + 64 * e;
+            size_t pos;
+            if (is_v) {
+                const int n = xd >> 4;
+                pos = (((size_t)(n >> 2) * 4 + (tau >> 2)) * 16 + (xd & 15)) * 16 + (size_t)(n & 3) * 4 + (tau & 3);
+            } else {
+                pos = ((size_t)(xd >> 6) * 64 + (size_t)((xd >> 4) & 3) * 16 + tau) * 16 + (xd & 15);
+            }
+            pool[sub + pos] = (char)(signed char)(int)r;
+        }
+        if (lane == 0) *reinterpret_cast<float*>(pool + plane + srow * 4) = amax > 0.f ? __fdiv_rn(amax, 127.f) : 0.f;
+    }
+}
+
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s) {
+    if (dtype == kI8B || dtype == kI8H) {
+        const int64_t rows = p.num_tokens * p.kv_heads;
+        const int64_t blocks = (rows + 3) / 4;
+        if (blocks <= 0) return hipSuccess;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 g((unsigned)blocks), b(256);
+        if (dtype == kI8B)
+            p.head_dim == 64 ? append_q8_kernel<BF16, 64><<<g, b, 0, s>>>(p) : append_q8_kernel<BF16, 128><<<g, b, 0, s>>>(p);
+        else
+            p.head_dim == 64 ? append_q8_kernel<F16, 64><<<g, b, 0, s>>>(p) : append_q8_kernel<F16, 128><<<g, b, 0, s>>>(p);
+        return hipGetLastError();
+    }
     const int E = dtype == kF32 ? 4 : 8;
     const int64_t threads = p.num_tokens * p.kv_heads * (p.head_dim / E);
     const int64_t blocks = (threads + 255) / 256;

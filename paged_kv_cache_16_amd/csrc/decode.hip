@@ -294,6 +294,8 @@ hipError_t launch_decode(int dtype, int head_dim, int mode, bool direct, const D
     switch (dtype) {
         case kF32: return launch_decode_d<F32>(head_dim, mode, direct, p, batch, s);
         case kF16: return launch_decode_d<F16>(head_dim, mode, direct, p, batch, s);
+        case kI8B:
+        case kI8H: return hipErrorInvalidValue;  // INT8 caches take the stream path only
         default: return launch_decode_d<BF16>(head_dim, mode, direct, p, batch, s);
     }
 }

@@ -29,18 +29,79 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // dtype tags -----------------------------------------------------------------------------
+// kBytes / kE: bytes and elements of one cache element / 16-byte chunk. In: the type of q
+// and of the MFMA operands. kQ8: an INT8 cache (int8 data plane + fp32 row-scale plane).
 struct F32 {
     static constexpr int kBytes = 4;
     static constexpr int kE = 4;  // elements per 16-byte chunk
+    static constexpr bool kQ8 = false;
+    using In = F32;
 };
 struct F16 {
     static constexpr int kBytes = 2;
     static constexpr int kE = 8;
+    static constexpr bool kQ8 = false;
+    using In = F16;
 };
 struct BF16 {
     static constexpr int kBytes = 2;
     static constexpr int kE = 8;
+    static constexpr bool kQ8 = false;
+    using In = BF16;
 };
+// INT8 caches with bf16 / fp16 inputs. A 16-byte chunk holds 16 elements; converted, it is
+// exactly two chunks of the input type (int8 values are exact in bf16 and fp16).
+struct I8B {
+    static constexpr int kBytes = 1;
+    static constexpr int kE = 16;
+    static constexpr bool kQ8 = true;
+    using In = BF16;
+};
+struct I8H {
+    static constexpr int kBytes = 1;
+    static constexpr int kE = 16;
+    static constexpr bool kQ8 = true;
+    using In = F16;
+};
+
+// Sign-extended byte k (0..3) of w, as a float.
+__device__ __forceinline__ float sbyte_f32(unsigned w, int k) {
+    // the builtin is typed unsigned; its bits are the sign-extended byte
+    return (float)(int)__builtin_amdgcn_sbfe(w, 8 * k, 8);
+}
+// 16 int8 values -> two chunks of 8 bf16 / fp16 (elements 0..7, 8..15), exact.
+template <class In>
+__device__ __forceinline__ void widen_i8(const u32x4& c, u32x4& lo, u32x4& hi);
+template <>
+__device__ __forceinline__ void widen_i8<BF16>(const u32x4& c, u32x4& lo, u32x4& hi) {
+    unsigned o[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // bf16 of a small integer = the upper half of its fp32 bits (the low half is zero);
+        // one byte permute joins the upper halves of two values
+        const unsigned f0 = __float_as_uint(sbyte_f32(c[w], 0)), f1 = __float_as_uint(sbyte_f32(c[w], 1));
+        const unsigned f2 = __float_as_uint(sbyte_f32(c[w], 2)), f3 = __float_as_uint(sbyte_f32(c[w], 3));
+        o[2 * w] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        o[2 * w + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    }
+    lo = u32x4{o[0], o[1], o[2], o[3]};
+    hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+template <>
+__device__ __forceinline__ void widen_i8<F16>(const u32x4& c, u32x4& lo, u32x4& hi) {
+    unsigned o[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const _Float16 h0 = (_Float16)sbyte_f32(c[w], 0), h1 = (_Float16)sbyte_f32(c[w], 1);
+        const _Float16 h2 = (_Float16)sbyte_f32(c[w], 2), h3 = (_Float16)sbyte_f32(c[w], 3);
+        o[2 * w] = (unsigned)__builtin_bit_cast(unsigned short, h0) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, h1) << 16);
+        o[2 * w + 1] = (unsigned)__builtin_bit_cast(unsigned short, h2) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, h3) << 16);
+    }
+    lo = u32x4{o[0], o[1], o[2], o[3]};
+    hi = u32x4{o[4], o[5], o[6], o[7]};
+}
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 // Streaming load for data read exactly once (K/V tiles): the nontemporal hint keeps the

@@ -8,7 +8,8 @@
 namespace pkv {
 
 enum Mode : int { kFull = 0, kWindow = 1, kPages = 2 };
-enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// kI8B / kI8H: INT8 cache with bf16 / fp16 inputs (library-internal codes)
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8B = 3, kI8H = 4 };
 
 constexpr int kWaves = 4;           // wavefronts per workgroup of the split kernel
 constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane

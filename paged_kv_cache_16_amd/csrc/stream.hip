@@ -88,6 +88,7 @@ template <class DT, int D>
 struct RingBuf {
     static constexpr int NC = D / (4 * DT::kE);
     u32x4 k[NC], v[NC];
+    f32x4 ks, vs;  // INT8 caches: row scales of the lane's tokens 4j..4j+3 (K, V)
     int t0;
     int u;  // unit index within the segment
 };
@@ -107,6 +108,13 @@ __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>&
         for (int cc = 0; cc < NC; ++cc) rb.k[cc] = load16_stream(kp + cc * 1024);
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) rb.v[cc] = load16_stream(vp + cc * 1024);
+        if constexpr (DT::kQ8) {
+            // scale plane after the data plane; the sub-tile's first row is off / D
+            const size_t plane = (size_t)p.num_blocks * p.kv_heads * p.block_size * D;
+            const size_t srow = off / D + 4 * (lane >> 4);
+            rb.ks = *reinterpret_cast<const f32x4*>(p.k_cache + plane + srow * 4);
+            rb.vs = *reinterpret_cast<const f32x4*>(p.v_cache + plane + srow * 4);
+        }
     }
 }
 
@@ -209,8 +217,11 @@ constexpr int kLgFloats = 1024;
 template <class DT, int D, int MODE, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
-    using T = Tile<DT, D / (4 * DT::kE)>;
-    constexpr int NC = D / (4 * DT::kE);
+    static_assert(!(DT::kQ8 && FUSED), "INT8 caches take the separate quantising append");
+    using TI = typename DT::In;               // q and MFMA operand type
+    constexpr int NC = D / (4 * TI::kE);      // operand chunks per lane (q, widened K/V)
+    constexpr int NCC = D / (4 * DT::kE);     // cache chunks per lane (K, V)
+    using T = Tile<TI, NC>;
     constexpr int NACC = T::kAcc;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -275,17 +286,25 @@ void decode_stream_kernel(DecodeParams p) {
 #pragma unroll
         for (int kk = 0; kk < NC; ++kk) q[kk] = u32x4{0u, 0u, 0u, 0u};
         if (qhead < G) {
-            const char* qp = p.q + (((size_t)b * p.q_heads + kvh * G + qhead) * D + j * DT::kE) * DT::kBytes;
+            const char* qrow = p.q + ((size_t)b * p.q_heads + kvh * G + qhead) * D * TI::kBytes;
+            if constexpr (DT::kQ8) {
+                // widened INT8 chunk m of lane group j holds dims 64m + 16j .. +15: operand
+                // chunks 2m and 2m + 1 take q's dims 64m + 16j .. +7 and .. +15
 #pragma unroll
-            for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qp + kk * 4 * DT::kE * DT::kBytes);
+                for (int kk = 0; kk < NC; ++kk)
+                    q[kk] = load16(qrow + ((kk >> 1) * 64 + 16 * j + 8 * (kk & 1)) * TI::kBytes);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qrow + (kk * 4 * TI::kE + j * TI::kE) * TI::kBytes);
+            }
         }
         float m_run = kNegInf, l_run = 0.f;
         f32x4 acc[NACC];
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[a] = zero4();
-        NewRow<DT, D> nrow;
+        NewRow<TI, D> nrow;
         const int t_new = sp.L - 1;  // the token this step appended
-        if (FUSED) load_new_row<DT, D>(p, nrow, b, kvh, j, c);
+        if constexpr (FUSED) load_new_row<TI, D>(p, nrow, b, kvh, j, c);
 
         // score export: the run's logits are staged in LDS and stored in contiguous bursts
         int lg_n = 0, lg_u0 = u0;
@@ -297,24 +316,18 @@ void decode_stream_kernel(DecodeParams p) {
             lg_u0 += lg_n;
             lg_n = 0;
         };
-        auto process = [&](RingBuf<DT, D>& rb) __attribute__((always_inline)) {
-            if constexpr (SCORES) {
-                if ((lg_n + 1) * G * 16 > kLgFloats) flush();
-                if (rb.t0 < 0) {
-                    ++lg_n;
-                    return;
-                }
-            }
-            if (rb.t0 < 0) return;
-            if (FUSED && (unsigned)(t_new - rb.t0) < 16u) patch_tile<DT, D>(rb.k, rb.v, nrow, t_new - rb.t0, j, c);
+        // One unit: kt / vt are the MFMA operands (the ring buffer's own chunks, or for an
+        // INT8 cache their exact widening).
+        auto unit = [&](RingBuf<DT, D>& rb, u32x4 (&kt)[NC], u32x4 (&vt)[NC]) __attribute__((always_inline)) {
             f32x4 s = zero4();
-            T::qk(s, rb.k, q);
+            T::qk(s, kt, q);
             const unsigned keep = token_keep(sp, rb.t0, j);
             float x[4];
             float mx = kNegInf;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i] = (keep >> i) & 1 ? s[i] * qk_scale : kNegInf;
+                const float si = DT::kQ8 ? s[i] * rb.ks[i] : s[i];  // dequantised logit
+                x[i] = (keep >> i) & 1 ? si * qk_scale : kNegInf;
                 mx = fmaxf(mx, x[i]);
             }
             if constexpr (SCORES) {
@@ -332,9 +345,41 @@ void decode_stream_kernel(DecodeParams p) {
             l_run = l_run * alpha + ((pr.x + pr.y) + (pr.z + pr.w));
 #pragma unroll
             for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
-            if (!unit_full(sp, rb.t0)) T::mask_v(rb.v, keep);
-            T::pv(acc, rb.v, pr, upper);
+            if (!unit_full(sp, rb.t0)) T::mask_v(vt, keep);
+            if constexpr (DT::kQ8) {
+                // V's row scales enter through P (a masked token's scale is never multiplied)
+                f32x4 pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = (keep >> i) & 1 ? pr[i] * rb.vs[i] : 0.f;
+                T::pv(acc, vt, pv, upper);
+            } else {
+                T::pv(acc, vt, pr, upper);
+            }
             m_run = m_new;
+        };
+        auto process = [&](RingBuf<DT, D>& rb) __attribute__((always_inline)) {
+            if constexpr (SCORES) {
+                if ((lg_n + 1) * G * 16 > kLgFloats) flush();
+                if (rb.t0 < 0) {
+                    ++lg_n;
+                    return;
+                }
+            }
+            if (rb.t0 < 0) return;
+            if constexpr (DT::kQ8) {
+                u32x4 kt[NC], vt[NC];
+#pragma unroll
+                for (int m = 0; m < NCC; ++m) {
+                    widen_i8<TI>(rb.k[m], kt[2 * m], kt[2 * m + 1]);
+                    widen_i8<TI>(rb.v[m], vt[2 * m], vt[2 * m + 1]);
+                }
+                unit(rb, kt, vt);
+            } else {
+                if constexpr (FUSED) {
+                    if ((unsigned)(t_new - rb.t0) < 16u) patch_tile<TI, D>(rb.k, rb.v, nrow, t_new - rb.t0, j, c);
+                }
+                unit(rb, rb.k, rb.v);
+            }
         };
 
         for (int ub = 0; ub < cnt; ub += 64) {
@@ -353,22 +398,53 @@ void decode_stream_kernel(DecodeParams p) {
                     }
                 }
             }
-            RingBuf<DT, D> R0, R1, R2, R3;
-            ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
-            ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
-            ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
-            for (int k = 0; k < n; k += 4) {
-                ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
-                process(R0);
-                if (k + 1 >= n) break;
-                ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
-                process(R1);
-                if (k + 2 >= n) break;
-                ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
-                process(R2);
-                if (k + 3 >= n) break;
-                ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
-                process(R3);
+            // a ring of register buffers: unit k + depth - 1 is requested right before unit k
+            // is processed (depth 4 for 2/4-byte caches; 6 for INT8, whose units are half
+            // the bytes, so that a wave keeps as many bytes in flight)
+            if constexpr (!DT::kQ8) {
+                RingBuf<DT, D> R0, R1, R2, R3;
+                ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
+                for (int k = 0; k < n; k += 4) {
+                    ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
+                    process(R0);
+                    if (k + 1 >= n) break;
+                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
+                    process(R1);
+                    if (k + 2 >= n) break;
+                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
+                    process(R2);
+                    if (k + 3 >= n) break;
+                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
+                    process(R3);
+                }
+            } else {
+                RingBuf<DT, D> R0, R1, R2, R3, R4, R5;
+                ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R3, my_tok, my_off, 3, n, lane, u0 + ub);
+                ring_load<DT, D>(p, R4, my_tok, my_off, 4, n, lane, u0 + ub);
+                for (int k = 0; k < n; k += 6) {
+                    ring_load<DT, D>(p, R5, my_tok, my_off, k + 5, n, lane, u0 + ub);
+                    process(R0);
+                    if (k + 1 >= n) break;
+                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 6, n, lane, u0 + ub);
+                    process(R1);
+                    if (k + 2 >= n) break;
+                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 7, n, lane, u0 + ub);
+                    process(R2);
+                    if (k + 3 >= n) break;
+                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 8, n, lane, u0 + ub);
+                    process(R3);
+                    if (k + 4 >= n) break;
+                    ring_load<DT, D>(p, R3, my_tok, my_off, k + 9, n, lane, u0 + ub);
+                    process(R4);
+                    if (k + 5 >= n) break;
+                    ring_load<DT, D>(p, R4, my_tok, my_off, k + 10, n, lane, u0 + ub);
+                    process(R5);
+                }
             }
         }
 
@@ -670,7 +746,13 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
         if (e != hipSuccess) return e;
     }
     const dim3 grid(blocks), block(64 * kWaves);
-    if (scores) {
+    if constexpr (DT::kQ8) {
+        if (fused) return hipErrorInvalidValue;
+        if (scores)
+            decode_stream_kernel<DT, D, MODE, false, true><<<grid, block, 0, s>>>(p);
+        else
+            decode_stream_kernel<DT, D, MODE, false, false><<<grid, block, 0, s>>>(p);
+    } else if (scores) {
         if (fused)
             decode_stream_kernel<DT, D, MODE, true, true><<<grid, block, 0, s>>>(p);
         else
@@ -729,6 +811,8 @@ hipError_t launch_decode_stream(int dtype, int head_dim, int mode, bool fused, b
     switch (dtype) {
         case kF32: return launch_stream_d<F32>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
         case kF16: return launch_stream_d<F16>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
+        case kI8B: return launch_stream_d<I8B>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
+        case kI8H: return launch_stream_d<I8H>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
         default: return launch_stream_d<BF16>(head_dim, mode, fused, scores, p, s, ev_start, ev_stop);
     }
 }
@@ -738,9 +822,10 @@ static int occupancy_t() {
     int n = 0;
     // the least occupancy of the variants, so that every launch fits at once
     int m = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, true, false>, 64 * kWaves,
+    constexpr bool F = !DT::kQ8;  // the fused variants exist for the 16/32-bit caches
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, F, false>, 64 * kWaves,
                                                      0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_stream_kernel<DT, D, MODE, true, true>, 64 * kWaves,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_stream_kernel<DT, D, MODE, F, true>, 64 * kWaves,
                                                      0) != hipSuccess)
         return 1;
     n = m < n ? m : n;
@@ -761,6 +846,8 @@ int stream_blocks_per_cu(int dtype, int head_dim, int mode) {
     switch (dtype) {
         case kF32: return occupancy_d<F32>(head_dim, mode);
         case kF16: return occupancy_d<F16>(head_dim, mode);
+        case kI8B: return occupancy_d<I8B>(head_dim, mode);
+        case kI8H: return occupancy_d<I8H>(head_dim, mode);
         default: return occupancy_d<BF16>(head_dim, mode);
     }
 }
