@@ -115,6 +115,14 @@ class Oracle:
                                         _P, _I, _P, _P]
         L.oracle_quantise_rows.restype = _I
         L.oracle_quantise_rows.argtypes = [_P, _I, _I, _P, _P]
+        L.oracle_ring_pages.restype = _I
+        L.oracle_ring_pages.argtypes = [_I, _I]
+        L.oracle_ring_column.restype = _I64
+        L.oracle_ring_column.argtypes = [_I64, _I, _I, _I]
+        L.oracle_ring_expand.restype = _I
+        L.oracle_ring_expand.argtypes = [_P, _I, _I, _I, _I, _I, _I, _P]
+        L.oracle_policy_blocks.restype = _I64
+        L.oracle_policy_blocks.argtypes = [_I64, _I, _I, _I, _I]
         L.oracle_kv_cache_bytes.restype = ctypes.c_uint64
         L.oracle_kv_cache_bytes.argtypes = [_I64] * 7
         self.lib = L
@@ -144,6 +152,35 @@ class Oracle:
                                               _ptr(slots), slots.size), "kv_append")
         return kpool, vpool
 
+    def ring_pages(self, window, P) -> int:
+        return int(self.lib.oracle_ring_pages(int(window), int(P)))
+
+    def ring_column(self, page, *, sinks, P, ring_pages) -> int:
+        return int(self.lib.oracle_ring_column(int(page), int(sinks), int(P), int(ring_pages)))
+
+    def ring_expand(self, ring_table, *, sinks, P, ring_pages, pages):
+        """[B][cols] ring rows -> [B][pages] plain rows (logical page j in column j)."""
+        rt = _i32(ring_table)
+        B, cols = rt.shape
+        plain = np.full((B, pages), -1, np.int32)
+        self._check(self.lib.oracle_ring_expand(_ptr(rt), B, cols, int(sinks), int(P), int(ring_pages),
+                                                int(pages), _ptr(plain)), "ring_expand")
+        return plain
+
+    def policy_blocks(self, L, *, P, window, sinks=0, ring_pages=0) -> int:
+        n = int(self.lib.oracle_policy_blocks(int(L), int(P), int(window), int(sinks), int(ring_pages)))
+        if n < 0:
+            raise OracleError("policy_blocks: bad arguments")
+        return n
+
+    def _plain_table(self, block_table, context_lens, P, sinks, ring_pages):
+        """A ring table (ring_pages > 0) as the plain table that addresses the same blocks."""
+        if not ring_pages:
+            return block_table
+        cl = _i32(context_lens).reshape(-1)
+        pages = max(1, (int(cl.max(initial=0)) + P - 1) // P)
+        return self.ring_expand(block_table, sinks=sinks, P=P, ring_pages=ring_pages, pages=pages)
+
     def _common(self, dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list):
         kpool, vpool, q = _raw_pool(kpool, dtype), _raw_pool(vpool, dtype), _raw(q, dtype)
         bt = _i32(block_table)
@@ -157,8 +194,10 @@ class Oracle:
         return kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb
 
     def decode_attention(self, dtype, kpool, vpool, q, block_table, context_lens, *, P, Hkv, d,
-                         scale=0.0, window=0, sinks=0, page_list=None):
-        """Returns (out [B][Hq][d] float64, lse [B][Hq] float64)."""
+                         scale=0.0, window=0, sinks=0, page_list=None, ring_pages=0):
+        """Returns (out [B][Hq][d] float64, lse [B][Hq] float64). ring_pages > 0: block_table
+        is a window layer's ring table."""
+        block_table = self._plain_table(block_table, context_lens, P, sinks, ring_pages)
         kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
             dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list)
         out = np.zeros((B, Hq, d), np.float64)
@@ -170,9 +209,10 @@ class Oracle:
         return out, lse
 
     def decode_scores(self, dtype, kpool, q, block_table, context_lens, *, P, Hkv, d, stride,
-                      scale=0.0, window=0, sinks=0, page_list=None, score=None, block=1):
+                      scale=0.0, window=0, sinks=0, page_list=None, score=None, block=1, ring_pages=0):
         """Adds one step's scores into `score` ([B][Hkv][stride] float64, zeros when None) and
         returns it. block: tokens per score entry."""
+        block_table = self._plain_table(block_table, context_lens, P, sinks, ring_pages)
         kpool, _, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
             dtype, kpool, kpool, q, block_table, context_lens, P, Hkv, d, page_list)
         if score is None:
@@ -200,8 +240,9 @@ class Oracle:
 
     def decode_attention_split(self, dtype, kpool, vpool, q, block_table, context_lens, *, P,
                                Hkv, d, units, max_splits, scale=0.0, window=0, sinks=0,
-                               page_list=None):
+                               page_list=None, ring_pages=0):
         """Returns (o_part, m_part, l_part, out, lse), all float64."""
+        block_table = self._plain_table(block_table, context_lens, P, sinks, ring_pages)
         kpool, vpool, q, bt, cl, B, Hq, mb, pl, pps, nb = self._common(
             dtype, kpool, vpool, q, block_table, context_lens, P, Hkv, d, page_list)
         o_part = np.zeros((B, Hq, max_splits, d), np.float64)
@@ -299,3 +340,19 @@ def quantise_rows(*a, **k):
 
 def kv_cache_bytes(*a, **k):
     return default().kv_cache_bytes(*a, **k)
+
+
+def ring_pages(*a, **k):
+    return default().ring_pages(*a, **k)
+
+
+def ring_column(*a, **k):
+    return default().ring_column(*a, **k)
+
+
+def ring_expand(*a, **k):
+    return default().ring_expand(*a, **k)
+
+
+def policy_blocks(*a, **k):
+    return default().policy_blocks(*a, **k)

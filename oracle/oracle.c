@@ -33,6 +33,10 @@
  *   - L == 0 gives out = 0 and lse = -inf;
  *   - a token's score sums the softmax probabilities of the query heads that share its
  *     kv head (the cache is per kv head), one query per head per decode step.
+ *   - INT8 rows are quantised symmetrically, one fp32 scale per (token, kv head) row;
+ *   - a window layer's block table is a ring of ceil(S/P) sink columns plus R columns, R the
+ *     most pages W consecutive tokens touch, so a block is reused only when none of its
+ *     tokens is attended.
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms,
  * invariants, brute force, the primer's worked KV-size values); none is unpinned.
@@ -599,6 +603,70 @@ int oracle_bruteforce(int dt, const void* K_log, const void* V_log, int Lmax,
     free(idx);
     free(lg);
     return ORC_OK;
+}
+
+/* Per-layer memory policy ([Novita] §關鍵技術 1: each layer takes either a full cache or
+ * a sliding window over the one paged memory, so window layers need fewer blocks;
+ * [primer] §4.3: a window layer keeps only the last W tokens). A window layer attends to
+ * the sinks [0, S) and the window [L-W, L) (the reading attention uses). Its block-table
+ * row is a ring: the first ceil(S / P) columns hold the sink pages for good, and logical
+ * page j past them lives in column sink_pages + (j - sink_pages) mod R, so the block of a
+ * page is written over by the page R later. That is safe as long as no two pages that
+ * can be attended together share a column: R at least the number of pages that W
+ * consecutive tokens can touch. */
+
+static int64_t ring_sink_pages(int sinks, int P) { return sinks > 0 ? ((int64_t)sinks + P - 1) / P : 0; }
+
+/* The most pages W consecutive tokens touch: over the first token's offset o within its
+ * page, the pages covering offsets [o, o + W). 0 for W <= 0. */
+int oracle_ring_pages(int window, int P) {
+    if (window <= 0 || P <= 0) return 0;
+    int most = 0;
+    for (int o = 0; o < P; ++o) {
+        int touched = (o + window + P - 1) / P;
+        if (touched > most) most = touched;
+    }
+    return most;
+}
+
+/* Column of logical page j in a ring row. */
+int64_t oracle_ring_column(int64_t page, int sinks, int P, int ring_pages) {
+    int64_t sp = ring_sink_pages(sinks, P);
+    if (page < sp) return page;
+    return sp + (page - sp) % ring_pages;
+}
+
+/* Plain rows from ring rows: plain[b][j] = ring[b][column(j)] for j < pages, so that
+ * block_table[b][t / P] addressing reads what the ring addressing reads. ring: [B][cols];
+ * plain: [B][pages]. */
+int oracle_ring_expand(const int32_t* ring, int B, int cols, int sinks, int P, int ring_pages,
+                       int pages, int32_t* plain) {
+    if (B < 0 || cols < 0 || sinks < 0 || P <= 0 || ring_pages <= 0 || pages < 0) return ORC_ERR_ARG;
+    if (ring_sink_pages(sinks, P) + ring_pages > cols) return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < pages; ++j)
+            plain[(size_t)b * pages + j] = ring[(size_t)b * cols + oracle_ring_column(j, sinks, P, ring_pages)];
+    return ORC_OK;
+}
+
+/* Blocks one sequence of L tokens holds in a layer: the distinct table columns its pages
+ * [0, ceil(L / P)) use. window <= 0: a full layer (one block per page); otherwise the
+ * ring above with R = ring_pages (0: the least safe R). -1 on bad arguments. */
+int64_t oracle_policy_blocks(int64_t L, int P, int window, int sinks, int ring_pages) {
+    if (L < 0 || P <= 0 || sinks < 0) return -1;
+    int64_t pages = (L + P - 1) / P;
+    if (window <= 0) return pages;
+    if (ring_pages <= 0) ring_pages = oracle_ring_pages(window, P);
+    int64_t cols = ring_sink_pages(sinks, P) + ring_pages;
+    char* used = (char*)calloc((size_t)cols, 1);
+    if (!used) return -1;
+    int64_t n = 0;
+    for (int64_t j = 0; j < pages; ++j) {
+        int64_t c = oracle_ring_column(j, sinks, P, ring_pages);
+        if (!used[c]) { used[c] = 1; ++n; }
+    }
+    free(used);
+    return n;
 }
 
 /* KV-cache size ([primer] §3.1): 2 (K and V) x batch x layers x heads x head_dim

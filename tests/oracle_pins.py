@@ -510,6 +510,111 @@ def pin_int8_attention(o):
         assert np.abs(s8 - s32).max() <= 1e-12, kw
 
 
+def pin_ring_golden(o):
+    """Ring sizes, ring columns and blocks held, worked out by hand in
+    tests/golden/ring_policy.json; pool bytes against the primer's KV formula."""
+    with open(os.path.join(GOLDEN, "ring_policy.json")) as f:
+        g = json.load(f)
+    for c in g["ring_pages"]:
+        assert o.ring_pages(c["W"], c["P"]) == c["R"], c["what"]
+    for c in g["columns"]:
+        got = [o.ring_column(j, sinks=c["S"], P=c["P"], ring_pages=c["R"]) for j in c["pages"]]
+        assert got == c["cols"], (c["what"], got)
+    for c in g["blocks"]:
+        assert o.policy_blocks(c["L"], P=c["P"], window=c["W"], sinks=c["S"]) == c["n"], c["what"]
+    for c in g["bytes"]:
+        n = o.policy_blocks(c["L"], P=c["P"], window=c["W"], sinks=c["S"])
+        assert n * c["P"] * 2 * c["Hkv"] * c["d"] * c["es"] == c["bytes"], c["what"]
+        if c["W"] <= 0:
+            assert o.kv_cache_bytes(1, 1, c["Hkv"], c["d"], c["L"], c["es"], c["P"]) == c["bytes"], c["what"]
+
+
+def pin_ring_pages_bruteforce(o):
+    """The ring size is the most pages any W consecutive tokens touch (enumerated over window
+    positions), and the blocks a sequence holds follow min(ceil(L/P), ceil(S/P) + R)."""
+    for P in (16, 32):
+        for W in range(1, 3 * P + 3):
+            most = max(len({t // P for t in range(L - W, L)}) for L in range(W, W + 2 * P + 1))
+            assert o.ring_pages(W, P) == most, (W, P)
+    rng = np.random.default_rng(77)
+    for _ in range(300):
+        P = int(rng.choice([16, 32, 64]))
+        W = int(rng.integers(0, 700))
+        S = int(rng.integers(0, 70))
+        L = int(rng.integers(0, 5000))
+        R = 0 if W <= 0 else o.ring_pages(W, P) + int(rng.integers(0, 3))
+        pages = -(-L // P)
+        want = pages if W <= 0 else min(pages, -(-S // P) + R)
+        assert o.policy_blocks(L, P=P, window=W, sinks=S, ring_pages=R) == want, (L, P, W, S, R)
+
+
+def _ring_problem(o, seed, *, B, Hq, Hkv, d, dtype, P, lens, W, S, R):
+    """A window layer over a ring table: every token of every sequence appended in order
+    through the ring (later pages write over the blocks of dead ones), into NaN pools holding
+    only ceil(S/P) + R blocks per sequence."""
+    Lmax = max(lens + [1])
+    q = synth.normal((B, Hq, d), seed, "q", dtype=dtype)
+    K = synth.normal((B, Lmax, Hkv, d), seed, "k", dtype=dtype)
+    V = synth.normal((B, Lmax, Hkv, d), seed, "v", dtype=dtype)
+    cols = -(-S // P) + R
+    ring, nb = synth.block_tables([cols * P] * B, P, seed, spare_blocks=1)
+    plain = o.ring_expand(ring.numpy(), sinks=S, P=P, ring_pages=R, pages=max(1, -(-Lmax // P)))
+    n_el = nb * Hkv * P * d
+    kpool = np.full(n_el, NAN_BITS[dtype], dtype=_raw_dtype(dtype))
+    vpool = np.full(n_el, NAN_BITS[dtype], dtype=_raw_dtype(dtype))
+    slots = synth.token_slots(torch.from_numpy(plain), lens, P)
+    k_new = torch.cat([K[b, :L] for b, L in enumerate(lens)])
+    v_new = torch.cat([V[b, :L] for b, L in enumerate(lens)])
+    o.kv_append(dtype, kpool, vpool, synth.raw_numpy(k_new), synth.raw_numpy(v_new), slots.numpy(), P=P,
+                Hkv=Hkv, d=d)
+    return SimpleNamespace(q=q, K=K, V=V, bt=ring, nb=nb, lens=lens, kpool=kpool, vpool=vpool, P=P, Hkv=Hkv,
+                           Hq=Hq, d=d, dtype=dtype, B=B)
+
+
+def pin_ring_attention(o):
+    """Attention of a window layer through its ring table equals the brute force on the
+    contiguous logical rows, over lengths that wrap the ring several times. A ring slot is
+    shared by tokens R*P apart, so a ring of R pages with R*P < W drops window tokens: some
+    result must then differ."""
+    cases = [(16, 23, 0), (16, 23, 3), (16, 40, 16), (16, 16, 20), (32, 33, 5), (16, 1, 0), (16, 1, 2)]
+    for i, (P, W, S) in enumerate(cases):
+        Rmin = o.ring_pages(W, P)
+        lens = [1, W, W + 1, 5 * P + 7, 11 * P, 9 * P + 1, 13 * P - 1]
+        for R, must_match in ((Rmin, True), (Rmin + 2, True), (-(-W // P) - 1, False)):
+            if R <= 0:
+                continue
+            pr = _ring_problem(o, 600 + i, B=len(lens), Hq=2, Hkv=1, d=64, dtype="bf16", P=P, lens=lens, W=W,
+                               S=S, R=R)
+            out, lse = attend(o, pr, window=W, sinks=S, ring_pages=R)
+            bo, bl = brute(o, pr, window=W, sinks=S)
+            same = (np.abs(out - bo.astype(np.float64)).max() <= TOL and
+                    np.abs(lse - bl.astype(np.float64)).max() <= TOL)
+            assert same == must_match, (P, W, S, R)
+
+
+def pin_ring_reuse(o):
+    """With the least ring size, a block is taken over by a new page only when none of its
+    tokens is attended any more (the block lies wholly outside sinks and window); one page
+    fewer breaks that. Checked by walking a sequence token by token."""
+    def reuse_ok(P, W, S, R, Lmax):
+        owner = {}  # column -> logical page it holds
+        for L in range(1, Lmax + 1):
+            j = (L - 1) // P
+            c = o.ring_column(j, sinks=S, P=P, ring_pages=R)
+            old = owner.get(c)
+            if old is not None and old != j:
+                live = [t for t in range(old * P, old * P + P) if t < S or t >= L - W]
+                if live:
+                    return False
+            owner[c] = j
+        return True
+
+    for P, W, S in ((16, 23, 0), (16, 23, 3), (16, 32, 0), (16, 40, 16), (32, 33, 5), (16, 17, 0), (16, 64, 4)):
+        R = o.ring_pages(W, P)
+        assert reuse_ok(P, W, S, R, 14 * P + 5), (P, W, S)
+        assert not reuse_ok(P, W, S, R - 1, 14 * P + 5), (P, W, S)
+
+
 def pin_empty(o):
     pr = build(o, 14, B=2, Hq=2, Hkv=1, d=64, dtype="f16", P=16, lens=[0, 3])
     out, lse = attend(o, pr)
@@ -520,7 +625,8 @@ PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundt
         pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
         pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
         pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_scores_block, pin_select_pages,
-        pin_int8_quantise, pin_int8_attention, pin_empty]
+        pin_int8_quantise, pin_int8_attention, pin_ring_golden, pin_ring_pages_bruteforce,
+        pin_ring_attention, pin_ring_reuse, pin_empty]
 
 
 if __name__ == "__main__":

@@ -49,6 +49,12 @@ MUTATIONS = [
     ("int8 scale per tile, not per row", "memcpy(&sc, (const char*)pool + plane + (((size_t)blk * Hkv + h) * P + t) * 4, 4);",
      "memcpy(&sc, (const char*)pool + plane + (((size_t)blk * Hkv + h) * P) * 4, 4);"),
     ("int8 amax from the first element", "if (a > amax) amax = a;", "if (i == 0) amax = a;"),
+    ("ring size ignores the page offset", "int touched = (o + window + P - 1) / P;",
+     "int touched = (window + P - 1) / P;"),
+    ("ring column drops the sink offset", "return sp + (page - sp) % ring_pages;",
+     "return (page - sp) % ring_pages;"),
+    ("sink pages rounded down", "return sinks > 0 ? ((int64_t)sinks + P - 1) / P : 0;", "return sinks / P;"),
+    ("window blocks counted per page", "if (!used[c]) { used[c] = 1; ++n; }", "{ used[c] = 1; ++n; }"),
 ]
 
 
