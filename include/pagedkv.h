@@ -77,7 +77,8 @@ typedef enum {
     PKV_ERR_UNSUPPORTED = 3, /* dtype / head_dim / block_size / group size not built */
     PKV_ERR_MODE = 4,        /* window and page_list both set, or a bad sparsity field */
     PKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
-    PKV_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+    PKV_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
+    PKV_ERR_NO_BLOCKS = 7    /* block manager: a pool has too few free blocks (nothing changed) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
@@ -135,7 +136,19 @@ typedef struct {
  * PKV_ERR_SHAPE). Score export always uses the work-split path; it needs split_tokens == 0
  * (else PKV_ERR_MODE) and is not available to paged_decode_attention_partial
  * (PKV_ERR_MODE). Every entry's update is made by one thread, in a fixed order: results do
- * not depend on timing. */
+ * not depend on timing.
+ *
+ * Ring block tables ([Novita] §關鍵技術 1: a layer may keep a sliding window instead of the
+ * full cache, and then needs fewer blocks; [primer] §4.3). With ring_pages = R > 0 (only
+ * together with window > 0, else PKV_ERR_MODE) row b of block_table is a ring: with
+ * sink_pages = ceil(num_sinks / P), logical page j is read from column j when
+ * j < sink_pages and from column sink_pages + (j - sink_pages) mod R otherwise, so the
+ * block of page j is reused by page j + R. R must be at least pkv_ring_pages(window, P),
+ * the most pages `window` consecutive tokens touch (else PKV_ERR_MODE): then a block is
+ * only reused once none of its tokens is attended, and the attended tokens are exactly
+ * those of the window mode. max_blocks_per_seq (the row width) must be at least
+ * sink_pages + R (else PKV_ERR_SHAPE) and no longer limits the context length. The slots
+ * of appended tokens follow the same columns (pkv_bm_append computes them). */
 typedef struct {
     int32_t window;          /* <= 0: no window */
     int32_t num_sinks;       /* >= 0 */
@@ -149,6 +162,7 @@ typedef struct {
     float* score_acc;        /* nullable: score export, see above (device) */
     int32_t score_stride;    /* row length of score_acc */
     int32_t score_block;     /* tokens per score entry; 0 or 1: one entry per token */
+    int32_t ring_pages;      /* 0: plain block table; > 0: ring table of this many pages (above) */
 } pkv_decode_opts;
 
 /* kv_cache_append — decode-step cache write ([primer] §2.2; [naive] §"KV cache的思想";
@@ -322,6 +336,86 @@ pkv_status paged_decode_combine(const float* o_part, const float* m_part, const 
 pkv_status paged_select_pages(const float* scores, int32_t heads, int32_t stride,
                               const int32_t* context_lens, int32_t batch, int32_t block_size,
                               int32_t k, int32_t recent, int32_t* page_list, void* stream);
+
+/* ---- Per-layer memory policy (host) ---------------------------------------------------
+ * [Novita] §關鍵技術 1: every layer takes either a full cache or a sliding window over the
+ * one paged memory, with its own block-table strategy, and window layers hold fewer blocks.
+ * Layers with the same policy form a group: they share one block table and one slot mapping
+ * per step (token positions are the same on every layer) and each has its own pools of the
+ * group's num_blocks blocks ([naive] §"KV cache的思想": one write position per step serves
+ * all layers). A full group gives a sequence one block per page ([primer] §4.1); a window
+ * group keeps ceil(S / P) sink blocks plus a ring of R blocks, reused as the window moves.
+ * The manager is host code: it hands out block ids and slots; the caller copies tables and
+ * slots to the device. It is not thread-safe; calls on one manager must not overlap. */
+
+/* The least ring size for a window of `window` tokens: the most pages that many consecutive
+ * tokens touch, floor((window + 2 * block_size - 2) / block_size); 0 when window <= 0 or
+ * block_size <= 0. */
+int32_t pkv_ring_pages(int32_t window, int32_t block_size);
+
+/* Blocks a sequence of context_len tokens holds in one layer: ceil(L / P) for a full layer
+ * (window <= 0); min(ceil(L / P), ceil(S / P) + R) for a window layer, R = ring_pages or,
+ * when ring_pages is 0, pkv_ring_pages(window, P). -1 on bad arguments. Times
+ * 2 x kv_heads x head_dim x P x element bytes it is the layer's share of the [primer] §3.1
+ * KV size. */
+int64_t pkv_policy_blocks(int64_t context_len, int32_t block_size, int32_t window, int32_t num_sinks,
+                          int32_t ring_pages);
+
+typedef struct pkv_block_manager pkv_block_manager;
+
+typedef struct {
+    int32_t window;     /* <= 0: full cache; > 0: sliding window of this many tokens (ring table) */
+    int32_t num_sinks;  /* window > 0: the first num_sinks tokens are kept as well (>= 0) */
+    int32_t ring_pages; /* window > 0: ring size R; 0 selects pkv_ring_pages(window, block_size) */
+    int32_t num_blocks; /* blocks in each pool of the group's layers (ids 0 .. num_blocks - 1) */
+} pkv_layer_group;
+
+/* Creates a manager for sequences 0 .. max_seqs - 1 (all empty) over num_groups groups.
+ * block_size: a multiple of 16 in [16, 256]. max_pages_per_seq: the row width of a full
+ * group's table, so its longest sequence is max_pages_per_seq * block_size tokens.
+ * Errors: PKV_ERR_NULL (groups or out NULL), PKV_ERR_SHAPE (non-positive sizes, negative
+ * sinks or blocks), PKV_ERR_MODE (ring_pages below the least size), PKV_ERR_UNSUPPORTED
+ * (block_size, or num_blocks * block_size beyond int32). *out is set only on success. */
+pkv_status pkv_bm_create(int32_t block_size, int32_t max_seqs, int32_t max_pages_per_seq,
+                         const pkv_layer_group* groups /* host [num_groups] */, int32_t num_groups,
+                         pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Row width of group g's block table: max_pages_per_seq for a full group, sink pages + R for a
+ * window group (the max_blocks_per_seq to pass with it; a window group's row goes with
+ * opts.ring_pages = pkv_bm_ring_pages). 0 for a bad group. */
+int32_t pkv_bm_table_cols(const pkv_block_manager* bm, int32_t group);
+/* R of a window group; 0 for a full group or a bad group. */
+int32_t pkv_bm_ring_pages(const pkv_block_manager* bm, int32_t group);
+
+/* Appends num_new[i] tokens to sequence seq_ids[i], i < n (num_new NULL: one token each, a
+ * decode step). Blocks are taken from each group's free list as pages are first reached
+ * (every page of a full group; every column of a window group's ring, after which blocks are
+ * reused). Writes, for group g and the k-th new token in call order (sequence by sequence,
+ * positions ascending), slots[g * T + k] = block * block_size + position % block_size, with
+ * T = the total of num_new; a window group writes -1 instead for a token that is neither a
+ * sink nor among the last `window` tokens once all of the call's tokens are in, so that no
+ * two tokens of one call share a slot. context_lens (nullable, [n]) receives the new lengths.
+ * All or nothing: PKV_ERR_SHAPE (seq id out of range or repeated, negative count, a full
+ * group's row or int32 length exceeded) and PKV_ERR_NO_BLOCKS change nothing. */
+pkv_status pkv_bm_append(pkv_block_manager* bm, const int32_t* seq_ids /* host [n] */,
+                         const int32_t* num_new /* host [n], nullable */, int32_t n,
+                         int32_t* slots /* host [num_groups][T] */,
+                         int32_t* context_lens /* host [n], nullable */);
+
+/* Returns every block of sequence seq_id to the free lists and sets its length to 0. */
+pkv_status pkv_bm_release(pkv_block_manager* bm, int32_t seq_id);
+
+/* Copies the rows of seq_ids[0 .. n-1] of group g's table into table ([n][cols], host).
+ * Columns not yet given a block hold -1 (attention never reads them). */
+pkv_status pkv_bm_block_tables(const pkv_block_manager* bm, int32_t group, const int32_t* seq_ids, int32_t n,
+                               int32_t* table);
+
+/* Context length of a sequence; -1 for a bad id. */
+int64_t pkv_bm_context_len(const pkv_block_manager* bm, int32_t seq_id);
+/* Blocks of group g held by all sequences (the sum of pkv_policy_blocks over them); -1 for
+ * a bad group. */
+int64_t pkv_bm_blocks_in_use(const pkv_block_manager* bm, int32_t group);
 
 /* KV-cache size in bytes by the formula of [primer] §3.1,
  *   2 x batch x layers x kv_heads x head_dim x seq_len x dtype_bytes,

@@ -15,13 +15,14 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 __all__ = [
     "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
-    "select_pages", "new_cache",
+    "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -48,7 +49,12 @@ class CacheDesc(ctypes.Structure):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("window", _i32), ("num_sinks", _i32), ("page_list", _vp),
                 ("pages_per_seq", _i32), ("split_tokens", _i32), ("timing_start", _vp),
-                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32), ("score_block", _i32)]
+                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32), ("score_block", _i32),
+                ("ring_pages", _i32)]
+
+
+class LayerGroup(ctypes.Structure):
+    _fields_ = [("window", _i32), ("num_sinks", _i32), ("ring_pages", _i32), ("num_blocks", _i32)]
 
 
 _P_DESC = ctypes.POINTER(CacheDesc)
@@ -76,6 +82,28 @@ _lib.paged_select_pages.restype = ctypes.c_int
 _lib.paged_select_pages.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
 _lib.pkv_kv_cache_bytes.restype = ctypes.c_uint64
 _lib.pkv_kv_cache_bytes.argtypes = [_i64] * 7
+_lib.pkv_ring_pages.restype = _i32
+_lib.pkv_ring_pages.argtypes = [_i32, _i32]
+_lib.pkv_policy_blocks.restype = _i64
+_lib.pkv_policy_blocks.argtypes = [_i64, _i32, _i32, _i32, _i32]
+_lib.pkv_bm_create.restype = ctypes.c_int
+_lib.pkv_bm_create.argtypes = [_i32, _i32, _i32, ctypes.POINTER(LayerGroup), _i32, ctypes.POINTER(_vp)]
+_lib.pkv_bm_destroy.restype = None
+_lib.pkv_bm_destroy.argtypes = [_vp]
+_lib.pkv_bm_table_cols.restype = _i32
+_lib.pkv_bm_table_cols.argtypes = [_vp, _i32]
+_lib.pkv_bm_ring_pages.restype = _i32
+_lib.pkv_bm_ring_pages.argtypes = [_vp, _i32]
+_lib.pkv_bm_append.restype = ctypes.c_int
+_lib.pkv_bm_append.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp]
+_lib.pkv_bm_release.restype = ctypes.c_int
+_lib.pkv_bm_release.argtypes = [_vp, _i32]
+_lib.pkv_bm_block_tables.restype = ctypes.c_int
+_lib.pkv_bm_block_tables.argtypes = [_vp, _i32, _vp, _i32, _vp]
+_lib.pkv_bm_context_len.restype = _i64
+_lib.pkv_bm_context_len.argtypes = [_vp, _i32]
+_lib.pkv_bm_blocks_in_use.restype = _i64
+_lib.pkv_bm_blocks_in_use.argtypes = [_vp, _i32]
 _lib.pkv_status_string.restype = ctypes.c_char_p
 _lib.pkv_status_string.argtypes = [ctypes.c_int]
 
@@ -145,9 +173,9 @@ def new_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int
 
 
 def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None,
-          score_block=1) -> DecodeOpts:
+          score_block=1, ring_pages=0) -> DecodeOpts:
     o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None, None, 0,
-                   int(score_block))
+                   int(score_block), int(ring_pages))
     if timing is not None:
         o.timing_start, o.timing_stop = int(timing[0]), int(timing[1])
     if page_list is not None:
@@ -175,10 +203,10 @@ def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
 
 
 def workspace_size(k_cache, batch: int, num_q_heads: int, max_context_len: int, *, window=0,
-                   num_sinks=0, page_list=None, split_tokens=0, scores=False) -> int:
+                   num_sinks=0, page_list=None, split_tokens=0, scores=False, ring_pages=0) -> int:
     """scores: True (or the score tensor) when the calls export scores."""
     desc = cache_desc(k_cache)
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens))
+    o = _opts(window, num_sinks, None, split_tokens, ring_pages=ring_pages)
     if page_list is not None:
         o.page_list = ctypes.c_void_p(1)  # only its presence matters to the size
         o.pages_per_seq = page_list.shape[1]
@@ -189,9 +217,9 @@ def workspace_size(k_cache, batch: int, num_q_heads: int, max_context_len: int, 
 
 
 def num_splits(k_cache, batch: int, max_context_len: int, *, window=0, num_sinks=0, page_list=None,
-               split_tokens: int = 0) -> int:
+               split_tokens: int = 0, ring_pages: int = 0) -> int:
     desc = cache_desc(k_cache)
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens))
+    o = _opts(window, num_sinks, None, split_tokens, ring_pages=ring_pages)
     if page_list is not None:
         o.page_list = ctypes.c_void_p(1)
         o.pages_per_seq = page_list.shape[1]
@@ -202,8 +230,12 @@ def num_splits(k_cache, batch: int, max_context_len: int, *, window=0, num_sinks
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, max_context_len: int,
                            scale: float = 0.0, window: int = 0, num_sinks: int = 0, page_list=None,
                            split_tokens: int = 0, out=None, out_dtype=None, lse=None, workspace=None,
-                           want_lse: bool = True, timing=None, scores=None, score_block: int = 1):
+                           want_lse: bool = True, timing=None, scores=None, score_block: int = 1,
+                           ring_pages: int = 0):
     """One decode query per sequence over its paged cache. Returns (out, lse).
+
+    ring_pages > 0: block_table holds a window layer's ring rows (BlockManager.block_table of a
+    window group, with window/num_sinks of that group).
 
     timing: optional pair of raw hipEvent_t handles recorded around the main kernel.
     scores: optional [B, Hkv, stride] float32 tensor; every attended token's softmax
@@ -215,7 +247,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block, ring_pages)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
@@ -236,7 +268,7 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
                                   window: int = 0, num_sinks: int = 0, page_list=None,
                                   split_tokens: int = 0, out=None, out_dtype=None, lse=None,
                                   workspace=None, want_lse: bool = True, timing=None, scores=None,
-                                  score_block: int = 1):
+                                  score_block: int = 1, ring_pages: int = 0):
     """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
     slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
     scores: as in paged_decode_attention."""
@@ -246,7 +278,7 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block)
+    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block, ring_pages)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
@@ -269,11 +301,11 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
 def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_lens, *,
                                    max_context_len: int, split_tokens: int = 0, scale: float = 0.0,
                                    window: int = 0, num_sinks: int = 0, page_list=None,
-                                   o_part=None, m_part=None, l_part=None):
+                                   o_part=None, m_part=None, l_part=None, ring_pages: int = 0):
     """Split-K partials (o [B,Hq,S,d], m [B,Hq,S], l [B,Hq,S], fp32) over explicit partitions."""
     desc = cache_desc(k_cache, q.dtype)
     B, Hq, d = q.shape
-    o = _opts(window, num_sinks, page_list, split_tokens)
+    o = _opts(window, num_sinks, page_list, split_tokens, ring_pages=ring_pages)
     S = int(_lib.paged_decode_attention_num_splits(ctypes.byref(desc), B, max_context_len, ctypes.byref(o)))
     if S <= 0:
         raise ValueError("invalid partition request")
@@ -318,6 +350,96 @@ def select_pages(scores, context_lens, *, block_size: int, k: int, recent: int =
         _dev(scores, "scores", torch.float32), H, stride, _dev(context_lens, "context_lens", torch.int32), B,
         int(block_size), int(k), int(recent), _dev(page_list, "page_list", torch.int32), _stream(scores)))
     return page_list
+
+
+def ring_pages(window: int, block_size: int) -> int:
+    """Least ring size of a window layer: the most pages `window` consecutive tokens touch."""
+    return int(_lib.pkv_ring_pages(int(window), int(block_size)))
+
+
+def policy_blocks(context_len: int, block_size: int, window: int = 0, num_sinks: int = 0,
+                  ring_pages: int = 0) -> int:
+    """Blocks one sequence holds in one layer under its policy (full: one per page)."""
+    n = int(_lib.pkv_policy_blocks(int(context_len), int(block_size), int(window), int(num_sinks),
+                                   int(ring_pages)))
+    if n < 0:
+        raise ValueError("policy_blocks: bad arguments")
+    return n
+
+
+def _host_i32(a, name):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if a.ndim != 1:
+        raise ValueError(f"{name} must be one-dimensional")
+    return a
+
+
+class BlockManager:
+    """Host block manager of the per-layer memory policy (pkv_bm_* in libpagedkv): per group of
+    layers sharing a policy, a free list of block ids and one block-table row per sequence
+    (a ring for window groups). groups: dicts with window (0: full cache), num_sinks, ring_pages
+    (0: the least size) and num_blocks."""
+
+    def __init__(self, block_size: int, max_seqs: int, max_pages_per_seq: int, groups):
+        arr = (LayerGroup * len(groups))()
+        for i, g in enumerate(groups):
+            arr[i] = LayerGroup(int(g.get("window", 0)), int(g.get("num_sinks", 0)), int(g.get("ring_pages", 0)),
+                                int(g["num_blocks"]))
+        h = _vp()
+        _check("pkv_bm_create", _lib.pkv_bm_create(int(block_size), int(max_seqs), int(max_pages_per_seq), arr,
+                                                   len(groups), ctypes.byref(h)))
+        self._h = h
+        self.block_size = int(block_size)
+        self.num_groups = len(groups)
+
+    def close(self, _destroy=_lib.pkv_bm_destroy) -> None:
+        # the destroy function is bound at definition time: __del__ may run at interpreter exit
+        if getattr(self, "_h", None):
+            _destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def table_cols(self, group: int) -> int:
+        return int(_lib.pkv_bm_table_cols(self._h, int(group)))
+
+    def ring_pages(self, group: int) -> int:
+        return int(_lib.pkv_bm_ring_pages(self._h, int(group)))
+
+    def append(self, seq_ids, num_new=None):
+        """Adds num_new[i] tokens (default 1) to sequence seq_ids[i]. Returns (slots
+        [num_groups, T] int32 — -1 for a window group's tokens already out of its window —, new
+        context lengths [n] int32), numpy arrays."""
+        ids = _host_i32(seq_ids, "seq_ids")
+        cnt = None if num_new is None else _host_i32(num_new, "num_new")
+        if cnt is not None and cnt.size != ids.size:
+            raise ValueError("num_new must match seq_ids")
+        T = ids.size if cnt is None else int(cnt.astype(np.int64).sum())
+        slots = np.empty((self.num_groups, max(T, 0)), np.int32)
+        lens = np.empty(ids.size, np.int32)
+        _check("pkv_bm_append", _lib.pkv_bm_append(
+            self._h, ids.ctypes.data if ids.size else None, None if cnt is None else cnt.ctypes.data, ids.size,
+            slots.ctypes.data if slots.size else None, lens.ctypes.data if lens.size else None))
+        return slots, lens
+
+    def release(self, seq_id: int) -> None:
+        _check("pkv_bm_release", _lib.pkv_bm_release(self._h, int(seq_id)))
+
+    def block_table(self, group: int, seq_ids):
+        """[n, table_cols(group)] int32 numpy rows (-1 where no block is held)."""
+        ids = _host_i32(seq_ids, "seq_ids")
+        out = np.empty((ids.size, self.table_cols(group)), np.int32)
+        _check("pkv_bm_block_tables", _lib.pkv_bm_block_tables(
+            self._h, int(group), ids.ctypes.data if ids.size else None, ids.size,
+            out.ctypes.data if out.size else None))
+        return out
+
+    def context_len(self, seq_id: int) -> int:
+        return int(_lib.pkv_bm_context_len(self._h, int(seq_id)))
+
+    def blocks_in_use(self, group: int) -> int:
+        return int(_lib.pkv_bm_blocks_in_use(self._h, int(group)))
 
 
 def kv_cache_bytes(batch, layers, kv_heads, head_dim, seq_len, dtype_bytes, block_size=0) -> int:

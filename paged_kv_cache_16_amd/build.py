@@ -17,6 +17,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["append.hip", "decode.hip", "stream.hip", "select.hip", "api.hip"]
+HOST_SOURCES = ["blocks.cpp"]  # host-only C++ (the block manager), built with the host compiler
+CXX = os.environ.get("CXX", "g++")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     # packed-fp32 VALU forms are kept out of the generated code
@@ -33,10 +35,20 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _compile_host(src: str) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, "-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{CXX} failed for {src}:\n{r.stderr}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        jobs = [ex.submit(_compile, s) for s in SOURCES] + [ex.submit(_compile_host, s) for s in HOST_SOURCES]
+        objs = [j.result() for j in jobs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -105,9 +105,12 @@ int device_occupancy(int dev, int dtype, int head_dim, int mode) {
     return n;
 }
 
+int ring_sink_pages(int sinks, int block_size) { return (int)(((long long)sinks + block_size - 1) / block_size); }
+
 pkv_status check_opts(const pkv_decode_opts* o) {
     if (!o) return PKV_OK;
     if (o->num_sinks < 0 || o->split_tokens < 0) return PKV_ERR_MODE;
+    if (o->ring_pages < 0 || (o->ring_pages > 0 && o->window <= 0)) return PKV_ERR_MODE;
     if (o->page_list && o->window > 0) return PKV_ERR_MODE;
     if (o->page_list && o->pages_per_seq <= 0) return PKV_ERR_MODE;
     if (o->score_acc && o->split_tokens > 0) return PKV_ERR_MODE;
@@ -122,7 +125,9 @@ Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_
     pl.q8 = d->dtype == PKV_I8;
     const int P = d->block_size;
     long long cap = max_context_len;
-    if (max_blocks >= 0 && (long long)max_blocks * P < cap) cap = (long long)max_blocks * P;
+    // a ring table addresses any length through its columns
+    const bool ring = o && o->ring_pages > 0;
+    if (!ring && max_blocks >= 0 && (long long)max_blocks * P < cap) cap = (long long)max_blocks * P;
     if (cap < 0) cap = 0;
     pl.len_cap = (int)cap;
     const int full_units = (int)((cap + 15) / 16);
@@ -207,6 +212,10 @@ pkv_status check_decode_args(const pkv_cache_desc* d, const void* k, const void*
     if (st != PKV_OK) return st;
     if (batch > 0 && (!k || !v || !q || !bt || !cl)) return PKV_ERR_NULL;
     if (batch > 0 && max_blocks == 0) return PKV_ERR_SHAPE;
+    if (o && o->ring_pages > 0) {
+        if (o->ring_pages < pkv_ring_pages(o->window, d->block_size)) return PKV_ERR_MODE;
+        if ((long long)ring_sink_pages(o->num_sinks, d->block_size) + o->ring_pages > max_blocks) return PKV_ERR_SHAPE;
+    }
     return PKV_OK;
 }
 
@@ -230,6 +239,10 @@ DecodeParams fill_params(const pkv_cache_desc* d, const void* k, const void* v, 
     p.window = o ? o->window : 0;
     p.sinks = o ? o->num_sinks : 0;
     p.pages_per_seq = o ? o->pages_per_seq : 0;
+    if (o && o->ring_pages > 0) {
+        p.ring_sink_pages = ring_sink_pages(o->num_sinks, d->block_size);
+        p.ring_pages = o->ring_pages;
+    }
     p.units_per_split = pl.units_per_split;
     p.num_splits = pl.num_splits;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->head_dim);
@@ -525,6 +538,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_MODE: return "invalid sparsity options (window with page_list, bad field)";
         case PKV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case PKV_ERR_HIP: return "HIP launch error";
+        case PKV_ERR_NO_BLOCKS: return "too few free blocks";
     }
     return "unknown status";
 }

@@ -110,7 +110,7 @@ void decode_split_kernel(DecodeParams p) {
         const int u = u_begin + w + lane * kWaves;
         const int t0 = unit_token<MODE>(p, sp, b, u);
         if (t0 >= 0) {
-            const int phys = p.block_table[(size_t)b * p.max_blocks + t0 / p.block_size];
+            const int phys = p.block_table[(size_t)b * p.max_blocks + table_col(p, t0 / p.block_size)];
             if (phys >= 0 && phys < p.num_blocks) {
                 const size_t elem = (((size_t)phys * p.kv_heads + kvh) * p.block_size + (t0 % p.block_size)) * D;
                 my_off = (unsigned)(elem * DT::kBytes / 16);

@@ -47,7 +47,9 @@ struct DecodeParams {
     int32_t q_heads;
     int32_t group;
     int32_t max_blocks;
-    int32_t len_cap;       // min(max_context_len, max_blocks * block_size)
+    int32_t len_cap;       // max_context_len, and with a plain table at most max_blocks * block_size
+    int32_t ring_sink_pages;  // ring table: columns [0, ring_sink_pages) hold the sink pages
+    int32_t ring_pages;       // ring table: pages past them cycle through this many columns (0: plain)
     int32_t window;
     int32_t sinks;
     int32_t pages_per_seq;

@@ -63,6 +63,15 @@ __device__ __forceinline__ int unit_token(const DecodeParams& p, const SeqPlan& 
     return u << 4;
 }
 
+// Block-table column of logical page `page`: the page itself, or on a window layer's ring
+// table ([Novita] §關鍵技術 1: a window layer keeps fewer blocks) the sink columns first and
+// then page - sink_pages taken modulo the ring size.
+__device__ __forceinline__ int table_col(const DecodeParams& p, int page) {
+    if (p.ring_pages > 0 && page >= p.ring_sink_pages)
+        return p.ring_sink_pages + (page - p.ring_sink_pages) % p.ring_pages;
+    return page;
+}
+
 // Bit i set: token t0 + 4j + i is attended.
 __device__ __forceinline__ unsigned token_keep(const SeqPlan& sp, int t0, int j) {
     if (t0 < 0) return 0u;

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:pkv_status|size_t|int32_t|uint64_t|const char\s*\*)\s+(\w+)\s*\(",
+    names = re.findall(r"^\s*(?:pkv_status|size_t|int32_t|int64_t|uint64_t|void|const char\s*\*)\s+(\w+)\s*\(",
                        text, flags=re.M)
     return names
 
@@ -30,7 +30,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("kv_cache_append", "paged_decode_attention", "paged_decode_attention_workspace_size",
                  "paged_decode_attention_partial", "paged_decode_combine", "pkv_status_string",
-                 "pkv_kv_cache_bytes", "paged_decode_attention_num_splits"):
+                 "pkv_kv_cache_bytes", "paged_decode_attention_num_splits", "paged_select_pages",
+                 "pkv_ring_pages", "pkv_policy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_append",
+                 "pkv_bm_release", "pkv_bm_block_tables", "pkv_bm_blocks_in_use"):
         assert must in names
 
 
@@ -41,7 +43,7 @@ def test_library_exports_every_declared_symbol(pkv):
 
 
 def test_status_strings(pkv):
-    for s in range(7):
+    for s in range(8):
         assert pkv.status_string(s) and pkv.status_string(s) != "unknown status"
     assert pkv.status_string(99) == "unknown status"
 
