@@ -86,6 +86,10 @@ def parse():
     ap.add_argument("--loop", action="store_true",
                     help="page-selected workload: close the loop; each step exports per-page scores and "
                          "paged_select_pages picks the next step's pages from them (newest page kept)")
+    ap.add_argument("--policy", action="store_true",
+                    help="multi-layer workloads with window layers: per-layer memory policy; window layers keep "
+                         "only sink pages plus a ring of pages in pools of their own, and every layer's table "
+                         "and slots come from the library's block manager")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -195,23 +199,71 @@ def cpu_baseline(w, lens, seed, reps, seconds, dev):
                 seconds=round(total_s, 3))
 
 
-def _layer_caches(w, lens, P, seed, dev, tag, bt):
-    """One layer's K/V pools, prefilled with tokens [0, L_b - 1) of every sequence."""
+def _layer_caches(w, lens, P, seed, dev, tag, bt, nb=None, slots=None):
+    """One layer's K/V pools, prefilled with tokens [0, L_b - 1) of every sequence: at the slots
+    of the plain table bt, or at slots[b] (the block manager's, for a pool of nb blocks)."""
     import torch
 
     import paged_kv_cache_16_amd as pkv
     import synth
 
     d, Hkv = w.head_dim, w.kv_heads
-    nb = int(bt.max()) + 1
+    nb = int(bt.max()) + 1 if nb is None else nb
     gk = torch.empty((nb, Hkv, P, d), dtype=synth.TORCH_DTYPE[w.dtype], device=dev)
     gv = torch.empty_like(gk)
     for b, L in enumerate(lens):
         if L > 1:
             kb = synth.normal((L - 1, Hkv, d), seed, w.name, tag, b, "k", dtype=w.dtype, device=dev)
             vb = synth.normal((L - 1, Hkv, d), seed, w.name, tag, b, "v", dtype=w.dtype, device=dev)
-            pkv.kv_cache_append(gk, gv, kb, vb, synth.token_slots(bt[b:b + 1], [L - 1], P).to(dev))
+            sl = synth.token_slots(bt[b:b + 1], [L - 1], P).to(dev) if slots is None else slots[b]
+            pkv.kv_cache_append(gk, gv, kb, vb, sl)
     return gk, gv
+
+
+def _policy_setup(w, base, steps, P, bt, nb, dev):
+    """Per-layer memory policy: group 0 = full layers (nb blocks), group 1 = window layers (a
+    ring of sink pages + R pages per sequence). The block manager takes the prefill of L-1
+    tokens and then every step's new tokens; returns its slots and tables on the device."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+
+    B = len(base)
+    R = pkv.ring_pages(w.window, P)
+    nb_ring = B * (-(-w.sinks // P) + R)
+    bm = pkv.BlockManager(P, B, bt.shape[1], [dict(num_blocks=nb), dict(window=w.window, num_sinks=w.sinks,
+                                                                       num_blocks=nb_ring)])
+    ids = np.arange(B, dtype=np.int32)
+    pre, _ = bm.append(ids, [L - 1 for L in base])
+    pre_slots = []
+    for g in range(2):
+        cuts = np.cumsum([0] + [L - 1 for L in base])
+        pre_slots.append([torch.from_numpy(pre[g, cuts[b]:cuts[b + 1]].copy()).to(dev) for b in range(B)])
+    step_slots = []
+    for _ in range(steps):
+        sl, _ = bm.append(ids)
+        step_slots.append([torch.from_numpy(sl[g].copy()).to(dev) for g in range(2)])
+    # tables only gain entries after a page is first reached, so the last step's tables serve
+    # every step
+    tables = [torch.from_numpy(bm.block_table(g, ids)).to(dev) for g in range(2)]
+    in_use = [bm.blocks_in_use(g) for g in range(2)]
+    # host cost of the manager per decode step (through the Python binding): one append for the
+    # batch and both tables
+    n = 2000
+    bm2 = pkv.BlockManager(P, B, bt.shape[1] + n // P + 1, [dict(num_blocks=nb + B * (n // P + 1)),
+                                               dict(window=w.window, num_sinks=w.sinks, num_blocks=nb_ring)])
+    bm2.append(ids, [L - 1 for L in base])
+    t0 = time.perf_counter()
+    for _ in range(n):
+        bm2.append(ids)
+        bm2.block_table(0, ids)
+        bm2.block_table(1, ids)
+    host_us = (time.perf_counter() - t0) * 1e6 / n
+    bm.close()
+    bm2.close()
+    return dict(R=R, nb_ring=nb_ring, pre_slots=pre_slots, step_slots=step_slots, tables=tables, in_use=in_use,
+                host_us=host_us)
 
 
 def run_multilayer(w, args, dev):
@@ -233,18 +285,27 @@ def run_multilayer(w, args, dev):
     cap = [L + steps - 1 for L in base]
     bt, nb = synth.block_tables(cap, P, args.seed, w.name)
     gbt = bt.to(dev)
+    policy = _policy_setup(w, base, steps, P, bt, nb, dev) if args.policy and w.window_layers else None
+    slots_plain = [torch.tensor([synth.slot_of(bt, b, L + s - 1, P) for b, L in enumerate(base)],
+                                dtype=torch.int32, device=dev) for s in range(steps)]
     layers = []
     for layer in range(w.layers):
-        gk, gv = _layer_caches(w, base, P, args.seed, dev, 1000 + layer, bt)
+        win = layer in w.window_layers
+        if policy:
+            g = 1 if win else 0
+            gk, gv = _layer_caches(w, base, P, args.seed, dev, 1000 + layer, bt,
+                                   nb=policy["nb_ring"] if win else nb, slots=policy["pre_slots"][g])
+            table, slots, ring = policy["tables"][g], [st[g] for st in policy["step_slots"]], policy["R"] if win else 0
+        else:
+            gk, gv = _layer_caches(w, base, P, args.seed, dev, 1000 + layer, bt)
+            table, slots, ring = gbt, slots_plain, 0
         layers.append(dict(
-            k=gk, v=gv,
+            k=gk, v=gv, bt=table, slots=slots, ring=ring,
             q=synth.normal((B, Hq, d), args.seed, w.name, layer, "q", dtype=w.dtype, device=dev),
             kn=synth.normal((steps, B, Hkv, d), args.seed, w.name, layer, "kn", dtype=w.dtype, device=dev),
             vn=synth.normal((steps, B, Hkv, d), args.seed, w.name, layer, "vn", dtype=w.dtype, device=dev),
-            window=w.window if layer in w.window_layers else 0))
+            window=w.window if win else 0))
     lens_s = [torch.tensor([L + s for L in base], dtype=torch.int32, device=dev) for s in range(steps)]
-    slots_s = [torch.tensor([synth.slot_of(bt, b, L + s - 1, P) for b, L in enumerate(base)],
-                            dtype=torch.int32, device=dev) for s in range(steps)]
     mcl = max(cap)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -259,10 +320,10 @@ def run_multilayer(w, args, dev):
         # events on the layers with (s_i + layer) % every == 0, so the sample rotates over layers
         for li, ly in enumerate(layers):
             ev = evs[li] if evs is not None and (s_i + li) % every == 0 else None
-            pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], slots_s[s],
-                                              gbt, lens_s[s], max_context_len=mcl, window=ly["window"],
+            pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], ly["slots"][s],
+                                              ly["bt"], lens_s[s], max_context_len=mcl, window=ly["window"],
                                               num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
-                                              workspace=ws, timing=ev)
+                                              workspace=ws, timing=ev, ring_pages=ly["ring"])
 
     reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
     for s in range(min(steps, 4)):
@@ -336,6 +397,21 @@ def run_multilayer(w, args, dev):
         "attention_us_window_layer_mean": round(statistics.fmean(win_us), 2) if win_us else None,
         "hbm_frac_of_peak": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBS, 4),
     }
+    blk_bytes = 2 * Hkv * P * d * synth.DTYPE_BYTES[w.dtype]  # K and V of one block
+    n_win = len(w.window_layers)
+    res["kv_pool_bytes"] = w.layers * nb * blk_bytes
+    if policy:
+        res["config"]["memory_policy"] = (f"full layers: one block per page; window layers: ring of "
+                                          f"{-(-w.sinks // P)} sink + {policy['R']} pages per sequence")
+        res["kv_pool_bytes_policy"] = ((w.layers - n_win) * nb + n_win * policy["nb_ring"]) * blk_bytes
+        # what the sequences hold at the last step, per the accounting of the [primer] KV formula
+        res["kv_bytes_held"] = {
+            "full_layers": (w.layers - n_win) * policy["in_use"][0] * blk_bytes,
+            "window_layers": n_win * policy["in_use"][1] * blk_bytes,
+            "all_layers_full_cache": w.layers * sum(pkv.kv_cache_bytes(1, 1, Hkv, d, L + steps - 1,
+                                                                       synth.DTYPE_BYTES[w.dtype], P)
+                                                    for L in base)}
+        res["block_manager_us_per_step"] = round(policy["host_us"], 2)
     if full_us:
         per_layer_bytes = sum(base) * w.kv_bytes_per_token()  # first step's full-layer bytes
         res["attention_full_layer_GBps_at_step1"] = round(per_layer_bytes / (min(full_us) * 1e3), 1)
