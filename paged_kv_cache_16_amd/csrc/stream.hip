@@ -512,6 +512,25 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
     const int lane = threadIdx.x;
     const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
+    const size_t base = (size_t)g * p.kmax * G + head;  // partial row of slot k: base + k * G
+    const float* op = p.o_part + base * D + lane * PER;
+    // Slots come in batches of KB, fetched whole: every slot below kmax is addressable, and
+    // the slots past the count are dropped by selection (their contents are stale, never
+    // multiplied in). The first batch is requested before the count and the context length
+    // arrive, so that the three loads share one round trip.
+    constexpr int KB = 16;
+    float lv[KB], mv[KB], v[KB][PER];
+    auto fetch = [&](int k) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const size_t rk = base + (size_t)(k + u < p.kmax ? k + u : 0) * G;
+            lv[u] = p.l_part[rk];
+            mv[u] = p.m_part[rk];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[u][i] = op[(rk - base) * D + i];
+        }
+    };
+    fetch(0);
     const int nu = seq_units<MODE>(p, b);
     int cnt = p.seg_count[g];
     if (nu == 0) {
@@ -523,48 +542,37 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     }
     if (cnt == 0) return;
     if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
-    const size_t base = (size_t)g * p.kmax * G + head;  // partial row of slot k: base + k * G
-    const float* op = p.o_part + base * D + lane * PER;
-    const size_t stride = (size_t)G * D;
-    // Online merge over batches of 8 slots; every slot below kmax is addressable, so a batch
-    // is fetched whole and the slots past cnt are dropped by selection (their contents are
-    // stale, never multiplied in).
+    // online merge over the batches
     float M = kNegInf, Ls = 0.f;
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    for (int k = 0; k < cnt; k += 8) {
-        float lv[8], mv[8], v[8][PER];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool in = k + u < p.kmax;
-            const size_t rk = base + (size_t)(in ? k + u : 0) * G;
-            lv[u] = p.l_part[rk];
-            mv[u] = p.m_part[rk];
-#pragma unroll
-            for (int i = 0; i < PER; ++i) v[u][i] = op[(size_t)(in ? k + u : 0) * stride + i];
-        }
+    for (int k = 0;;) {
         float bm = kNegInf;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < KB; ++u) {
             const bool live = k + u < cnt && lv[u] > 0.f;
             bm = fmaxf(bm, live ? mv[u] : kNegInf);
         }
         const float m_new = fmaxf(M, bm);
-        if (m_new == kNegInf) continue;
-        const float sc = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
-        Ls *= sc;
+        if (m_new != kNegInf) {
+            const float sc = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+            Ls *= sc;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] *= sc;
+            for (int i = 0; i < PER; ++i) o[i] *= sc;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool live = k + u < cnt && lv[u] > 0.f;
-            const float w = live ? __builtin_amdgcn_exp2f(mv[u] - m_new) : 0.f;
-            Ls += live ? w * lv[u] : 0.f;
+            for (int u = 0; u < KB; ++u) {
+                const bool live = k + u < cnt && lv[u] > 0.f;
+                const float w = live ? __builtin_amdgcn_exp2f(mv[u] - m_new) : 0.f;
+                Ls += live ? w * lv[u] : 0.f;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) o[i] += live ? w * v[u][i] : 0.f;
+                for (int i = 0; i < PER; ++i) o[i] += live ? w * v[u][i] : 0.f;
+            }
+            M = m_new;
         }
-        M = m_new;
+        k += KB;
+        if (k >= cnt) break;
+        fetch(k);
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
