@@ -14,6 +14,7 @@ constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 2
 constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persistent kernel: small
                                          // problems spread over many waves (one wave streams only
                                          // a few GB/s, so bandwidth comes from wave count)
+constexpr int kRunSetupBytes = 8192;    // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
@@ -58,6 +59,8 @@ struct Plan {
     enum Path { kDirect, kPartitions, kStream } path = kDirect;
     int kmax = 0;       // stream path: partial slots per segment
     int chunk_min = 0;  // stream path: minimum units per wave
+    int lead = 0;       // stream path: virtual units charged at each segment start
+    int unit_bytes = 0;  // K and V bytes of one 16-token unit of one kv head
     bool q8 = false;    // INT8 cache: the stream path only
 };
 
@@ -75,9 +78,15 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
         pl.path = Plan::kStream;
         // at least kStreamChunkMin units per wave, and few enough slots per segment for
         // the combine's LDS table
+        // A run's set-up (query and descriptors fetched, load ring refilled) takes about as
+        // long as streaming 8 KiB per wave, so every segment start counts as that many bytes'
+        // worth of units: a wave whose share crosses into a new segment streams fewer units.
+        pl.lead = pl.unit_bytes > 0 ? (kRunSetupBytes + pl.unit_bytes / 2) / pl.unit_bytes : 1;
+        if (pl.lead < 1) pl.lead = 1;
+        const int span = pl.units_bound + pl.lead;  // flat positions of the longest segment
         pl.chunk_min = kStreamChunkMin;
-        while ((pl.units_bound + pl.chunk_min - 1) / pl.chunk_min + 1 > kMaxSlots) pl.chunk_min *= 2;
-        pl.kmax = (pl.units_bound + pl.chunk_min - 1) / pl.chunk_min + 1;
+        while ((span + pl.chunk_min - 1) / pl.chunk_min + 1 > kMaxSlots) pl.chunk_min *= 2;
+        pl.kmax = (span + pl.chunk_min - 1) / pl.chunk_min + 1;
     }
 }
 
@@ -123,6 +132,7 @@ Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_
                const pkv_decode_opts* o) {
     Plan pl;
     pl.q8 = d->dtype == PKV_I8;
+    pl.unit_bytes = 2 * 16 * (d->head_dim * elem_bytes(d->dtype) + (pl.q8 ? 4 : 0));
     const int P = d->block_size;
     long long cap = max_context_len;
     // a ring table addresses any length through its columns
@@ -356,15 +366,15 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         const int G = num_q_heads / desc->num_kv_heads;
         const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim, scores, pl.units_bound);
         if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
-        const long long n_bound = (long long)batch * desc->num_kv_heads * pl.units_bound;
+        const long long n_bound = (long long)batch * desc->num_kv_heads * (pl.units_bound + pl.lead);
         if (n_bound > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
         const long long resident =
-            (long long)device_cus(dev) * device_occupancy(dev, kdt(desc), desc->head_dim, pl.mode) * kWaves;
+            (long long)device_cus(dev) * device_occupancy(dev, kdt(desc), desc->head_dim, pl.mode) * kStreamWaves;
         waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
         if (waves > resident) waves = resident;
-        waves = (waves + kWaves - 1) / kWaves * kWaves;
+        waves = (waves + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
         p.o_part = (float*)((char*)workspace + wl.o_off);
         p.m_part = (float*)((char*)workspace + wl.m_off);
         p.l_part = (float*)((char*)workspace + wl.l_off);
@@ -373,6 +383,7 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.waves_total = (int)waves;
         p.chunk_min = pl.chunk_min;
         p.kmax = pl.kmax;
+        p.seg_lead = pl.lead;
         if (scores) {
             p.logits = (float*)((char*)workspace + wl.logits_off);
             p.row_lse2 = (float*)((char*)workspace + wl.lse2_off);

@@ -19,10 +19,10 @@ struct SeqPlan {
     int n_units;  // units enumerated for this sequence
 };
 
+// Plan of a sequence whose context_lens entry is L (clamped here).
 template <int MODE>
-__device__ __forceinline__ SeqPlan make_plan(const DecodeParams& p, int b) {
+__device__ __forceinline__ SeqPlan make_plan_len(const DecodeParams& p, int L) {
     SeqPlan sp;
-    int L = p.context_lens[b];
     L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
     sp.L = L;
     sp.e0 = 0;
@@ -45,6 +45,11 @@ __device__ __forceinline__ SeqPlan make_plan(const DecodeParams& p, int b) {
         sp.n_units = nu_full;
     }
     return sp;
+}
+
+template <int MODE>
+__device__ __forceinline__ SeqPlan make_plan(const DecodeParams& p, int b) {
+    return make_plan_len<MODE>(p, p.context_lens[b]);
 }
 
 // First logical token of unit u, or -1 when the unit holds no attended token.

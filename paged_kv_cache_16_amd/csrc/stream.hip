@@ -62,10 +62,10 @@ struct UnitPos {
     int b, kvh, u, nu;
 };
 
-// Advances a position by k units (k >= 0), skipping sequences without units. Returns
-// b == batch when it runs off the end.
-template <int MODE>
-__device__ __forceinline__ UnitPos advance(const DecodeParams& p, UnitPos s, int k) {
+// Advances a position by k units (k >= 0), skipping sequences without units (units_of(b):
+// the units of sequence b). Returns b == batch when it runs off the end.
+template <class UnitsOf>
+__device__ __forceinline__ UnitPos advance(const DecodeParams& p, UnitPos s, int k, UnitsOf units_of) {
     while (s.b < p.batch) {
         const int rem = s.nu - s.u;
         if (k < rem) {
@@ -78,7 +78,7 @@ __device__ __forceinline__ UnitPos advance(const DecodeParams& p, UnitPos s, int
             s.kvh = 0;
             do {
                 ++s.b;
-            } while (s.b < p.batch && (s.nu = seq_units<MODE>(p, s.b)) == 0);
+            } while (s.b < p.batch && (s.nu = units_of(s.b)) == 0);
         }
     }
     return s;
@@ -193,12 +193,14 @@ __device__ __forceinline__ void patch_tile(u32x4 (&k)[D / (4 * DT::kE)], u32x4 (
             // token 4j+i of dim 16n + c is element (n % R) * 4 + i of chunk n / R
             if constexpr (DT::kBytes == 2) {
                 const int target = (n % R) * 2 + (i >> 1);  // dword holding the element
-                const bool high = i & 1;
+                // one byte permute puts the element's two bytes in the high or low half of the
+                // dword (bytes 0-3 select from wd, 4-7 from the new row); nothing here depends
+                // on the new row alone, so its loads are not waited for before the tile is
+                const unsigned sel = (i & 1) ? 0x05040100u : 0x03020504u;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const unsigned wd = v[n / R][w];
-                    const unsigned upd = high ? ((wd & 0x0000ffffu) | (nr.v[n] << 16))
-                                              : ((wd & 0xffff0000u) | (nr.v[n] & 0xffffu));
+                    const unsigned upd = __builtin_amdgcn_perm(nr.v[n], wd, sel);
                     v[n / R][w] = w == target ? upd : wd;
                 }
             } else {
@@ -215,7 +217,7 @@ __device__ __forceinline__ void patch_tile(u32x4 (&k)[D / (4 * DT::kE)], u32x4 (
 constexpr int kLgFloats = 1024;
 
 template <class DT, int D, int MODE, bool FUSED, bool SCORES>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
     static_assert(!(DT::kQ8 && FUSED), "INT8 caches take the separate quantising append");
     using TI = typename DT::In;               // q and MFMA operand type
@@ -224,17 +226,35 @@ void decode_stream_kernel(DecodeParams p) {
     using T = Tile<TI, NC>;
     constexpr int NACC = T::kAcc;
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = blockIdx.x * kStreamWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane >> 4, c = lane & 15;
     const int B = p.batch, Hkv = p.kv_heads, G = p.group;
 
-    // Total units N of the batch (uniform: kept in scalar registers).
-    int N = 0;
-    for (int b0 = 0; b0 < B; b0 += 64) {
+    // Context lengths of the first 64 sequences, one per lane, are read once: the work split,
+    // every run's plan and the step to the next sequence take them from here by readlane
+    // (sequences past 64 are read from memory).
+    const int L_lane = lane < B ? p.context_lens[lane] : 0;
+    auto len_of = [&](int b) -> int {  // b is wave-uniform
+        return b < 64 ? __builtin_amdgcn_readlane(L_lane, b) : p.context_lens[b];
+    };
+    // Flat positions of a segment: its units plus `lead` virtual ones in front, which stand
+    // for the set-up of a run (query and descriptors fetched, load ring refilled). A wave whose
+    // share takes a segment's start therefore streams that many fewer units, and shares that
+    // cross segment boundaries take as long as those that do not.
+    const int lead = p.seg_lead;
+    auto flat_of = [&](int nu) -> int { return nu > 0 ? nu + lead : 0; };
+    auto units_of = [&](int b) -> int { return flat_of(make_plan_len<MODE>(p, len_of(b)).n_units); };
+
+    // Total flat positions N of the batch (uniform: kept in scalar registers). The first 64
+    // sequences' inclusive scan gives their total and also serves the search for the wave's
+    // first position.
+    const int nu_lane = lane < B ? flat_of(make_plan_len<MODE>(p, L_lane).n_units) : 0;
+    const int incl_lane = wave_incl_scan(nu_lane * Hkv, lane);
+    int N = __builtin_amdgcn_readlane(incl_lane, 63);
+    for (int b0 = 64; b0 < B; b0 += 64) {
         const int b = b0 + lane;
-        N += __builtin_amdgcn_readfirstlane(wave_sum(b < B ? seq_units<MODE>(p, b) : 0));
+        N += __builtin_amdgcn_readfirstlane(wave_sum(b < B ? flat_of(seq_units<MODE>(p, b)) : 0)) * Hkv;
     }
-    N *= Hkv;
     const int W = p.waves_total;
     int C = (N + W - 1) / W;
     if (C < p.chunk_min) C = p.chunk_min;
@@ -248,9 +268,8 @@ void decode_stream_kernel(DecodeParams p) {
         int cum = 0;
         for (int b0 = 0; b0 < B; b0 += 64) {
             const int b = b0 + lane;
-            const int nu = b < B ? seq_units<MODE>(p, b) : 0;
-            const int cnt = nu * Hkv;
-            const int incl = wave_incl_scan(cnt, lane);
+            const int nu = b0 == 0 ? nu_lane : (b < B ? flat_of(seq_units<MODE>(p, b)) : 0);
+            const int incl = b0 == 0 ? incl_lane : wave_incl_scan(nu * Hkv, lane);
             const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
             if (cum + chunk_total > f_begin) {
                 const unsigned long long hit = __ballot(cum + incl > f_begin);
@@ -272,15 +291,21 @@ void decode_stream_kernel(DecodeParams p) {
     // kv head) segment piece with its own query, softmax state and load pipeline.
     const int qhead = c & 7;
     const bool upper = c >= 8;
-    __shared__ float lg_stage[kWaves * (SCORES ? kLgFloats : 1)];
+    __shared__ float lg_stage[kStreamWaves * (SCORES ? kLgFloats : 1)];
     float* lgb = lg_stage + (SCORES ? (threadIdx.x >> 6) * kLgFloats : 0);
     const float qk_scale = p.qk_scale_log2;
     int f_run = f_begin;
     while (f_run < f_end && pos.b < B) {
-        const int b = pos.b, kvh = pos.kvh, u0 = pos.u, nu = pos.nu;
-        const int cnt = f_end - f_run < nu - u0 ? f_end - f_run : nu - u0;
+        // pos.u / pos.nu: flat positions within the segment; real units are u0 .. u0 + cnt
+        const int b = pos.b, kvh = pos.kvh, v0 = pos.u, nv = pos.nu;
+        const int cntv = f_end - f_run < nv - v0 ? f_end - f_run : nv - v0;
+        const int nu = nv - lead;
+        const int u0 = v0 > lead ? v0 - lead : 0;
+        const int cnt = (v0 + cntv > lead ? v0 + cntv - lead : 0) - u0;
+        // cnt == 0 (the share holds only virtual positions of this segment) leaves an empty
+        // piece, l = 0, which the combine skips; it is never the segment's last piece
         const int seg = b * Hkv + kvh;
-        const SeqPlan sp = make_plan<MODE>(p, b);
+        const SeqPlan sp = make_plan_len<MODE>(p, len_of(b));
 
         u32x4 q[NC];
 #pragma unroll
@@ -454,7 +479,7 @@ void decode_stream_kernel(DecodeParams p) {
         const int head = T::acc_head(c);
         const bool writer = head < G && T::acc_owner(c);
         const bool last = u0 + cnt == nu;
-        if (u0 == 0 && last) {
+        if (v0 == 0 && last) {
             const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             if (writer) {
@@ -472,7 +497,7 @@ void decode_stream_kernel(DecodeParams p) {
             }
             if (lane == 0) p.seg_count[seg] = 0;
         } else {
-            const int s_g = f_run - u0;  // flat index of the segment's unit 0
+            const int s_g = f_run - v0;  // flat index of the segment's first position
             const int k_slot = wave - s_g / C;
             if (k_slot < p.kmax) {
                 const size_t row = ((size_t)seg * p.kmax + k_slot) * G + head;
@@ -488,8 +513,8 @@ void decode_stream_kernel(DecodeParams p) {
                 if (lane == 0 && last) p.seg_count[seg] = k_slot + 1;
             }
         }
-        f_run += cnt;
-        pos = advance<MODE>(p, pos, cnt);
+        f_run += cntv;
+        pos = advance(p, pos, cntv, units_of);
         pos.b = __builtin_amdgcn_readfirstlane(pos.b);
         pos.kvh = __builtin_amdgcn_readfirstlane(pos.kvh);
         pos.u = __builtin_amdgcn_readfirstlane(pos.u);
@@ -748,12 +773,12 @@ __global__ __launch_bounds__(256) void score_page_kernel(DecodeParams p) {
 template <class DT, int D, int MODE>
 static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p, hipStream_t s, hipEvent_t e0,
                                   hipEvent_t e1) {
-    const unsigned blocks = (unsigned)(p.waves_total / kWaves);
+    const unsigned blocks = (unsigned)(p.waves_total / kStreamWaves);
     if (e0) {
         hipError_t e = hipEventRecord(e0, s);
         if (e != hipSuccess) return e;
     }
-    const dim3 grid(blocks), block(64 * kWaves);
+    const dim3 grid(blocks), block(64 * kStreamWaves);
     if constexpr (DT::kQ8) {
         if (fused) return hipErrorInvalidValue;
         if (scores)
@@ -831,9 +856,9 @@ static int occupancy_t() {
     // the least occupancy of the variants, so that every launch fits at once
     int m = 0;
     constexpr bool F = !DT::kQ8;  // the fused variants exist for the 16/32-bit caches
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, F, false>, 64 * kWaves,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<DT, D, MODE, F, false>, 64 * kStreamWaves,
                                                      0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_stream_kernel<DT, D, MODE, F, true>, 64 * kWaves,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_stream_kernel<DT, D, MODE, F, true>, 64 * kStreamWaves,
                                                      0) != hipSuccess)
         return 1;
     n = m < n ? m : n;
