@@ -14,7 +14,7 @@ constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 2
 constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persistent kernel: small
                                          // problems spread over many waves (one wave streams only
                                          // a few GB/s, so bandwidth comes from wave count)
-constexpr int kRunSetupBytes = 8192;    // streaming time per wave of one run's set-up, in bytes
+constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
@@ -78,9 +78,11 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
         pl.path = Plan::kStream;
         // at least kStreamChunkMin units per wave, and few enough slots per segment for
         // the combine's LDS table
-        // A run's set-up (query and descriptors fetched, load ring refilled) takes about as
-        // long as streaming 8 KiB per wave, so every segment start counts as that many bytes'
-        // worth of units: a wave whose share crosses into a new segment streams fewer units.
+        // A run's set-up (query and descriptors fetched, load ring refilled, and the previous
+        // run's partial stored) costs a wave about what streaming kRunSetupBytes does, so every
+        // segment start counts as that many bytes' worth of units: a wave whose share crosses
+        // into a new segment streams fewer units. The charge was set by timing the
+        // Llama-3-8B layer shape at 0..8 units (24 KiB: 3 units of a 2-byte d=128 cache).
         pl.lead = pl.unit_bytes > 0 ? (kRunSetupBytes + pl.unit_bytes / 2) / pl.unit_bytes : 1;
         if (pl.lead < 1) pl.lead = 1;
         const int span = pl.units_bound + pl.lead;  // flat positions of the longest segment
