@@ -14,6 +14,7 @@ constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 2
 constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persistent kernel: small
                                          // problems spread over many waves (one wave streams only
                                          // a few GB/s, so bandwidth comes from wave count)
+constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
@@ -376,6 +377,10 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
             (long long)device_cus(dev) * device_occupancy(dev, kdt(desc), desc->head_dim, pl.mode) * kStreamWaves;
         waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
         if (waves > resident) waves = resident;
+        // one wave per SIMD: each wave keeps several units of loads in flight, so 4 waves per
+        // CU already hold far more bytes in flight than the HBM latency needs; fewer, longer
+        // shares spend less of the kernel on per-share set-up and even out the finish times
+        if (waves > (long long)device_cus(dev) * kSimdsPerCu) waves = (long long)device_cus(dev) * kSimdsPerCu;
         waves = (waves + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
         p.o_part = (float*)((char*)workspace + wl.o_off);
         p.m_part = (float*)((char*)workspace + wl.m_off);
