@@ -531,7 +531,12 @@ template <int D, int MODE, int ES>
 __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;
     const int r = blockIdx.x;
-    if (p.new_slots && r < p.batch * p.kv_heads) write_new_row<ES, D>(p, r, threadIdx.x);
+    if (r >= p.batch * p.q_heads) {
+        // the fused step's new K/V rows, in workgroups of their own beside the merges (a merge
+        // workgroup that also stored a row waited for the row before fetching its partials)
+        write_new_row<ES, D>(p, r - p.batch * p.q_heads, threadIdx.x);
+        return;
+    }
     const int G = p.group;
     const int g = r / G, head = r - g * G;
     const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
@@ -802,7 +807,8 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
         err = hipEventRecord(e1, s);
         if (err != hipSuccess) return err;
     }
-    stream_combine_kernel<D, MODE, DT::kBytes><<<dim3((unsigned)(p.batch * p.q_heads)), dim3(64), 0, s>>>(p);
+    stream_combine_kernel<D, MODE, DT::kBytes>
+        <<<dim3((unsigned)(p.batch * p.q_heads + (p.new_slots ? p.batch * p.kv_heads : 0))), dim3(64), 0, s>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess || !scores) return err;
     if (MODE == kPages && p.score_block == p.block_size) {
