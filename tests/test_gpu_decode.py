@@ -175,6 +175,50 @@ def test_fuzz(f):
     assert_close(c, gpu_attend(c, **gkw), oracle_attend(c, **okw), "fuzz")
 
 
+# ---------------------------------------------------------------------------- batches past 64
+@pytest.mark.parametrize("B,mode,fused", [(65, "full", False), (129, "full", True), (130, "window", True),
+                                          (200, "pages", False), (200, "full", True)])
+def test_batches_beyond_64(B, mode, fused):
+    """More than 64 sequences: the persistent kernel holds the first 64 lengths in lanes and
+    reads the rest from memory, scanning them per 64-sequence chunk; empty sequences sit on
+    both sides of the chunk boundary and one long sequence past it takes many waves."""
+    import paged_kv_cache_16_amd as pkv
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(0, 160, size=B)]
+    lens[63] = 0
+    lens[64] = 0
+    lens[B - 2] = 1500
+    log(f"batch {B} {mode} fused={fused} sum(L)={sum(lens)}")
+    c = make_case(60 + B, B=B, Hq=8, Hkv=2, d=128, dtype="bf16", P=16, lens=lens)
+    okw, gkw = {}, {}
+    if mode == "window":
+        okw, gkw = dict(window=100, sinks=3), dict(window=100, num_sinks=3)
+    elif mode == "pages":
+        pl = np.full((B, 3), -1, np.int32)
+        for b, L in enumerate(lens):
+            npg = (L + 15) // 16
+            if npg:
+                pick = sorted(rng.choice(npg, size=min(3, npg), replace=False).tolist())
+                pl[b, :len(pick)] = pick
+        okw = dict(page_list=pl)
+        gkw = dict(page_list=torch.as_tensor(pl).cuda())
+    ref = oracle_attend(c, **okw)
+    if not fused:
+        got = gpu_attend(c, **{k: v for k, v in gkw.items() if k != "page_list"},
+                         page_list=okw.get("page_list"))
+    else:
+        # the cache already holds every row; the step appends row L-1 again from k_new/v_new
+        slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) if L else -1 for b, L in enumerate(lens)],
+                             dtype=torch.int32).cuda()
+        kn = torch.stack([c.K[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+        vn = torch.stack([c.V[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+        out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
+                                                     max_context_len=max(lens), **gkw)
+        torch.cuda.synchronize()
+        got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    assert_close(c, got, ref, f"batch {B} {mode}")
+
+
 # ---------------------------------------------------------------------------- special cases
 def test_empty_and_single_token():
     c = make_case(40, B=3, Hq=4, Hkv=1, d=128, dtype="bf16", P=16, lens=[0, 1, 0])
