@@ -17,6 +17,7 @@ launch stream around every 8th timed launch (--event-every).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -90,6 +91,12 @@ def parse():
                     help="multi-layer workloads with window layers: per-layer memory policy; window layers keep "
                          "only sink pages plus a ring of pages in pools of their own, and every layer's table "
                          "and slots come from the library's block manager")
+    ap.add_argument("--context", type=int, default=0,
+                    help="default workload: every sequence at this context length instead of U[1024, 4096] "
+                         "(4001: the 4000-token prompt plus one decode step)")
+    ap.add_argument("--tp-share", type=int, default=1,
+                    help="default workload at one tensor-parallel GPU's share: kv and query heads divided by "
+                         "this (8: 1 kv head, 4 query heads); 16 replicas so the MALL cannot serve repeats")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -536,7 +543,18 @@ def main():
     if w.pages_per_step:
         print(json.dumps(run_page_selected(w, args, dev)), flush=True)
         return
-    lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
+    variant = args.context > 0 or args.tp_share > 1
+    if variant:
+        if w.kv_heads % args.tp_share:
+            print(f"bench.py: {w.kv_heads} kv heads do not split {args.tp_share} ways", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, kv_heads=w.kv_heads // args.tp_share, q_heads=w.q_heads // args.tp_share)
+        if args.tp_share > 1 and args.replicas == 8:
+            args.replicas = 16
+    if args.context > 0:
+        lens = [args.context] * w.batch
+    else:
+        lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
     kv_bytes = sum(lens) * w.kv_bytes_per_token()
 
     if args.copy_probe_mib:
@@ -608,7 +626,9 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
-            "context": f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}, sum {sum(lens)}, max {mcl}",
+            "context": (f"all {args.context}" if args.context > 0 else f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}")
+            + f", sum {sum(lens)}, max {mcl}",
+            "tp_share": args.tp_share,
             "replicas": args.replicas, "split_tokens": args.split_tokens,
             "step": ("paged_decode_append_attention: append of the 32 new tokens fused into the "
                      "persistent split kernel, then the LSE combine" if args.kv_dtype != "int8" else
@@ -627,14 +647,14 @@ def main():
             if args.split_tokens == 0 else "decode_split_kernel<BF16,128,full>",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (args.scores or args.kv_dtype) else measured_traffic(w.name, args.split_tokens),
+            "traffic": None if (args.scores or args.kv_dtype or variant) else measured_traffic(w.name, args.split_tokens),
             "traffic_unit": "bytes per launch",
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
             "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),
         },
     }
-    if args.cpu_seconds > 0 and not args.kv_dtype:
+    if args.cpu_seconds > 0 and not args.kv_dtype and not variant:
         res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_seconds, dev)
     print(json.dumps(res), flush=True)
 
