@@ -31,7 +31,8 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the comment says "host". The caller owns
  *     every buffer (including workspaces); the library never allocates or frees
- *     memory and keeps no state between calls, so calls are reentrant.
+ *     memory and keeps no state between calls other than the device error word
+ *     (pkv_device_errors), so calls are reentrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *     enqueued asynchronously; no entry point synchronises the host.
  *   - The return value reports host-side argument validation and launch errors
@@ -40,7 +41,8 @@
  *   - Device-side preconditions (listed per call) are not checked on the host.
  *     Where a violation could address memory outside the caller's buffers the
  *     kernels skip the offending element instead (documented per call), so a bad
- *     index never faults; the result for that sequence is then unspecified.
+ *     index never faults; the result for that sequence is then unspecified, and a
+ *     PKV_DEV_* bit is set in the device error word (pkv_device_errors).
  *
  * Cache layout ("lane-chunk order"). Both pools are arrays of
  *   num_blocks x num_kv_heads page tiles, each tile holding block_size x head_dim
@@ -416,6 +418,22 @@ int64_t pkv_bm_context_len(const pkv_block_manager* bm, int32_t seq_id);
 /* Blocks of group g held by all sequences (the sum of pkv_policy_blocks over them); -1 for
  * a bad group. */
 int64_t pkv_bm_blocks_in_use(const pkv_block_manager* bm, int32_t group);
+
+/* Device error word. The kernels set these bits when they skip work whose device-side
+ * precondition does not hold (they never fault on it):
+ *   PKV_DEV_BLOCK_ID  a block-table entry of an attended page outside [0, num_blocks);
+ *   PKV_DEV_SLOT      an append slot >= num_blocks * block_size (kv_cache_append, fused step);
+ *   PKV_DEV_CONTEXT   context_lens[b] above max_context_len or, with a plain table, above
+ *                     max_blocks_per_seq * block_size (the kernels clamp it);
+ *   PKV_DEV_PAGES     paged_select_pages: a sequence with more pages than the score stride.
+ * Page-list order and slot uniqueness are not checked. */
+enum { PKV_DEV_BLOCK_ID = 1, PKV_DEV_SLOT = 2, PKV_DEV_CONTEXT = 4, PKV_DEV_PAGES = 8 };
+
+/* Waits for `stream`, then stores the calling device's error word (an OR of PKV_DEV_* bits
+ * since it was last cleared; 0 when clean) in *flags (host) and, with clear != 0, zeroes it.
+ * Not for use inside graph capture (it synchronises). Work on other streams of the device
+ * may set bits between the read and the clear. Errors: PKV_ERR_NULL, PKV_ERR_HIP. */
+pkv_status pkv_device_errors(uint32_t* flags /* host */, int32_t clear, void* stream);
 
 /* KV-cache size in bytes by the formula of [primer] §3.1,
  *   2 x batch x layers x kv_heads x head_dim x seq_len x dtype_bytes,

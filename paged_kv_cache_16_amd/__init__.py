@@ -22,7 +22,7 @@ __all__ = [
     "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
-    "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks",
+    "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks", "device_errors",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -104,6 +104,8 @@ _lib.pkv_bm_context_len.restype = _i64
 _lib.pkv_bm_context_len.argtypes = [_vp, _i32]
 _lib.pkv_bm_blocks_in_use.restype = _i64
 _lib.pkv_bm_blocks_in_use.argtypes = [_vp, _i32]
+_lib.pkv_device_errors.restype = ctypes.c_int
+_lib.pkv_device_errors.argtypes = [_vp, _i32, _vp]
 _lib.pkv_status_string.restype = ctypes.c_char_p
 _lib.pkv_status_string.argtypes = [ctypes.c_int]
 
@@ -440,6 +442,18 @@ class BlockManager:
 
     def blocks_in_use(self, group: int) -> int:
         return int(_lib.pkv_bm_blocks_in_use(self._h, int(group)))
+
+
+DEV_BLOCK_ID, DEV_SLOT, DEV_CONTEXT, DEV_PAGES = 1, 2, 4, 8
+
+
+def device_errors(clear: bool = True, stream=None) -> int:
+    """The current device's error word (an OR of the DEV_* bits the kernels set when they skip a
+    violated device-side precondition); waits for the stream (default: torch's current one)."""
+    flags = ctypes.c_uint32(0)
+    st = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+    _check("pkv_device_errors", _lib.pkv_device_errors(ctypes.byref(flags), 1 if clear else 0, st))
+    return int(flags.value)
 
 
 def kv_cache_bytes(batch, layers, kv_heads, head_dim, seq_len, dtype_bytes, block_size=0) -> int:

@@ -6,9 +6,30 @@
 #include "../../include/pagedkv.h"
 #include "pkv_internal.h"
 
+// The device error word: kernels OR a PKV_DEV_* bit into it when they skip an element whose
+// device-side precondition does not hold; pkv_device_errors reads (and clears) it. Each device
+// holds its own copy of this module global for the life of the process.
+__device__ unsigned int g_pkv_dev_errors;
+
 namespace {
 
 using namespace pkv;
+
+// Address of the current device's error word (nullptr if it cannot be had: reports are then
+// dropped). Looked up once per device; a race between two first calls stores the same value.
+unsigned* g_err_ptr[64];
+bool g_err_known[64];
+unsigned* dev_err_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (!g_err_known[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_pkv_dev_errors)) != hipSuccess) ptr = nullptr;
+        g_err_ptr[dev] = static_cast<unsigned*>(ptr);
+        g_err_known[dev] = true;
+    }
+    return g_err_ptr[dev];
+}
 
 constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 256 CUs
 constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persistent kernel: small
@@ -239,6 +260,7 @@ DecodeParams fill_params(const pkv_cache_desc* d, const void* k, const void* v, 
                          const int32_t* bt, int32_t max_blocks, const int32_t* cl, int32_t q_heads,
                          float scale, const pkv_decode_opts* o, const Plan& pl) {
     DecodeParams p = {};
+    p.err = dev_err_word();
     p.k_cache = (const char*)k;
     p.v_cache = (const char*)v;
     p.q = (const char*)q;
@@ -281,6 +303,7 @@ pkv_status kv_cache_append(const pkv_cache_desc* desc, void* k_cache, void* v_ca
     if (num_tokens == 0) return PKV_OK;
     if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
     AppendParams p;
+    p.err = dev_err_word();
     p.k_cache = k_cache;
     p.v_cache = v_cache;
     p.k_new = k_new;
@@ -417,6 +440,7 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     const bool fuse = fa && pl.path == Plan::kStream && desc->dtype != PKV_I8;
     if (fa && !fuse) {  // separate append launch ahead of attention
         AppendParams ap;
+        ap.err = p.err;
         ap.k_cache = fa->k_cache;
         ap.v_cache = fa->v_cache;
         ap.k_new = fa->k_new;
@@ -579,6 +603,7 @@ extern "C" pkv_status paged_select_pages(const float* scores, int32_t heads, int
     if (batch == 0) return PKV_OK;
     if (!scores || !context_lens || !page_list) return PKV_ERR_NULL;
     SelectParams p;
+    p.err = dev_err_word();
     p.scores = scores;
     p.context_lens = context_lens;
     p.page_list = page_list;
@@ -589,4 +614,19 @@ extern "C" pkv_status paged_select_pages(const float* scores, int32_t heads, int
     p.k = k;
     p.recent = recent;
     return hip_status(launch_select(p, (hipStream_t)stream));
+}
+
+extern "C" pkv_status pkv_device_errors(uint32_t* flags, int32_t clear, void* stream) {
+    if (!flags) return PKV_ERR_NULL;
+    unsigned* w = dev_err_word();
+    if (!w) return PKV_ERR_HIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return PKV_ERR_HIP;
+    unsigned v = 0;
+    if (hipMemcpy(&v, w, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return PKV_ERR_HIP;
+    *flags = v;
+    if (clear && v) {
+        const unsigned zero = 0;
+        if (hipMemcpy(w, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return PKV_ERR_HIP;
+    }
+    return PKV_OK;
 }

@@ -30,7 +30,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int qc = rem - h * chunks;
 
     const int64_t slot = p.slots[i];
-    if (slot < 0 || slot >= p.num_slots) return;
+    if (slot < 0) return;
+    if (slot >= p.num_slots) {
+        if (rem == 0) report(p.err, kDevSlot);
+        return;
+    }
     const int64_t blk = slot / p.block_size;
     const int t = (int)(slot - blk * p.block_size);
     const int tau = t & 15;
@@ -95,7 +99,11 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
     const int64_t i = row / p.kv_heads;
     const int h = (int)(row - i * p.kv_heads);
     const int64_t slot = p.slots[i];
-    if (slot < 0 || slot >= p.num_slots) return;
+    if (slot < 0) return;
+    if (slot >= p.num_slots) {
+        if (h == 0 && lane == 0) report(p.err, kDevSlot);
+        return;
+    }
     const int64_t blk = slot / p.block_size;
     const int t = (int)(slot - blk * p.block_size);
     const int tau = t & 15;

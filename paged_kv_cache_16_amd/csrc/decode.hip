@@ -115,6 +115,8 @@ void decode_split_kernel(DecodeParams p) {
                 const size_t elem = (((size_t)phys * p.kv_heads + kvh) * p.block_size + (t0 % p.block_size)) * D;
                 my_off = (unsigned)(elem * DT::kBytes / 16);
                 my_tok = t0;
+            } else {
+                report(p.err, kDevBlockId);  // the unit is skipped
             }
         }
     }

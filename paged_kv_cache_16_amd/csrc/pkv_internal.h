@@ -17,6 +17,14 @@ constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
 constexpr int kMaxSlots = 512;      // partial slots per segment the stream combine handles
 constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
 
+// Bits of the device error word (the PKV_DEV_* values of the C ABI).
+enum DevError : unsigned { kDevBlockId = 1u, kDevSlot = 2u, kDevContext = 4u, kDevPages = 8u };
+
+// Records a skipped device-side precondition violation (vector atomic; error paths only).
+__device__ __forceinline__ void report(unsigned* err, unsigned bit) {
+    if (err) atomicOr(err, bit);
+}
+
 struct AppendParams {
     void* k_cache;
     void* v_cache;
@@ -28,6 +36,7 @@ struct AppendParams {
     int32_t block_size;
     int32_t kv_heads;
     int32_t head_dim;
+    unsigned* err;  // device error word
 };
 
 struct DecodeParams {
@@ -64,6 +73,7 @@ struct DecodeParams {
     int32_t chunk_min;     // minimum units per wave
     int32_t kmax;          // partial slots per (sequence, kv head) segment
     int32_t seg_lead;      // virtual units charged at the start of every segment (run set-up)
+    unsigned* err;         // device error word
     int32_t* seg_count;    // [B*Hkv]: partials written for the segment; 0 = final row written
     // fused decode step only: the batch's new rows ([B][Hkv][D]) and their slots ([B])
     char* k_cache_w;
@@ -92,6 +102,7 @@ struct SelectParams {
     int32_t block_size;
     int32_t k;
     int32_t recent;
+    unsigned* err;  // device error word
 };
 
 struct CombineParams {

@@ -23,6 +23,7 @@ struct SeqPlan {
 template <int MODE>
 __device__ __forceinline__ SeqPlan make_plan_len(const DecodeParams& p, int L) {
     SeqPlan sp;
+    if (L > p.len_cap) report(p.err, kDevContext);  // clamped: beyond max_context_len or the table
     L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
     sp.L = L;
     sp.e0 = 0;

@@ -93,7 +93,10 @@ __global__ __launch_bounds__(kThreads) void select_pages_kernel(SelectParams p) 
     }
     const int L = L_raw < 0 ? 0 : L_raw;
     long long n = ((long long)L + p.block_size - 1) / p.block_size;
-    if (n > p.stride) n = p.stride;
+    if (n > p.stride) {
+        if (tid == 0) report(p.err, kDevPages);  // pages past the stride are never read
+        n = p.stride;
+    }
     const int first_recent = (int)(n - p.recent > 0 ? n - p.recent : 0);
     const int want = p.k - p.recent < first_recent ? p.k - p.recent : first_recent;
     const int chunk = (first_recent + kThreads - 1) / kThreads;

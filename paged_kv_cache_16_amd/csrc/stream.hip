@@ -127,7 +127,11 @@ __device__ __forceinline__ void write_new_row(const DecodeParams& p, int r, int 
     constexpr int E = 16 / ES, R = E / 4;
     const int b = r / p.kv_heads, h = r - b * p.kv_heads;
     const int64_t slot = p.new_slots[b];
-    if (slot < 0 || slot >= p.num_slots) return;
+    if (slot < 0) return;
+    if (slot >= p.num_slots) {
+        if (h == 0 && lane == 0) report(p.err, kDevSlot);
+        return;
+    }
     const int64_t blk = slot / p.block_size;
     const int t = (int)(slot - blk * p.block_size);
     const int tau = t & 15;
@@ -420,6 +424,8 @@ void decode_stream_kernel(DecodeParams p) {
                         const size_t elem = (((size_t)phys * Hkv + kvh) * p.block_size + (t0 % p.block_size)) * D;
                         my_off = (unsigned)(elem * DT::kBytes / 16);
                         my_tok = t0;
+                    } else {
+                        report(p.err, kDevBlockId);  // the unit is skipped
                     }
                 }
             }

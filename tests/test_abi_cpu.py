@@ -137,6 +137,11 @@ def test_score_export_validation(pkv):
                 fake, fake, fake, 1, None) == 4         # the partial call exports no scores
 
 
+def test_device_errors_validation(pkv):
+    # a missing output pointer is rejected before any device call
+    assert pkv._lib.pkv_device_errors(None, 1, None) == 1
+
+
 def test_select_pages_validation(pkv):
     """paged_select_pages rejects bad shapes and limits on the host (no launch)."""
     sel = pkv._lib.paged_select_pages
