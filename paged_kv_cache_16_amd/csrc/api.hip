@@ -38,6 +38,8 @@ constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persis
 constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
+constexpr int kDirectWideUnits = 40;     // ... or this many, when there are at least kDirectWideSegments
+constexpr int kDirectWideSegments = 256; // (sequence, kv head) segments to fill the GPU with workgroups
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
 constexpr size_t kAlign = 256;
@@ -84,6 +86,7 @@ struct Plan {
     int lead = 0;       // stream path: virtual units charged at each segment start
     int unit_bytes = 0;  // K and V bytes of one 16-token unit of one kv head
     bool q8 = false;    // INT8 cache: the stream path only
+    long long segments = 0;  // (sequence, kv head) segments of the call
 };
 
 // Path selection for paged_decode_attention (the partial call always uses partitions).
@@ -92,10 +95,15 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
     const bool stream_only = (o && o->score_acc) || pl.q8;
     if (o && o->split_tokens > 0) {
         pl.path = pl.num_splits > 1 ? Plan::kPartitions : Plan::kDirect;
-    } else if (pl.units_bound <= kDirectMaxUnits && !stream_only) {
+    } else if (!stream_only && (pl.units_bound <= kDirectMaxUnits ||
+                                (pl.units_bound <= kDirectWideUnits && pl.segments >= kDirectWideSegments))) {
+        // one kernel, one workgroup per segment: short sequences, or up to kDirectWideUnits units
+        // when the segments alone fill the GPU (measured: the page-selected MHA-7B shape, 512
+        // segments of 32 units, 31.8 -> 29.5 us per step; the KV-sparse window layers, 64
+        // segments of 33 units, are faster on the work-split path)
         pl.path = Plan::kDirect;
         pl.num_splits = 1;
-        pl.units_per_split = kDirectMaxUnits;
+        pl.units_per_split = pl.units_bound <= kDirectMaxUnits ? kDirectMaxUnits : kDirectWideUnits;
     } else {
         pl.path = Plan::kStream;
         // at least kStreamChunkMin units per wave, and few enough slots per segment for
@@ -159,6 +167,7 @@ Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_
                const pkv_decode_opts* o) {
     Plan pl;
     pl.q8 = d->dtype == PKV_I8;
+    pl.segments = (long long)batch * d->num_kv_heads;
     pl.unit_bytes = 2 * 16 * (d->head_dim * elem_bytes(d->dtype) + (pl.q8 ? 4 : 0));
     const int P = d->block_size;
     long long cap = max_context_len;

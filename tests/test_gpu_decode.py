@@ -219,6 +219,48 @@ def test_batches_beyond_64(B, mode, fused):
     assert_close(c, got, ref, f"batch {B} {mode}")
 
 
+# ---------------------------------------------------------------------------- one-kernel path, many segments
+@pytest.mark.parametrize("mode,fused", [("full", False), ("window", True), ("pages", False), ("full", True)])
+def test_direct_path_many_segments(mode, fused):
+    """256 (sequence, kv head) segments of at most 40 units take the one-kernel path (no workspace):
+    every sequence against the oracle, lengths 0..640 (up to 40 units)."""
+    import paged_kv_cache_16_amd as pkv
+    B, Hkv, G = 64, 4, 2
+    rng = np.random.default_rng(77 + len(mode))
+    lens = [int(x) for x in rng.integers(0, 641, size=B)]
+    lens[5] = 0
+    lens[9] = 640
+    log(f"direct path {mode} fused={fused} sum(L)={sum(lens)}")
+    c = make_case(77, B=B, Hq=G * Hkv, Hkv=Hkv, d=128, dtype="bf16", P=32, lens=lens)
+    okw, gkw = {}, {}
+    if mode == "window":
+        okw, gkw = dict(window=200, sinks=5), dict(window=200, num_sinks=5)
+    elif mode == "pages":
+        pl = np.full((B, 6), -1, np.int32)
+        for b, L in enumerate(lens):
+            npg = (L + 31) // 32
+            if npg:
+                pick = sorted(rng.choice(npg, size=min(6, npg), replace=False).tolist())
+                pl[b, :len(pick)] = pick
+        okw = dict(page_list=pl)
+        gkw = dict(page_list=torch.as_tensor(pl).cuda())
+    assert pkv.workspace_size(c.gk, B, G * Hkv, max(lens), window=gkw.get("window", 0),
+                              num_sinks=gkw.get("num_sinks", 0), page_list=gkw.get("page_list")) == 0
+    ref = oracle_attend(c, **okw)
+    if not fused:
+        got = gpu_attend(c, **{k: v for k, v in gkw.items() if k != "page_list"}, page_list=okw.get("page_list"))
+    else:
+        slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) if L else -1 for b, L in enumerate(lens)],
+                             dtype=torch.int32).cuda()
+        kn = torch.stack([c.K[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+        vn = torch.stack([c.V[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+        out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
+                                                     max_context_len=max(lens), **gkw)
+        torch.cuda.synchronize()
+        got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    assert_close(c, got, ref, f"direct {mode}")
+
+
 # ---------------------------------------------------------------------------- special cases
 def test_empty_and_single_token():
     c = make_case(40, B=3, Hq=4, Hkv=1, d=128, dtype="bf16", P=16, lens=[0, 1, 0])
