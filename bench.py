@@ -32,16 +32,19 @@ METRIC = "paged decode-attention KV GB/s and % of HBM peak; decode steps/s per l
 HBM_PEAK_GBS = 8000.0
 
 
+# The sources that define the measured kernel and its launch (grid, split plan): a change to
+# any of them invalidates the committed HBM counters.
+KERNEL_SOURCES = ("api.hip", "pkv_device.h", "pkv_internal.h", "pkv_plan.h", "stream.hip")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources of the library (names and contents, sorted by name)."""
-    import glob
+    """sha256 over KERNEL_SOURCES (names and contents, in that order)."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_16_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")),
-                    key=os.path.basename):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 

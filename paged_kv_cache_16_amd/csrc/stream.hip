@@ -266,7 +266,7 @@ void decode_stream_kernel(DecodeParams p) {
     const int f_begin = wave * C;
     const int f_end = (long long)f_begin + C < N ? f_begin + C : N;
 
-    // Locate the first unit: the sequence whose units (times Hkv) cover flat index f_begin.
+    // Locate the first position: the sequence whose flat positions (times Hkv) cover f_begin.
     UnitPos pos = {B, 0, 0, 0};
     {
         int cum = 0;
