@@ -524,7 +524,7 @@ def run_page_selected(w, args, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU; the decode path shards by kv head or by "
+        print("bench.py measures one GPU; the decode path shards by kv head or by "
               "sequence with no exchange (see the design notes), and multi-GPU runs are not "
               "part of it. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
