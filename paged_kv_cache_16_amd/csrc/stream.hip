@@ -554,7 +554,7 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     // the slots past the count are dropped by selection (their contents are stale, never
     // multiplied in). The first batch is requested before the count and the context length
     // arrive, so that the three loads share one round trip.
-    constexpr int KB = 16;
+    constexpr int KB = 8;  // one wave per SIMD leaves at most ~7 pieces per segment at 4k contexts
     float lv[KB], mv[KB], v[KB][PER];
     auto fetch = [&](int k) {
 #pragma unroll
