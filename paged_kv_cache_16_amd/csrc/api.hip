@@ -361,7 +361,8 @@ struct FusedAppend {
 };
 
 // paged_decode_attention, optionally preceded by the append of one new token per sequence
-// (fused into the persistent kernel on its path, a separate append launch otherwise).
+// (fused into the attention kernel on the persistent and one-kernel paths, a separate
+// append launch on the partition path and for INT8 caches).
 pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache, const void* q,
                        const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
@@ -446,7 +447,15 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.l_part = (float*)((char*)workspace + wl.l_off);
     }
 
-    const bool fuse = fa && pl.path == Plan::kStream && desc->dtype != PKV_I8;
+    const bool fuse = fa && pl.path != Plan::kPartitions && desc->dtype != PKV_I8;
+    if (fuse) {
+        p.k_cache_w = (char*)fa->k_cache;
+        p.v_cache_w = (char*)fa->v_cache;
+        p.k_new = (const char*)fa->k_new;
+        p.v_new = (const char*)fa->v_new;
+        p.new_slots = fa->slots;
+        p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
+    }
     if (fa && !fuse) {  // separate append launch ahead of attention
         AppendParams ap;
         ap.err = p.err;
@@ -470,14 +479,6 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         return st;
     }
     if (pl.path == Plan::kStream) {
-        if (fuse) {
-            p.k_cache_w = (char*)fa->k_cache;
-            p.v_cache_w = (char*)fa->v_cache;
-            p.k_new = (const char*)fa->k_new;
-            p.v_new = (const char*)fa->v_new;
-            p.new_slots = fa->slots;
-            p.num_slots = (int64_t)desc->num_blocks * desc->block_size;
-        }
         return hip_status(
             launch_decode_stream(kdt(desc), desc->head_dim, pl.mode, fuse, scores, p, s, ev0, ev1));
     }

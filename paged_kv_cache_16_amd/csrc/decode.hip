@@ -64,9 +64,13 @@ __device__ __forceinline__ void load_unit(const DecodeParams& p, UnitBuf<DT, D>&
     }
 }
 
-template <class DT, int D, int MODE, bool DIRECT>
+// FUSED (one-kernel path only): the step's new token enters attention from k_new/v_new,
+// patched into the tile that holds position L-1, and the workgroup stores it to the cache
+// after its own reads; no other workgroup reads that (sequence, kv head) row.
+template <class DT, int D, int MODE, bool DIRECT, bool FUSED>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeParams p) {
+    static_assert(DIRECT || !FUSED, "the fused append needs the whole sequence in one workgroup");
     using T = Tile<DT, D / (4 * DT::kE)>;
     constexpr int NC = D / (4 * DT::kE);
     constexpr int NACC = T::kAcc;
@@ -80,12 +84,15 @@ void decode_split_kernel(DecodeParams p) {
     const int j = lane >> 4, c = lane & 15;
     const int G = p.group;
 
-    const SeqPlan sp = make_plan<MODE>(p, b);
+    const int L_b = p.context_lens[b];
+    const SeqPlan sp = make_plan_len<MODE>(p, L_b);
     const int u_begin = split * p.units_per_split;
     int u_end = u_begin + p.units_per_split;
     if (u_end > sp.n_units) u_end = sp.n_units;
 
     if (u_begin >= u_end) {  // empty partition
+        if constexpr (FUSED)
+            if (w == kWaves - 1) write_new_row<DT::kBytes, D>(p, b * p.kv_heads + kvh, lane);
         if (DIRECT) {
             for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
                 const int g = idx / D, x = idx - g * D;
@@ -137,9 +144,18 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int a = 0; a < NACC; ++a) acc[a] = zero4();
 
+    NewRow<DT, D> nrow;
+    // the token this step appends (past every attended unit when the length was clamped)
+    const int t_new = L_b - 1;
+    if constexpr (FUSED) load_new_row<DT, D>(p, nrow, b, kvh, j, c);
+
     const float qk_scale = p.qk_scale_log2;
     const bool upper = c >= 8;
     auto process = [&](UnitBuf<DT, D>& X, UnitBuf<DT, D>& Y) __attribute__((always_inline)) {
+        if constexpr (FUSED) {
+            if ((unsigned)(t_new - X.t0) < 16u) patch_tile<DT, D>(X.k, X.v, nrow, t_new - X.t0, j, c);
+            if ((unsigned)(t_new - Y.t0) < 16u) patch_tile<DT, D>(Y.k, Y.v, nrow, t_new - Y.t0, j, c);
+        }
         f32x4 s0 = zero4(), s1 = zero4();
         T::qk(s0, X.k, q);
         T::qk(s1, Y.k, q);
@@ -204,6 +220,9 @@ void decode_split_kernel(DecodeParams p) {
         for (int a = 0; a < NACC; ++a) *reinterpret_cast<f32x4*>(&s_o[w][head][T::acc_dim(a, j, c)]) = acc[a];
     }
     __syncthreads();
+    // every wave's loads have returned: the segment's row can take the new token
+    if constexpr (FUSED)
+        if (w == kWaves - 1) write_new_row<DT::kBytes, D>(p, b * p.kv_heads + kvh, lane);
 
     for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
         const int g = idx / D, x = idx - g * D;
@@ -267,10 +286,15 @@ template <class DT, int D, int MODE>
 static hipError_t launch_decode_t(bool direct, const DecodeParams& p, int batch, hipStream_t s) {
     const dim3 grid((unsigned)p.num_splits, (unsigned)p.kv_heads, (unsigned)batch);
     const dim3 block(64 * kWaves);
-    if (direct)
-        decode_split_kernel<DT, D, MODE, true><<<grid, block, 0, s>>>(p);
-    else
-        decode_split_kernel<DT, D, MODE, false><<<grid, block, 0, s>>>(p);
+    if (direct && p.new_slots) {
+        if (p.num_splits != 1) return hipErrorInvalidValue;
+        decode_split_kernel<DT, D, MODE, true, true><<<grid, block, 0, s>>>(p);
+    } else if (direct) {
+        decode_split_kernel<DT, D, MODE, true, false><<<grid, block, 0, s>>>(p);
+    } else {
+        if (p.new_slots) return hipErrorInvalidValue;
+        decode_split_kernel<DT, D, MODE, false, false><<<grid, block, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

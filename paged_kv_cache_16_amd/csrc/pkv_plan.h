@@ -106,4 +106,104 @@ __device__ __forceinline__ void store_out(void* out, int out_dtype, size_t idx, 
     }
 }
 
+// Fused append ----------------------------------------------------------------------------
+
+// Cache write of the fused decode step, one new row (sequence b, kv head h) per call: stored
+// at slot new_slots[b] in the cache's lane-chunk order. It runs after every read of that
+// (sequence, kv head) row set has returned (in the combine kernel on the persistent path, at
+// the end of the segment's own workgroup on the one-kernel path); attention takes the new
+// token from k_new/v_new directly.
+template <int ES, int D>
+__device__ __forceinline__ void write_new_row(const DecodeParams& p, int r, int lane) {
+    constexpr int E = 16 / ES, R = E / 4;
+    const int b = r / p.kv_heads, h = r - b * p.kv_heads;
+    const int64_t slot = p.new_slots[b];
+    if (slot < 0) return;
+    if (slot >= p.num_slots) {
+        if (h == 0 && lane == 0) report(p.err, kDevSlot);
+        return;
+    }
+    const int64_t blk = slot / p.block_size;
+    const int t = (int)(slot - blk * p.block_size);
+    const int tau = t & 15;
+    const size_t sub = (((size_t)blk * p.kv_heads + h) * p.block_size + (t - tau)) * D;
+    const size_t src = (size_t)r * D;
+    if (lane < D / E) {  // K: one whole 16-byte chunk per lane
+        const size_t chunk = (size_t)(lane >> 2) * 64 + (size_t)(lane & 3) * 16 + tau;
+        *reinterpret_cast<u32x4*>(p.k_cache_w + (sub + chunk * E) * ES) = load16(p.k_new + (src + lane * E) * ES);
+    }
+    for (int x = lane; x < D; x += 64) {  // V: element by element
+        const int n = x >> 4;
+        const size_t chunk = ((size_t)(n / R) * 4 + (tau >> 2)) * 16 + (x & 15);
+        const size_t pos = (size_t)(n % R) * 4 + (tau & 3);
+        if constexpr (ES == 2)
+            *reinterpret_cast<unsigned short*>(p.v_cache_w + (sub + chunk * E + pos) * 2) =
+                *reinterpret_cast<const unsigned short*>(p.v_new + (src + x) * 2);
+        else
+            *reinterpret_cast<unsigned*>(p.v_cache_w + (sub + chunk * E + pos) * 4) =
+                *reinterpret_cast<const unsigned*>(p.v_new + (src + x) * 4);
+    }
+}
+
+// The new token's values as lane (j, c) holds them in a tile: K chunks of token c (dims
+// kk*4E + j*E ..), and the V elements of dims 16n + c. Loaded once per run of the fused step.
+template <class DT, int D>
+struct NewRow {
+    static constexpr int NC = D / (4 * DT::kE);
+    static constexpr int NV = D / 16;  // V dims 16n + c, n < D/16
+    u32x4 k[NC];
+    unsigned v[NV];  // raw element bits (low 16 bits for 2-byte types)
+};
+
+template <class DT, int D>
+__device__ __forceinline__ void load_new_row(const DecodeParams& p, NewRow<DT, D>& nr, int b, int kvh, int j,
+                                             int c) {
+    constexpr int E = DT::kE, ES = DT::kBytes;
+    const size_t src = ((size_t)b * p.kv_heads + kvh) * D;
+#pragma unroll
+    for (int kk = 0; kk < NewRow<DT, D>::NC; ++kk) nr.k[kk] = load16(p.k_new + (src + kk * 4 * E + j * E) * ES);
+#pragma unroll
+    for (int n = 0; n < NewRow<DT, D>::NV; ++n) {
+        if constexpr (ES == 2)
+            nr.v[n] = *reinterpret_cast<const unsigned short*>(p.v_new + (src + 16 * n + c) * 2);
+        else
+            nr.v[n] = *reinterpret_cast<const unsigned*>(p.v_new + (src + 16 * n + c) * 4);
+    }
+}
+
+// Replaces token tau of a loaded tile by the new row (lanes that hold it).
+template <class DT, int D>
+__device__ __forceinline__ void patch_tile(u32x4 (&k)[D / (4 * DT::kE)], u32x4 (&v)[D / (4 * DT::kE)],
+                                          const NewRow<DT, D>& nr, int tau, int j, int c) {
+    constexpr int NC = D / (4 * DT::kE);
+    constexpr int R = DT::kE / 4;
+    if (c == tau) {
+#pragma unroll
+        for (int kk = 0; kk < NC; ++kk) k[kk] = nr.k[kk];
+    }
+    if (j == (tau >> 2)) {
+        const int i = tau & 3;
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+            // token 4j+i of dim 16n + c is element (n % R) * 4 + i of chunk n / R
+            if constexpr (DT::kBytes == 2) {
+                const int target = (n % R) * 2 + (i >> 1);  // dword holding the element
+                // one byte permute puts the element's two bytes in the high or low half of the
+                // dword (bytes 0-3 select from wd, 4-7 from the new row); nothing here depends
+                // on the new row alone, so its loads are not waited for before the tile is
+                const unsigned sel = (i & 1) ? 0x05040100u : 0x03020504u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const unsigned wd = v[n / R][w];
+                    const unsigned upd = __builtin_amdgcn_perm(nr.v[n], wd, sel);
+                    v[n / R][w] = w == target ? upd : wd;
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[n][w] = w == i ? nr.v[n] : v[n][w];
+            }
+        }
+    }
+}
+
 }  // namespace pkv

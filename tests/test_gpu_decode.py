@@ -469,8 +469,19 @@ FUSED_CASES = [
          kw=dict(window=512, num_sinks=4)),
     dict(name="f16-pages", B=2, Hq=8, Hkv=8, d=128, dtype="f16", P=32, lens=[1000, 64], kw="pages"),
     dict(name="f32-d64", B=2, Hq=4, Hkv=4, d=64, dtype="f32", P=16, lens=[300, 45], kw={}),
-    dict(name="tiny-direct", B=2, Hq=4, Hkv=2, d=128, dtype="bf16", P=16, lens=[100, 7], kw={}),
+    dict(name="tiny-direct", B=2, Hq=4, Hkv=2, d=128, dtype="bf16", P=16, lens=[100, 7], kw={}, direct=True),
     dict(name="partitions", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", P=16, lens=[900, 333], kw=dict(split_tokens=128)),
+    # one-kernel path: the workgroup of each (sequence, kv head) patches the new token in and writes it
+    dict(name="direct-window", B=3, Hq=8, Hkv=2, d=128, dtype="bf16", P=16, lens=[300, 50, 1],
+         kw=dict(window=64, num_sinks=4), direct=True),
+    dict(name="direct-pages", B=2, Hq=8, Hkv=8, d=128, dtype="f16", P=32, lens=[1000, 64], kw=dict(pages=2),
+         direct=True),
+    dict(name="direct-pages-no-newest", B=2, Hq=8, Hkv=8, d=128, dtype="f16", P=32, lens=[1000, 70],
+         kw=dict(pages=2, newest=False), direct=True),
+    dict(name="direct-wide-pages", B=64, Hq=8, Hkv=4, d=128, dtype="f16", P=32,
+         lens=[int(x) for x in np.random.default_rng(61).integers(1, 900, size=64)], kw=dict(pages=6), direct=True),
+    dict(name="direct-wide-f32-d64", B=64, Hq=4, Hkv=4, d=64, dtype="f32", P=16,
+         lens=[int(x) for x in np.random.default_rng(62).integers(1, 640, size=64)], kw={}, direct=True),
 ]
 
 
@@ -493,12 +504,21 @@ def test_fused_append_attention(fc):
     kn = torch.stack([c.K[b, L - 1] for b, L in enumerate(lens)]).cuda()
     vn = torch.stack([c.V[b, L - 1] for b, L in enumerate(lens)]).cuda()
     kw, okw = fc["kw"], {}
-    if kw == "pages":
-        pl = synth.page_lists(lens, c.P, 6, 60).numpy()
+    if kw == "pages" or "pages" in kw:
+        npages = 6 if kw == "pages" else kw["pages"]
+        if kw == "pages" or kw.get("newest", True):
+            pl = synth.page_lists(lens, c.P, npages, 60).numpy()
+        else:  # earlier pages only: the new token is written but not attended
+            pl = synth.page_lists([max(L - c.P, 1) for L in lens], c.P, npages, 60).numpy()
+            assert all((pl[b] < (L - 1) // c.P).all() for b, L in enumerate(lens))
         kw = dict(page_list=torch.as_tensor(pl).cuda())
         okw = dict(page_list=pl)
     elif "window" in kw:
         okw = dict(window=kw["window"], sinks=kw["num_sinks"])
+    if "direct" in fc:  # the path this case is meant to take (the one-kernel path needs no workspace)
+        n_ws = pkv.workspace_size(c.gk, fc["B"], fc["Hq"], max(lens), window=kw.get("window", 0),
+                                  num_sinks=kw.get("num_sinks", 0), page_list=kw.get("page_list"))
+        assert (n_ws == 0) == fc["direct"], n_ws
     out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
                                                  max_context_len=max(lens), **kw)
     torch.cuda.synchronize()
