@@ -169,8 +169,7 @@ void decode_split_kernel(DecodeParams p) {
             x1[i] = (keep1 >> i) & 1 ? s1[i] * qk_scale : kNegInf;
             mx = fmaxf(mx, fmaxf(x0[i], x1[i]));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = xor32_max(xor16_max(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == kNegInf ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -208,8 +207,7 @@ void decode_split_kernel(DecodeParams p) {
     }
 
     // The 4 lanes of one column hold partial sums of the same head under the same max.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = xor32_sum(xor16_sum(l_run));
     const int head = T::acc_head(c);
     if (j == 0 && c < 8 && head < G) {
         s_m[w][head] = m_run;

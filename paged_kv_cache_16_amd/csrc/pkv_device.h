@@ -112,6 +112,44 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Cross-lane steps on the VALU (no trip through the LDS crossbar, which __shfl takes). Callers
+// run them with all 64 lanes active.
+// xor-16 / xor-32 reductions: the gfx950 permlane swaps exchange 16-lane rows (odd rows of one
+// copy with even rows of the other) or wave halves, so combining the two swapped copies gives
+// every lane op(x[l], x[l ^ 16]) or op(x[l], x[l ^ 32]).
+__device__ __forceinline__ float xor32_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the wave with DPP: shifts by 1, 2, 4 and 8 lanes inside each
+// 16-lane row (lanes shifted in from outside the row add 0), then the last lane of row 0 is
+// added to row 1 and that of row 2 to row 3 (row_bcast:15 under row mask 0b1010), and lane 31,
+// by then the total of rows 0-1, to rows 2 and 3 (row_bcast:31 under row mask 0b1100).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+// Sum over the wave (uniform).
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
 // Packs two fp32 values into bf16 (round to nearest even, hardware conversion).
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;

@@ -102,6 +102,7 @@ struct SelectParams {
     int32_t block_size;
     int32_t k;
     int32_t recent;
+    int32_t stage_pages;  // pages per LDS staging chunk (a multiple of 4), 0 = unstaged loads
     unsigned* err;  // device error word
 };
 
@@ -128,6 +129,6 @@ int stream_blocks_per_cu(int dtype, int head_dim, int mode);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, hipStream_t s);
 constexpr int kSelectMaxK = 64;
-constexpr int kSelectMaxPages = 15360;  // page weights held in LDS (60 KiB)
+constexpr int kSelectMaxPages = 15360;  // page keys held in LDS (60 KiB)
 
 }  // namespace pkv

@@ -21,37 +21,6 @@
 
 namespace pkv {
 
-__device__ __forceinline__ float xor32_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_max(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
-    return v;
-}
-
 template <int MODE>
 __device__ __forceinline__ int seq_units(const DecodeParams& p, int b) {
     return make_plan<MODE>(p, b).n_units;
@@ -156,7 +125,7 @@ void decode_stream_kernel(DecodeParams p) {
     // sequences' inclusive scan gives their total and also serves the search for the wave's
     // first position.
     const int nu_lane = lane < B ? flat_of(make_plan_len<MODE>(p, L_lane).n_units) : 0;
-    const int incl_lane = wave_incl_scan(nu_lane * Hkv, lane);
+    const int incl_lane = wave_incl_scan(nu_lane * Hkv);
     int N = __builtin_amdgcn_readlane(incl_lane, 63);
     for (int b0 = 64; b0 < B; b0 += 64) {
         const int b = b0 + lane;
@@ -176,7 +145,7 @@ void decode_stream_kernel(DecodeParams p) {
         for (int b0 = 0; b0 < B; b0 += 64) {
             const int b = b0 + lane;
             const int nu = b0 == 0 ? nu_lane : (b < B ? flat_of(seq_units<MODE>(p, b)) : 0);
-            const int incl = b0 == 0 ? incl_lane : wave_incl_scan(nu * Hkv, lane);
+            const int incl = b0 == 0 ? incl_lane : wave_incl_scan(nu * Hkv);
             const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
             if (cum + chunk_total > f_begin) {
                 const unsigned long long hit = __ballot(cum + incl > f_begin);

@@ -77,6 +77,33 @@ def test_select_full_size(shape):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("case", ["stride-not-multiple-of-4", "staged-in-chunks", "unaligned-base", "one-head"])
+def test_select_load_paths(case):
+    """Both ways of reading the weights give the oracle's lists: rows staged in LDS with
+    16-byte loads (stride a multiple of 4, 16-byte aligned array; in several chunks when the
+    heads' rows exceed the LDS), and 4-byte loads otherwise."""
+    import paged_kv_cache_16_amd as pkv
+    rng = np.random.default_rng(410 + len(case))
+    B, P, k = 5, 16, 24
+    H = {"staged-in-chunks": 64, "one-head": 1}.get(case, 8)
+    lens = rng.integers(1, 1500 * P, size=B)
+    n = int((lens.max() + P - 1) // P)
+    stride = n + (-n) % 4 + (1 if case == "stride-not-multiple-of-4" else 0)
+    assert (stride % 4 != 0) == (case == "stride-not-multiple-of-4")
+    sc = (rng.integers(0, 7, size=(B, H, stride)) * 0.5).astype(np.float32)  # many ties
+    ref = oracle.select_pages(sc, lens, P=P, k=k, recent=2)
+    if case == "unaligned-base":
+        flat = torch.zeros(B * H * stride + 1, dtype=torch.float32, device="cuda")
+        flat[1:] = torch.as_tensor(sc).reshape(-1).cuda()
+        g = flat[1:].view(B, H, stride)
+        assert g.data_ptr() % 16 != 0
+    else:
+        g = torch.as_tensor(sc).cuda().contiguous()
+    out = pkv.select_pages(g, torch.as_tensor(lens.astype(np.int32)).cuda(), block_size=P, k=k, recent=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("block", [16, 32, 5])
 def test_score_export_per_page(block):
     import paged_kv_cache_16_amd as pkv
