@@ -102,7 +102,36 @@ def parse():
                          "this (8: 1 kv head, 4 query heads); 16 replicas so the MALL cannot serve repeats")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter calibration)")
+    ap.add_argument("--read-probe-mib", type=int, default=2048,
+                    help="after the timed region, time the library's read-rate probe over this many MiB "
+                         "(0: skip); the roofline then also gives achieved / probe")
     return ap.parse_args()
+
+
+def read_probe_gbs(mib: int, dev) -> dict:
+    """Best rate of pkv_read_probe (16-byte nontemporal loads, every wave on its own contiguous
+    share) over a buffer far larger than the last-level cache, at 1, 2 and 4 waves per SIMD."""
+    import torch
+    import paged_kv_cache_16_amd as pkv
+    buf = torch.zeros(mib << 20, dtype=torch.uint8, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(cus * 4 * 4, dtype=torch.int32, device=dev)
+    best = (0.0, 0)
+    for wps in (1, 2, 4):
+        nbytes = 0
+        for _ in range(3):
+            nbytes = pkv.read_probe(buf, wps, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            pkv.read_probe(buf, wps, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        best = max(best, (gbs, wps))
+    del buf, sink
+    return {"gbs": round(best[0], 1), "waves_per_simd": best[1], "mib": mib}
 
 
 class HipEvents:
@@ -612,6 +641,7 @@ def main():
     q = lambda f: kern_ms[min(len(kern_ms) - 1, int(f * len(kern_ms)))]
     achieved = kv_bytes / (kern_mean * 1e-3) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    probe = read_probe_gbs(args.read_probe_mib, dev) if args.read_probe_mib > 0 else None
 
     res = {
         "metric": METRIC,
@@ -655,6 +685,9 @@ def main():
             "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
             "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
             "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),
+            "read_probe_gbs": probe["gbs"] if probe else None,
+            "frac_of_read_probe": round(achieved / probe["gbs"], 4) if probe else None,
+            "read_probe": probe,
         },
     }
     if args.cpu_seconds > 0 and not args.kv_dtype and not variant:

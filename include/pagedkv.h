@@ -439,6 +439,21 @@ enum { PKV_DEV_BLOCK_ID = 1, PKV_DEV_SLOT = 2, PKV_DEV_CONTEXT = 4, PKV_DEV_PAGE
  * may set bits between the read and the clear. Errors: PKV_ERR_NULL, PKV_ERR_HIP. */
 pkv_status pkv_device_errors(uint32_t* flags /* host */, int32_t clear, void* stream);
 
+/* Measurement helper: the achievable HBM read rate that the attention kernel's rate is
+ * compared with ([primer] §7.1: a decode step reads the whole KV cache, so bandwidth bounds
+ * it). Launches one kernel in which each of cus * 4 * waves_per_simd wavefronts streams its own
+ * contiguous share of buf with 16-byte nontemporal loads (the attention kernel's load form)
+ * and discards the bytes; time it with events on `stream`.
+ *   buf, bytes:      the buffer to read (device); each wave reads bytes / waves rounded down
+ *                    to a multiple of 8 KiB, so *bytes_read (host) <= bytes is what is read.
+ *   waves_per_simd:  1..8.
+ *   sink:            [sink_len] uint32, sink_len >= cus * 4 * waves_per_simd; written only for
+ *                    one value pattern of the data (it keeps the loads from being optimised out).
+ * Errors: PKV_ERR_NULL; PKV_ERR_SHAPE (waves_per_simd out of range, under 8 KiB per wave, sink
+ * too short); PKV_ERR_HIP. */
+pkv_status pkv_read_probe(const void* buf, size_t bytes, int32_t waves_per_simd, uint32_t* sink,
+                          size_t sink_len, size_t* bytes_read /* host */, void* stream);
+
 /* KV-cache size in bytes by the formula of [primer] §3.1,
  *   2 x batch x layers x kv_heads x head_dim x seq_len x dtype_bytes,
  * with seq_len rounded up to a multiple of block_size when block_size > 0 (a paged

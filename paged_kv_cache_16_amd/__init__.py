@@ -106,6 +106,8 @@ _lib.pkv_bm_blocks_in_use.restype = _i64
 _lib.pkv_bm_blocks_in_use.argtypes = [_vp, _i32]
 _lib.pkv_device_errors.restype = ctypes.c_int
 _lib.pkv_device_errors.argtypes = [_vp, _i32, _vp]
+_lib.pkv_read_probe.restype = ctypes.c_int
+_lib.pkv_read_probe.argtypes = [_vp, ctypes.c_size_t, _i32, _vp, ctypes.c_size_t, _vp, _vp]
 _lib.pkv_status_string.restype = ctypes.c_char_p
 _lib.pkv_status_string.argtypes = [ctypes.c_int]
 
@@ -454,6 +456,19 @@ def device_errors(clear: bool = True, stream=None) -> int:
     st = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
     _check("pkv_device_errors", _lib.pkv_device_errors(ctypes.byref(flags), 1 if clear else 0, st))
     return int(flags.value)
+
+
+def read_probe(buf, waves_per_simd: int, sink) -> int:
+    """Enqueues the read-rate probe over the device tensor `buf` on torch's current stream
+    (sink: a device int32/uint32 tensor of at least CUs * 4 * waves_per_simd entries); returns
+    the number of bytes the launch reads."""
+    if not buf.is_cuda or not sink.is_cuda or sink.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("buf and sink must be device tensors, sink 32-bit")
+    n = ctypes.c_size_t(0)
+    _check("pkv_read_probe", _lib.pkv_read_probe(
+        ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), int(waves_per_simd),
+        ctypes.c_void_p(sink.data_ptr()), sink.numel(), ctypes.byref(n), _stream(buf)))
+    return int(n.value)
 
 
 def kv_cache_bytes(batch, layers, kv_heads, head_dim, seq_len, dtype_bytes, block_size=0) -> int:

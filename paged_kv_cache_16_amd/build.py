@@ -1,6 +1,6 @@
 """Builds libpagedkv.so (HIP, gfx950) in-tree with hipcc.
 
-Run as ``python -m paged_kv_cache_16_amd.build`` or through ``__graft_entry__.build()``.
+Run as ``python paged_kv_cache_16_amd/build.py`` or through ``__graft_entry__.build()``.
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["append.hip", "decode.hip", "stream.hip", "select.hip", "api.hip"]
+SOURCES = ["append.hip", "decode.hip", "stream.hip", "select.hip", "api.hip", "probe.hip"]
 HOST_SOURCES = ["blocks.cpp"]  # host-only C++ (the block manager), built with the host compiler
 CXX = os.environ.get("CXX", "g++")
 CFLAGS = [

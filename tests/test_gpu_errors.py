@@ -93,3 +93,23 @@ def test_select_pages_beyond_stride():
     cl = torch.tensor([16 * 10, 16 * 12], dtype=torch.int32, device="cuda")  # sequence 1: 12 pages > 10
     pkv.select_pages(scores, cl, block_size=16, k=4)
     assert pkv.device_errors() == pkv.DEV_PAGES
+
+
+def test_read_probe():
+    """The read-rate probe reads whole 8 KiB steps per wave, never past the buffer, and rejects a
+    short sink or too small a buffer before launching."""
+    import paged_kv_cache_16_amd as pkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros((64 << 20) + 4096, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(cus * 4 * 2, dtype=torch.int32, device="cuda")
+    n = pkv.read_probe(buf, 2, sink)
+    torch.cuda.synchronize()
+    waves = cus * 4 * 2
+    assert n == (buf.numel() // waves) // 8192 * 8192 * waves and 0 < n <= buf.numel()
+    assert int(sink.abs().sum()) == 0  # zero data never matches the sink pattern
+    with pytest.raises(pkv.PagedKVError):
+        pkv.read_probe(buf, 4, sink)  # sink shorter than the waves
+    with pytest.raises(pkv.PagedKVError):
+        pkv.read_probe(buf[: waves * 8192 - 1], 2, sink)  # under 8 KiB per wave
+    with pytest.raises(pkv.PagedKVError):
+        pkv.read_probe(buf, 0, sink)
