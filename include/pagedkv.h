@@ -31,10 +31,14 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the comment says "host". The caller owns
  *     every buffer (including workspaces); the library never allocates or frees
- *     memory and keeps no state between calls other than the device error word
- *     (pkv_device_errors), so calls are reentrant.
+ *     device memory (the host block manager's own host memory is allocated by
+ *     pkv_bm_create and freed by pkv_bm_destroy) and keeps no state between calls
+ *     other than the device error word (pkv_device_errors) and per-device
+ *     properties it asks the runtime for once (compute units, occupancy, LDS
+ *     size), so calls are reentrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
- *     enqueued asynchronously; no entry point synchronises the host.
+ *     enqueued asynchronously; no entry point other than pkv_device_errors
+ *     synchronises the host.
  *   - The return value reports host-side argument validation and launch errors
  *     only. Validation happens before anything is enqueued: on any error nothing
  *     is launched and no output is touched.

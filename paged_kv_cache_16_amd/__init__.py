@@ -23,13 +23,14 @@ __all__ = [
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
     "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks", "device_errors",
+    "read_probe",
     "PagedKVError", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_16_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_16_amd/build.py` "
                       "(hipcc, gfx950). There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/pagedkv.h"
 #include "pkv_internal.h"
 
@@ -16,19 +18,20 @@ namespace {
 using namespace pkv;
 
 // Address of the current device's error word (nullptr if it cannot be had: reports are then
-// dropped). Looked up once per device; a race between two first calls stores the same value.
-unsigned* g_err_ptr[64];
-bool g_err_known[64];
+// dropped). Looked up once per device (0 = not yet, 1 = unavailable); two first calls racing
+// store the same value.
+std::atomic<uintptr_t> g_err_word[64];
 unsigned* dev_err_word() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    if (!g_err_known[dev]) {
+    uintptr_t w = g_err_word[dev].load(std::memory_order_relaxed);
+    if (w == 0) {
         void* ptr = nullptr;
-        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_pkv_dev_errors)) != hipSuccess) ptr = nullptr;
-        g_err_ptr[dev] = static_cast<unsigned*>(ptr);
-        g_err_known[dev] = true;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_pkv_dev_errors)) != hipSuccess || !ptr) ptr = nullptr;
+        w = ptr ? (uintptr_t)ptr : 1;
+        g_err_word[dev].store(w, std::memory_order_relaxed);
     }
-    return g_err_ptr[dev];
+    return w == 1 ? nullptr : reinterpret_cast<unsigned*>(w);
 }
 
 constexpr int kTargetWorkgroups = 2048;  // ~8 resident workgroups per CU over 256 CUs
@@ -125,27 +128,30 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
     }
 }
 
+// Per-device facts asked of the runtime once (0 = not yet asked; racing first calls store
+// the same value).
 struct DeviceInfo {
-    int cus = 0;
-    int occupancy[5][2][3] = {};  // [internal dtype][head_dim 64/128][mode] workgroups per CU
+    std::atomic<int> cus{0};
+    std::atomic<int> occupancy[5][2][3] = {};  // [internal dtype][head_dim 64/128][mode] workgroups per CU
 };
 DeviceInfo g_dev[64];
 
 int device_cus(int dev) {
     if (dev < 0 || dev >= 64) return 256;
-    if (g_dev[dev].cus == 0) {
-        int n = 0;
+    int n = g_dev[dev].cus.load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        g_dev[dev].cus = n;
+        g_dev[dev].cus.store(n, std::memory_order_relaxed);
     }
-    return g_dev[dev].cus;
+    return n;
 }
 
 int device_occupancy(int dev, int dtype, int head_dim, int mode) {
-    int* slot = (dev >= 0 && dev < 64) ? &g_dev[dev].occupancy[dtype][head_dim == 128][mode] : nullptr;
-    if (slot && *slot) return *slot;
+    std::atomic<int>* slot = (dev >= 0 && dev < 64) ? &g_dev[dev].occupancy[dtype][head_dim == 128][mode] : nullptr;
+    const int known = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (known) return known;
     const int n = stream_blocks_per_cu(dtype, head_dim, mode);
-    if (slot) *slot = n;
+    if (slot) slot->store(n, std::memory_order_relaxed);
     return n;
 }
 

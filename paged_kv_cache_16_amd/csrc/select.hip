@@ -14,6 +14,8 @@
 //   3. One prefix count over the thread ranges gives, for each thread, the pages before it
 //      with key > T and with key == T; the taken pages (key > T, and the lowest-id `taken
 //      ties` of key == T) are written in ascending id order, then the newest pages and -1.
+#include <atomic>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void select_pages_kernel(SelectParams p) 
     for (int i = tid; i < p.k - want; i += kThreads) row[want + i] = i < n_new ? first_recent + i : -1;
 }
 
-int g_lds_max[64];  // per device: LDS bytes one workgroup may use (0 = not yet asked)
+std::atomic<int> g_lds_max[64];  // per device: LDS bytes one workgroup may use (0 = not yet asked)
 
 }  // namespace
 
@@ -230,14 +232,14 @@ hipError_t launch_select(const SelectParams& p, hipStream_t s) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int lds_max = dev >= 0 && dev < 64 ? g_lds_max[dev] : 0;
+    int lds_max = dev >= 0 && dev < 64 ? g_lds_max[dev].load(std::memory_order_relaxed) : 0;
     if (lds_max == 0) {
         e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute((const void*)select_pages_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 lds_max - kStaticLds);
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) g_lds_max[dev] = lds_max;
+        if (dev >= 0 && dev < 64) g_lds_max[dev].store(lds_max, std::memory_order_relaxed);
     }
     SelectParams q = p;
     const long long key_bytes = (long long)((p.stride + 3) & ~3) * 4;
