@@ -36,6 +36,37 @@ def test_append_bit_exact(dtype, P, d):
     assert np.array_equal(raw_bytes(c.gv), c.vpool.view(np.uint8))
 
 
+@pytest.mark.parametrize("P,dtype,d", [(48, "bf16", 128), (64, "f16", 64), (128, "f32", 128), (256, "bf16", 64),
+                                       (256, "f16", 128)])
+def test_block_sizes_up_to_256(P, dtype, d):
+    """Block sizes past 32, up to the largest the library takes (any multiple of 16 to 256):
+    append bit-exact, attention in every mode and on the partition path, and the fused step,
+    against the oracle."""
+    import paged_kv_cache_16_amd as pkv
+    lens = [3 * P + 5, P, 1, 0, 700]
+    log(f"block size {P} {dtype} d={d}")
+    c = make_case(33 + P, B=5, Hq=8, Hkv=2, d=d, dtype=dtype, P=P, lens=lens, spare=2)
+    assert np.array_equal(raw_bytes(c.gk), c.kpool.view(np.uint8))
+    assert np.array_equal(raw_bytes(c.gv), c.vpool.view(np.uint8))
+    assert_close(c, gpu_attend(c), oracle_attend(c), f"P={P} full")
+    assert_close(c, gpu_attend(c, split_tokens=P), oracle_attend(c), f"P={P} partitions")
+    W, S = P + 7, 3
+    assert_close(c, gpu_attend(c, window=W, num_sinks=S), oracle_attend(c, window=W, sinks=S), f"P={P} window")
+    pl = synth.page_lists(lens, P, 2, 33 + P).numpy()
+    assert_close(c, gpu_attend(c, page_list=pl), oracle_attend(c, page_list=pl), f"P={P} pages")
+    # fused step: the cache already holds every row, and row L-1 comes again from k_new/v_new
+    slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, P) if L else -1 for b, L in enumerate(lens)],
+                         dtype=torch.int32).cuda()
+    kn = torch.stack([c.K[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    vn = torch.stack([c.V[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
+                                                 max_context_len=max(lens))
+    torch.cuda.synchronize()
+    assert_close(c, (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)),
+                 oracle_attend(c), f"P={P} fused")
+    assert np.array_equal(raw_bytes(c.gk), c.kpool.view(np.uint8))
+
+
 def test_append_skips_negative_and_out_of_range_slots():
     import paged_kv_cache_16_amd as pkv
     c = make_case(32, B=1, Hq=2, Hkv=2, d=128, dtype="bf16", P=16, lens=[20], spare=2)
