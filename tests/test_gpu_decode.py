@@ -7,6 +7,8 @@ of memory outside the attended set shows up as NaN.
 """
 from __future__ import annotations
 
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 import torch
@@ -248,6 +250,58 @@ def test_batches_beyond_64(B, mode, fused):
         torch.cuda.synchronize()
         got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
     assert_close(c, got, ref, f"batch {B} {mode}")
+
+
+def test_max_batch_65535():
+    """The largest batch the library takes: 65535 sequences, almost all short and three long
+    (the longest puts the call on the persistent path), so every wave's prologue scans 1024
+    chunks of 64 lengths from memory. Attention and the fused step, every sequence against
+    the oracle."""
+    import paged_kv_cache_16_amd as pkv
+    from harness import NAN_BITS
+    B, Hq, Hkv, d, P, dt = 65535, 2, 1, 64, 16, "bf16"
+    rng = np.random.default_rng(65535)
+    lens = rng.integers(0, 24, size=B)
+    lens[[5, 40000, B - 1]] = [700, 650, 333]
+    T = int(lens.sum())
+    log(f"max batch {B}: {T} tokens")
+    K = synth.normal((T, Hkv, d), 91, "k", dtype=dt)
+    V = synth.normal((T, Hkv, d), 91, "v", dtype=dt)
+    q = synth.normal((B, Hq, d), 91, "q", dtype=dt)
+    bt, nb = synth.block_tables(lens.tolist(), P, 91, spare_blocks=1)
+    free = torch.ones(nb, dtype=torch.bool)
+    free[bt[bt >= 0].long()] = False
+    bt = torch.where(bt >= 0, bt, torch.full_like(bt, int(free.nonzero()[0])))
+    slots = synth.token_slots(bt, lens.tolist(), P)
+    n_el = nb * Hkv * P * d
+    kpool = np.full(n_el, NAN_BITS[dt], dtype=np.uint16)
+    vpool = np.full(n_el, NAN_BITS[dt], dtype=np.uint16)
+    oracle.kv_append(dt, kpool, vpool, synth.raw_numpy(K), synth.raw_numpy(V), slots.numpy(), P=P, Hkv=Hkv, d=d)
+    ref = oracle.decode_attention(dt, kpool, vpool, synth.raw_numpy(q), bt.numpy(), lens.astype(np.int32),
+                                  P=P, Hkv=Hkv, d=d)
+    dev = torch.device("cuda")
+    pkv.device_errors()  # start from a clear error word
+    gk = torch.full((nb, Hkv, P, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    gv = torch.full_like(gk, float("nan"))
+    pkv.kv_cache_append(gk, gv, K.to(dev), V.to(dev), slots.to(dev))
+    gq, gbt = q.to(dev), bt.to(dev)
+    gcl = torch.as_tensor(lens.astype(np.int32)).to(dev)
+    assert pkv.workspace_size(gk, B, Hq, int(lens.max())) > 0  # the persistent path
+    out, lse = pkv.paged_decode_attention(gq, gk, gv, gbt, gcl, max_context_len=int(lens.max()))
+    torch.cuda.synchronize()
+    c = SimpleNamespace(dtype=dt)
+    assert_close(c, (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)), ref,
+                 "max batch")
+    # fused step: row L-1 of every sequence again from k_new/v_new
+    last = np.cumsum(lens) - 1
+    take = torch.as_tensor(np.where(lens > 0, last, 0))
+    kn, vn = K[take].to(dev), V[take].to(dev)
+    sl = torch.as_tensor(np.where(lens > 0, slots.numpy()[np.maximum(last, 0)], -1).astype(np.int32)).to(dev)
+    out, lse = pkv.paged_decode_append_attention(gq, gk, gv, kn, vn, sl, gbt, gcl, max_context_len=int(lens.max()))
+    torch.cuda.synchronize()
+    assert_close(c, (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)), ref,
+                 "max batch fused")
+    assert pkv.device_errors() == 0
 
 
 # ---------------------------------------------------------------------------- one-kernel path, many segments
