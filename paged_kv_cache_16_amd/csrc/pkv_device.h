@@ -112,6 +112,25 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Buffer-resource loads for cache tiles. The wave-uniform tile base sits in scalar registers
+// and each lane adds a fixed 32-bit offset, so loading a tile forms no per-lane 64-bit
+// address: with global loads the compiler builds one in vector registers per tile and then
+// recycles those registers as load destinations, which makes it wait for every load in
+// flight before the next tile's loads can be issued. Offsets at or past `bytes` read as zero
+// (the resource's range check), never outside the tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+    // raw buffer (stride 0); word 3 = 32-bit data format, as gfx9 untyped loads require
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes at byte offset `voff` of the resource, nontemporal (read once).
+__device__ __forceinline__ u32x4 load16_tile_stream(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 2);
+}
+// 16 bytes at byte offset `voff` of the resource, default cache policy.
+__device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
 // Cross-lane steps on the VALU (no trip through the LDS crossbar, which __shfl takes). Callers
 // run them with all 64 lanes active.
 // xor-16 / xor-32 reductions: the gfx950 permlane swaps exchange 16-lane rows (odd rows of one

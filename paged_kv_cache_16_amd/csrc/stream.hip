@@ -66,24 +66,49 @@ template <class DT, int D>
 __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>& rb, int my_tok, unsigned my_off,
                                           int k, int n, int lane, int u_base) {
     constexpr int NC = D / (4 * DT::kE);
-    const int t0 = k < n ? __builtin_amdgcn_readlane(my_tok, k) : -1;
-    rb.t0 = t0;
-    rb.u = u_base + k;
-    if (t0 >= 0) {
-        const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
-        const char* kp = p.k_cache + off + lane * 16;
-        const char* vp = p.v_cache + off + lane * 16;
+    if constexpr (!DT::kQ8) {
+        // 2- and 4-byte caches: global loads under a branch. At the branch joins the
+        // compiler's count of loads in flight is conservative, so before a unit is processed
+        // the wave waits for all but the newest unit's loads: about one unit in flight per
+        // wave, 8 MiB over the chip at the benchmark shape. Counting exactly (the INT8 form
+        // below) keeps three units in flight and measured slower at the Llama-3-8B layer
+        // shape (step 61.7 -> 64.1 us; a 2-deep ring 63.1 us): more bytes in flight only queue.
+        const int t0 = k < n ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+        rb.t0 = t0;
+        rb.u = u_base + k;
+        if (t0 >= 0) {
+            const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
+            const char* kp = p.k_cache + off + lane * 16;
+            const char* vp = p.v_cache + off + lane * 16;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) rb.k[cc] = load16_stream(kp + cc * 1024);
+            for (int cc = 0; cc < NC; ++cc) rb.k[cc] = load16_stream(kp + cc * 1024);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) rb.v[cc] = load16_stream(vp + cc * 1024);
-        if constexpr (DT::kQ8) {
-            // scale plane after the data plane; the sub-tile's first row is off / D
-            const size_t plane = (size_t)p.num_blocks * p.kv_heads * p.block_size * D;
-            const size_t srow = off / D + 4 * (lane >> 4);
-            rb.ks = *reinterpret_cast<const f32x4*>(p.k_cache + plane + srow * 4);
-            rb.vs = *reinterpret_cast<const f32x4*>(p.v_cache + plane + srow * 4);
+            for (int cc = 0; cc < NC; ++cc) rb.v[cc] = load16_stream(vp + cc * 1024);
         }
+    } else {
+        // INT8: the loads are issued whether or not the slot holds a unit (an empty resource
+        // reads zeros and touches no memory). With no branch around them the compiler counts
+        // exactly how many loads are younger than the ones a unit waits for, and a wave keeps
+        // the whole ring in flight; the widening work per unit then hides behind the loads.
+        const bool live = k < n && __builtin_amdgcn_readlane(my_tok, k < n ? k : 0) >= 0;
+        rb.t0 = live ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+        rb.u = u_base + k;
+        const size_t off = live ? (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16 : 0;
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(p.k_cache + off, live ? NC * 1024 : 0);
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(p.v_cache + off, live ? NC * 1024 : 0);
+        const unsigned lane_off = (unsigned)lane * 16u;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) rb.k[cc] = load16_tile_stream(kr, lane_off + cc * 1024);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) rb.v[cc] = load16_tile_stream(vr, lane_off + cc * 1024);
+        // scale plane after the data plane; the sub-tile's first row is off / D, and lane
+        // (j, c) takes rows 4j .. 4j+3
+        const size_t plane = (size_t)p.num_blocks * p.kv_heads * p.block_size * D;
+        const size_t srow = off / D;
+        const __amdgpu_buffer_rsrc_t ksr = tile_rsrc(p.k_cache + plane + srow * 4, live ? 64 : 0);
+        const __amdgpu_buffer_rsrc_t vsr = tile_rsrc(p.v_cache + plane + srow * 4, live ? 64 : 0);
+        rb.ks = __builtin_bit_cast(f32x4, load16_tile(ksr, (unsigned)(lane >> 4) * 16u));
+        rb.vs = __builtin_bit_cast(f32x4, load16_tile(vsr, (unsigned)(lane >> 4) * 16u));
     }
 }
 
@@ -303,53 +328,25 @@ void decode_stream_kernel(DecodeParams p) {
                     }
                 }
             }
-            // a ring of register buffers: unit k + depth - 1 is requested right before unit k
-            // is processed (depth 4 for 2/4-byte caches; 6 for INT8, whose units are half
-            // the bytes, so that a wave keeps as many bytes in flight)
-            if constexpr (!DT::kQ8) {
-                RingBuf<DT, D> R0, R1, R2, R3;
-                ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
-                for (int k = 0; k < n; k += 4) {
-                    ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
-                    process(R0);
-                    if (k + 1 >= n) break;
-                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
-                    process(R1);
-                    if (k + 2 >= n) break;
-                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
-                    process(R2);
-                    if (k + 3 >= n) break;
-                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
-                    process(R3);
-                }
-            } else {
-                RingBuf<DT, D> R0, R1, R2, R3, R4, R5;
-                ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R3, my_tok, my_off, 3, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R4, my_tok, my_off, 4, n, lane, u0 + ub);
-                for (int k = 0; k < n; k += 6) {
-                    ring_load<DT, D>(p, R5, my_tok, my_off, k + 5, n, lane, u0 + ub);
-                    process(R0);
-                    if (k + 1 >= n) break;
-                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 6, n, lane, u0 + ub);
-                    process(R1);
-                    if (k + 2 >= n) break;
-                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 7, n, lane, u0 + ub);
-                    process(R2);
-                    if (k + 3 >= n) break;
-                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 8, n, lane, u0 + ub);
-                    process(R3);
-                    if (k + 4 >= n) break;
-                    ring_load<DT, D>(p, R3, my_tok, my_off, k + 9, n, lane, u0 + ub);
-                    process(R4);
-                    if (k + 5 >= n) break;
-                    ring_load<DT, D>(p, R4, my_tok, my_off, k + 10, n, lane, u0 + ub);
-                    process(R5);
-                }
+            // a ring of four register buffers: unit k + 3 is requested right before unit k is
+            // processed (for INT8 caches too: with their loads counted exactly, a deeper ring
+            // measured slower, as more bytes in flight per wave only queue at the memory)
+            RingBuf<DT, D> R0, R1, R2, R3;
+            ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
+            ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
+            ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
+            for (int k = 0; k < n; k += 4) {
+                ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
+                process(R0);
+                if (k + 1 >= n) break;
+                ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
+                process(R1);
+                if (k + 2 >= n) break;
+                ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
+                process(R2);
+                if (k + 3 >= n) break;
+                ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
+                process(R3);
             }
         }
 
