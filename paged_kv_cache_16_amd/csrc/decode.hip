@@ -40,28 +40,25 @@ struct UnitBuf {
     int t0;  // first logical token, -1 = no unit
 };
 
-// Issues the loads of this wave's unit number k (its descriptor sits in lane k).
+// Issues the loads of this wave's unit number k (its descriptor sits in lane k), whether or not
+// there is such a unit: an empty resource reads zeros and touches no memory. With no branch
+// around the loads the compiler counts exactly how many are younger than the ones a pair of
+// units waits for, so a wave keeps both pairs in flight (at two waves per SIMD this measured
+// faster than the conservative count a branch leaves: page-selected MHA-7B step 26.8 -> 25.9 us).
 template <class DT, int D>
 __device__ __forceinline__ void load_unit(const DecodeParams& p, UnitBuf<DT, D>& ub, int my_tok,
                                           unsigned my_off, int k, int nk, int lane) {
     constexpr int NC = D / (4 * DT::kE);
-    const int t0 = k < nk ? __builtin_amdgcn_readlane(my_tok, k) : -1;
-    ub.t0 = t0;
-    if (t0 >= 0) {
-        const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16;
-        const char* kp = p.k_cache + off + lane * 16;
-        const char* vp = p.v_cache + off + lane * 16;
+    const bool live = k < nk && __builtin_amdgcn_readlane(my_tok, k < nk ? k : 0) >= 0;
+    ub.t0 = live ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+    const size_t off = live ? (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16 : 0;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(p.k_cache + off, live ? NC * 1024 : 0);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(p.v_cache + off, live ? NC * 1024 : 0);
+    const unsigned lane_off = (unsigned)lane * 16u;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) ub.k[cc] = load16_stream(kp + cc * 1024);
+    for (int cc = 0; cc < NC; ++cc) ub.k[cc] = load16_tile_stream(kr, lane_off + cc * 1024);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) ub.v[cc] = load16_stream(vp + cc * 1024);
-    } else {
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            ub.k[cc] = u32x4{0u, 0u, 0u, 0u};
-            ub.v[cc] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
+    for (int cc = 0; cc < NC; ++cc) ub.v[cc] = load16_tile_stream(vr, lane_off + cc * 1024);
 }
 
 // FUSED (one-kernel path only): the step's new token enters attention from k_new/v_new,
@@ -193,16 +190,12 @@ void decode_split_kernel(DecodeParams p) {
     load_unit<DT, D>(p, A0, my_tok, my_off, 0, nk, lane);
     load_unit<DT, D>(p, A1, my_tok, my_off, 1, nk, lane);
     for (int k = 0; k < nk; k += 4) {
-        if (k + 2 < nk) {
-            load_unit<DT, D>(p, B0, my_tok, my_off, k + 2, nk, lane);
-            load_unit<DT, D>(p, B1, my_tok, my_off, k + 3, nk, lane);
-        }
+        load_unit<DT, D>(p, B0, my_tok, my_off, k + 2, nk, lane);
+        load_unit<DT, D>(p, B1, my_tok, my_off, k + 3, nk, lane);
         process(A0, A1);
         if (k + 2 >= nk) break;
-        if (k + 4 < nk) {
-            load_unit<DT, D>(p, A0, my_tok, my_off, k + 4, nk, lane);
-            load_unit<DT, D>(p, A1, my_tok, my_off, k + 5, nk, lane);
-        }
+        load_unit<DT, D>(p, A0, my_tok, my_off, k + 4, nk, lane);
+        load_unit<DT, D>(p, A1, my_tok, my_off, k + 5, nk, lane);
         process(B0, B1);
     }
 
