@@ -42,7 +42,7 @@ constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
 constexpr int kDirectWideUnits = 40;     // ... or this many, when there are at least kDirectWideSegments
-constexpr int kDirectWideSegments = 256; // (sequence, kv head) segments to fill the GPU with workgroups
+constexpr int kDirectWideSegments = 64;  // (sequence, kv head) segments, so no merge launch is needed
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
 constexpr size_t kAlign = 256;
@@ -101,9 +101,10 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
     } else if (!stream_only && (pl.units_bound <= kDirectMaxUnits ||
                                 (pl.units_bound <= kDirectWideUnits && pl.segments >= kDirectWideSegments))) {
         // one kernel, one workgroup per segment: short sequences, or up to kDirectWideUnits units
-        // when the segments alone fill the GPU (measured: the page-selected MHA-7B shape, 512
-        // segments of 32 units, 31.8 -> 29.5 us per step; the KV-sparse window layers, 64
-        // segments of 33 units, are faster on the work-split path)
+        // over at least kDirectWideSegments segments, where skipping the merge launch outweighs
+        // using fewer CUs (measured: the page-selected MHA-7B shape, 512 segments of 32 units,
+        // 31.8 -> 29.5 us per step; the KV-sparse window layers, 64 segments of 34 units, 32
+        // layers 1.912 -> 1.880 ms per step once the one-kernel path kept its loads in flight)
         pl.path = Plan::kDirect;
         pl.num_splits = 1;
         pl.units_per_split = pl.units_bound <= kDirectMaxUnits ? kDirectMaxUnits : kDirectWideUnits;
