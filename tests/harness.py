@@ -91,7 +91,8 @@ def max_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     both_ninf = np.isneginf(a) & np.isneginf(b)
-    diff = np.where(both_ninf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # -inf - -inf is NaN; those entries are replaced by 0 here
+        diff = np.where(both_ninf, 0.0, np.abs(a - b))
     diff = np.where(np.isnan(diff), np.inf, diff)
     return float(diff.max()) if diff.size else 0.0
 

@@ -638,6 +638,51 @@ def test_fused_append_attention(fc):
     assert_close(c, got, oracle_attend(c, **okw), f"fused {fc['name']}")
 
 
+@pytest.mark.parametrize("mode", ["full", "pages"])
+def test_graph_replay_one_kernel_fused_step(mode):
+    """The one-kernel fused step (64 segments of at most 40 units: no workspace, the append
+    inside the attention kernel) captured in a HIP graph: every replay, with eager calls in
+    between, gives the eager result bit for bit, and the eager result matches the oracle."""
+    import paged_kv_cache_16_amd as pkv
+    B, Hq, Hkv = 16, 8, 4
+    rng = np.random.default_rng(52)
+    lens = [int(x) for x in rng.integers(1, 600, size=B)]
+    c = make_case(52, B=B, Hq=Hq, Hkv=Hkv, d=128, dtype="f16", P=32, lens=lens)
+    kw, okw = {}, {}
+    if mode == "pages":
+        pl = synth.page_lists(lens, c.P, 5, 52).numpy()
+        kw, okw = dict(page_list=torch.as_tensor(pl).cuda()), dict(page_list=pl)
+    assert pkv.workspace_size(c.gk, B, Hq, max(lens), page_list=kw.get("page_list")) == 0  # one kernel
+    slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) for b, L in enumerate(lens)], dtype=torch.int32).cuda()
+    kn = torch.stack([c.K[b, L - 1] for b, L in enumerate(lens)]).cuda()
+    vn = torch.stack([c.V[b, L - 1] for b, L in enumerate(lens)]).cuda()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl, max_context_len=max(lens),
+                                          out=out, lse=lse, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    assert_close(c, (ref[0].cpu().numpy().astype(np.float64), ref[1].cpu().numpy().astype(np.float64)),
+                 oracle_attend(c, **okw), f"graph one-kernel {mode}: eager step")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {i} differs from the eager step"
+        pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens), window=100)
+        torch.cuda.synchronize()
+    assert np.array_equal(raw_bytes(c.gk), c.kpool.view(np.uint8))
+
+
 def test_graph_replay_fused_step():
     """The fused decode step captured in a HIP graph: every replay, with eager calls and
     synchronisations in between, reproduces the eager result bit for bit (the work split
