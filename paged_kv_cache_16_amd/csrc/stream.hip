@@ -112,10 +112,13 @@ __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>&
     }
 }
 
-// Score export: each wave stages the logits of its current run in 4 KiB of LDS and stores
-// them in contiguous full-wave bursts (a 16-lane store per unit cost about three times
-// as much at the benchmark shape).
-constexpr int kLgFloats = 1024;
+// Score export: each wave stages the logits of its current run in 16 KiB of LDS and stores
+// them in contiguous full-wave bursts (a 16-lane store per unit cost about three times as
+// much at the benchmark shape). 16 KiB holds a whole share at the Llama-3-8B layer shape, so
+// the stores leave at the end of the run: stores count in the same in-order counter as loads,
+// and a burst in mid-run made the next tile's wait cover it too (4 KiB: step 75.3 us, 16 KiB:
+// 70.5 us).
+constexpr int kLgFloats = 4096;
 
 template <class DT, int D, int MODE, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2)))
