@@ -71,8 +71,9 @@ __device__ __forceinline__ void ring_load(const DecodeParams& p, RingBuf<DT, D>&
         // compiler's count of loads in flight is conservative, so before a unit is processed
         // the wave waits for all but the newest unit's loads: about one unit in flight per
         // wave, 8 MiB over the chip at the benchmark shape. Counting exactly (the INT8 form
-        // below) keeps three units in flight and measured slower at the Llama-3-8B layer
-        // shape (step 61.7 -> 64.1 us; a 2-deep ring 63.1 us): more bytes in flight only queue.
+        // below) keeps the whole ring in flight and measured slower at the Llama-3-8B layer
+        // shape (step 61.7 -> 64.1 us with a 4-deep ring, 63.1 us with a 2-deep one): more
+        // bytes in flight only queue.
         const int t0 = k < n ? __builtin_amdgcn_readlane(my_tok, k) : -1;
         rb.t0 = t0;
         rb.u = u_base + k;
