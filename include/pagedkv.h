@@ -139,10 +139,12 @@ typedef struct {
  * array on every step accumulates scores over steps (the caller zeroes or decays it as its
  * policy wants). score_acc is a [batch][num_kv_heads][score_stride] fp32 device array with
  * score_stride >= ceil(min(max_context_len, max_blocks_per_seq * block_size) / B) (else
- * PKV_ERR_SHAPE). Score export always uses the work-split path; it needs split_tokens == 0
- * (else PKV_ERR_MODE) and is not available to paged_decode_attention_partial
- * (PKV_ERR_MODE). Every entry's update is made by one thread, in a fixed order: results do
- * not depend on timing.
+ * PKV_ERR_SHAPE). Score export runs in the attention kernel of the one-kernel path (the
+ * workgroup holding a (sequence, kv head) adds its scores after its own merge) or, on the
+ * work-split path, in a kernel after the merge; over a page list with 1 < B != block_size it
+ * always takes the work-split path. It needs split_tokens == 0 (else PKV_ERR_MODE) and is not
+ * available to paged_decode_attention_partial (PKV_ERR_MODE). Every entry's update is made by
+ * one thread, in a fixed order: results do not depend on timing.
  *
  * Ring block tables ([Novita] §關鍵技術 1: a layer may keep a sliding window instead of the
  * full cache, and then needs fewer blocks; [primer] §4.3). With ring_pages = R > 0 (only

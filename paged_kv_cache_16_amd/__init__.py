@@ -208,10 +208,11 @@ def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
 
 
 def workspace_size(k_cache, batch: int, num_q_heads: int, max_context_len: int, *, window=0,
-                   num_sinks=0, page_list=None, split_tokens=0, scores=False, ring_pages=0) -> int:
-    """scores: True (or the score tensor) when the calls export scores."""
+                   num_sinks=0, page_list=None, split_tokens=0, scores=False, score_block=1, ring_pages=0) -> int:
+    """scores: True (or the score tensor) when the calls export scores, with entries of
+    score_block tokens (the path, and so the size, can depend on it)."""
     desc = cache_desc(k_cache)
-    o = _opts(window, num_sinks, None, split_tokens, ring_pages=ring_pages)
+    o = _opts(window, num_sinks, None, split_tokens, score_block=score_block, ring_pages=ring_pages)
     if page_list is not None:
         o.page_list = ctypes.c_void_p(1)  # only its presence matters to the size
         o.pages_per_seq = page_list.shape[1]

@@ -40,8 +40,8 @@ constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persis
                                          // a few GB/s, so bandwidth comes from wave count)
 constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
-constexpr int kDirectMaxUnits = 8;       // at most this many units per sequence: one kernel
-constexpr int kDirectWideUnits = 40;     // ... or this many, when there are at least kDirectWideSegments
+constexpr int kDirectShortUnits = 8;     // at most this many units per sequence: one kernel
+constexpr int kDirectWideUnits = kDirectMaxUnits;  // ... or this many, with at least kDirectWideSegments
 constexpr int kDirectWideSegments = 64;  // (sequence, kv head) segments, so no merge launch is needed
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave
 constexpr int kMaxUnitsPerSplit = kMaxUnitsPerWave * kWaves;
@@ -90,15 +90,21 @@ struct Plan {
     int unit_bytes = 0;  // K and V bytes of one 16-token unit of one kv head
     bool q8 = false;    // INT8 cache: the stream path only
     long long segments = 0;  // (sequence, kv head) segments of the call
+    int block_size = 16;
 };
 
 // Path selection for paged_decode_attention (the partial call always uses partitions).
 void choose_path(Plan& pl, const pkv_decode_opts* o) {
-    // score export and INT8 caches exist on the stream path only
-    const bool stream_only = (o && o->score_acc) || pl.q8;
+    // INT8 caches take the stream path only; so does score export over a page list with
+    // entries other than single tokens or whole pages (the one-kernel path's score phase
+    // covers tokens, pages of a page list, and token ranges of full or windowed sequences)
+    const bool scores = o && o->score_acc;
+    const bool direct_scores = !scores || pl.mode != kPages || o->score_block <= 1 ||
+                               o->score_block == pl.block_size;
+    const bool stream_only = pl.q8 || !direct_scores;
     if (o && o->split_tokens > 0) {
         pl.path = pl.num_splits > 1 ? Plan::kPartitions : Plan::kDirect;
-    } else if (!stream_only && (pl.units_bound <= kDirectMaxUnits ||
+    } else if (!stream_only && (pl.units_bound <= kDirectShortUnits ||
                                 (pl.units_bound <= kDirectWideUnits && pl.segments >= kDirectWideSegments))) {
         // one kernel, one workgroup per segment: short sequences, or up to kDirectWideUnits units
         // over at least kDirectWideSegments segments, where skipping the merge launch outweighs
@@ -107,7 +113,7 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
         // layers 1.912 -> 1.880 ms per step once the one-kernel path kept its loads in flight)
         pl.path = Plan::kDirect;
         pl.num_splits = 1;
-        pl.units_per_split = pl.units_bound <= kDirectMaxUnits ? kDirectMaxUnits : kDirectWideUnits;
+        pl.units_per_split = pl.units_bound <= kDirectShortUnits ? kDirectShortUnits : kDirectWideUnits;
     } else {
         pl.path = Plan::kStream;
         // at least kStreamChunkMin units per wave, and few enough slots per segment for
@@ -174,6 +180,7 @@ Plan make_plan(const pkv_cache_desc* d, int batch, int max_context_len, int max_
                const pkv_decode_opts* o) {
     Plan pl;
     pl.q8 = d->dtype == PKV_I8;
+    pl.block_size = d->block_size;
     pl.segments = (long long)batch * d->num_kv_heads;
     pl.unit_bytes = 2 * 16 * (d->head_dim * elem_bytes(d->dtype) + (pl.q8 ? 4 : 0));
     const int P = d->block_size;
@@ -408,6 +415,12 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     if (pl.path != Plan::kDirect) {
         if (!workspace || ((uintptr_t)workspace) % kAlign != 0) return PKV_ERR_WORKSPACE;
     }
+    if (scores) {  // both paths; the stream path also takes its logit and normaliser buffers below
+        p.score = opts->score_acc;
+        p.score_stride = opts->score_stride;
+        p.units_bound = pl.units_bound;
+        p.score_block = score_block;
+    }
     if (pl.path == Plan::kStream) {
         const int G = num_q_heads / desc->num_kv_heads;
         const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim, scores, pl.units_bound);
@@ -441,10 +454,6 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         if (scores) {
             p.logits = (float*)((char*)workspace + wl.logits_off);
             p.row_lse2 = (float*)((char*)workspace + wl.lse2_off);
-            p.score = opts->score_acc;
-            p.score_stride = opts->score_stride;
-            p.units_bound = pl.units_bound;
-            p.score_block = score_block;
         }
     } else if (pl.path == Plan::kPartitions) {
         const WsLayout wl = ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim);

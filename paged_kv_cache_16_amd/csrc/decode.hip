@@ -37,7 +37,8 @@ template <class DT, int D>
 struct UnitBuf {
     static constexpr int NC = D / (4 * DT::kE);
     u32x4 k[NC], v[NC];
-    int t0;  // first logical token, -1 = no unit
+    int t0;    // first logical token, -1 = no unit
+    int slot;  // the wave's unit number (unit u_begin + w + slot * kWaves)
 };
 
 // Issues the loads of this wave's unit number k (its descriptor sits in lane k), whether or not
@@ -51,6 +52,7 @@ __device__ __forceinline__ void load_unit(const DecodeParams& p, UnitBuf<DT, D>&
     constexpr int NC = D / (4 * DT::kE);
     const bool live = k < nk && __builtin_amdgcn_readlane(my_tok, k < nk ? k : 0) >= 0;
     ub.t0 = live ? __builtin_amdgcn_readlane(my_tok, k) : -1;
+    ub.slot = k;
     const size_t off = live ? (size_t)(unsigned)__builtin_amdgcn_readlane((int)my_off, k) * 16 : 0;
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(p.k_cache + off, live ? NC * 1024 : 0);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(p.v_cache + off, live ? NC * 1024 : 0);
@@ -64,16 +66,23 @@ __device__ __forceinline__ void load_unit(const DecodeParams& p, UnitBuf<DT, D>&
 // FUSED (one-kernel path only): the step's new token enters attention from k_new/v_new,
 // patched into the tile that holds position L-1, and the workgroup stores it to the cache
 // after its own reads; no other workgroup reads that (sequence, kv head) row.
-template <class DT, int D, int MODE, bool DIRECT, bool FUSED>
+// SCORES (one-kernel path only): score export. Each unit's masked log2-domain logits are
+// staged in LDS as they are computed; once the merge has the rows' normalisers, the
+// workgroup adds each entry's softmax mass to the caller's score row of its (sequence,
+// kv head), one thread per entry, in the same order as the work-split path's score kernels.
+template <class DT, int D, int MODE, bool DIRECT, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeParams p) {
     static_assert(DIRECT || !FUSED, "the fused append needs the whole sequence in one workgroup");
+    static_assert(DIRECT || !SCORES, "score export needs the whole sequence in one workgroup");
     using T = Tile<DT, D / (4 * DT::kE)>;
     constexpr int NC = D / (4 * DT::kE);
     constexpr int NACC = T::kAcc;
     __shared__ float s_m[kWaves][kMaxGroup];
     __shared__ float s_l[kWaves][kMaxGroup];
     __shared__ __attribute__((aligned(16))) float s_o[kWaves][kMaxGroup][D + 4];
+    __shared__ float s_lg[SCORES ? kDirectMaxUnits : 1][kMaxGroup][16];  // [unit][head][token]
+    __shared__ float s_lse2[kMaxGroup];
 
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -166,6 +175,17 @@ void decode_split_kernel(DecodeParams p) {
             x1[i] = (keep1 >> i) & 1 ? s1[i] * qk_scale : kNegInf;
             mx = fmaxf(mx, fmaxf(x0[i], x1[i]));
         }
+        if constexpr (SCORES) {
+            // lanes c < 8 hold the first copy of head c's column: tokens 4j .. 4j+3 of the unit
+            const int ux = w + X.slot * kWaves, uy = w + Y.slot * kWaves;
+            if (c < 8 && c < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (X.t0 >= 0 && ux < kDirectMaxUnits) s_lg[ux][c][4 * j + i] = x0[i];
+                    if (Y.t0 >= 0 && uy < kDirectMaxUnits) s_lg[uy][c][4 * j + i] = x1[i];
+                }
+            }
+        }
         mx = xor32_max(xor16_max(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == kNegInf ? 0.f : m_new;
@@ -232,12 +252,95 @@ void decode_split_kernel(DecodeParams p) {
         if (DIRECT) {
             store_out(p.out, p.out_dtype, h * D + x, Ls > 0.f ? O / Ls : 0.f);
             if (x == 0 && p.lse) p.lse[h] = Ls > 0.f ? M * kLn2 + logf(Ls) : kNegInf;
+            if constexpr (SCORES)
+                if (x == 0) s_lse2[g] = Ls > 0.f ? M + __log2f(Ls) : kNegInf;
         } else {
             const size_t r = h * p.num_splits + split;
             p.o_part[r * D + x] = O;
             if (x == 0) {
                 p.m_part[r] = Ls > 0.f ? M * kLn2 : kNegInf;
                 p.l_part[r] = Ls;
+            }
+        }
+    }
+
+    if constexpr (SCORES) {
+        __syncthreads();  // the rows' normalisers
+        float l2[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) l2[g] = g < G ? s_lse2[g] : 0.f;
+        // softmax mass of the 16 tokens of staged unit u, the heads summed in order
+        auto unit_mass = [&](int u, float (&m)[16]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m[i] = 0.f;
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) m[i] += __builtin_amdgcn_exp2f(s_lg[u][g][i] - l2[g]);
+                }
+        };
+        const int nu = sp.n_units < kDirectMaxUnits ? sp.n_units : kDirectMaxUnits;
+        float* row = p.score + (size_t)(b * p.kv_heads + kvh) * p.score_stride;
+        if (p.score_block <= 1) {
+            // one entry per attended token
+            for (int idx = tid; idx < nu * 16; idx += 64 * kWaves) {
+                const int u = idx >> 4, i = idx & 15;
+                const int t0 = unit_token<MODE>(p, sp, b, u);
+                const int t = t0 + i;
+                if (t0 < 0 || !(t < sp.L && (t < sp.e0 || t >= sp.s1))) continue;
+                float mass = 0.f;
+#pragma unroll
+                for (int g = 0; g < kMaxGroup; ++g)
+                    if (g < G) mass += __builtin_amdgcn_exp2f(s_lg[u][g][i] - l2[g]);
+                row[t] += mass;
+            }
+        } else if (MODE == kPages) {
+            // one entry per listed page (score_block == block_size): list entry kk holds units
+            // kk * P/16 .. (kk + 1) * P/16 - 1, and its entry is the page id
+            const int per = p.block_size >> 4;
+            for (int kk = tid; kk < p.pages_per_seq; kk += 64 * kWaves) {
+                const int pg = p.page_list[(size_t)b * p.pages_per_seq + kk];
+                if (pg < 0 || (long long)pg * p.block_size >= sp.L) continue;
+                float accs = 0.f;
+                for (int cc = 0; cc < per; ++cc) {
+                    const int c0 = pg * p.block_size + 16 * cc;
+                    const int u = kk * per + cc;
+                    if (c0 >= sp.L || u >= nu) break;
+                    float m[16];
+                    unit_mass(u, m);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (c0 + i < sp.L) accs += m[i];
+                }
+                row[pg] += accs;
+            }
+        } else {
+            // entries of score_block tokens over the attended token ranges
+            const int B = p.score_block;
+            const int n_ent = (sp.L + B - 1) / B;
+            for (int e = tid; e < n_ent; e += 64 * kWaves) {
+                const int t_lo = e * B;
+                const int t_hi = (e + 1) * B < sp.L ? (e + 1) * B : sp.L;
+                float accs = 0.f;
+                bool any = false;
+                for (int c0 = t_lo & ~15; c0 < t_hi; c0 += 16) {
+                    const int cu = c0 >> 4;
+                    int u = cu;
+                    if (MODE == kWindow) u = cu < sp.n0 ? cu : (cu >= sp.u1a ? sp.n0 + (cu - sp.u1a) : -1);
+                    if (u < 0 || u >= nu) continue;
+                    float m[16];
+                    unit_mass(u, m);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = c0 + i;
+                        if (t >= t_lo && t < t_hi && (MODE != kWindow || t < sp.e0 || t >= sp.s1)) {
+                            accs += m[i];
+                            any = true;
+                        }
+                    }
+                }
+                if (any) row[e] += accs;
             }
         }
     }
@@ -277,14 +380,21 @@ template <class DT, int D, int MODE>
 static hipError_t launch_decode_t(bool direct, const DecodeParams& p, int batch, hipStream_t s) {
     const dim3 grid((unsigned)p.num_splits, (unsigned)p.kv_heads, (unsigned)batch);
     const dim3 block(64 * kWaves);
-    if (direct && p.new_slots) {
-        if (p.num_splits != 1) return hipErrorInvalidValue;
-        decode_split_kernel<DT, D, MODE, true, true><<<grid, block, 0, s>>>(p);
-    } else if (direct) {
-        decode_split_kernel<DT, D, MODE, true, false><<<grid, block, 0, s>>>(p);
+    if (direct) {
+        // one partition holding every unit of a segment (with score export, at most
+        // kDirectMaxUnits of them: the logits are staged in LDS)
+        if (p.num_splits != 1 || (p.score && p.units_per_split > kDirectMaxUnits)) return hipErrorInvalidValue;
+        if (p.new_slots && p.score)
+            decode_split_kernel<DT, D, MODE, true, true, true><<<grid, block, 0, s>>>(p);
+        else if (p.new_slots)
+            decode_split_kernel<DT, D, MODE, true, true, false><<<grid, block, 0, s>>>(p);
+        else if (p.score)
+            decode_split_kernel<DT, D, MODE, true, false, true><<<grid, block, 0, s>>>(p);
+        else
+            decode_split_kernel<DT, D, MODE, true, false, false><<<grid, block, 0, s>>>(p);
     } else {
-        if (p.new_slots) return hipErrorInvalidValue;
-        decode_split_kernel<DT, D, MODE, false, false><<<grid, block, 0, s>>>(p);
+        if (p.new_slots || p.score) return hipErrorInvalidValue;
+        decode_split_kernel<DT, D, MODE, false, false, false><<<grid, block, 0, s>>>(p);
     }
     return hipGetLastError();
 }

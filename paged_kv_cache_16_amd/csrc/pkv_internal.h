@@ -16,6 +16,8 @@ constexpr int kStreamWaves = 4;    // wavefronts per workgroup of the persistent
 constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
 constexpr int kMaxSlots = 512;      // partial slots per segment the stream combine handles
 constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
+constexpr int kDirectMaxUnits = 40;  // units per segment the one-kernel path takes (and stages
+                                     // logits for, with score export)
 
 // Bits of the device error word (the PKV_DEV_* values of the C ABI).
 enum DevError : unsigned { kDevBlockId = 1u, kDevSlot = 2u, kDevContext = 4u, kDevPages = 8u };

@@ -121,10 +121,15 @@ def test_score_export_validation(pkv):
     ws1 = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(scored))
     # logits of every unit and head: 32 seq x 8 kv heads x 256 units x 4 heads x 16 tokens x 4 B
     assert ws1 - ws0 >= 32 * 8 * 256 * 4 * 16 * 4
-    # scores force the work-split path, so even a tiny problem needs a workspace
+    # the one-kernel path exports scores itself, so a tiny problem still needs no workspace ...
     assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(plain)) == 0
     small = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 20)
-    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(small)) > 0
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(small)) == 0
+    # ... except over a page list with entries other than single tokens or whole pages
+    odd = pkv.DecodeOpts(0, 0, fake, 2, 0, None, None, fake, 20, 5)
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(odd)) > 0
+    per_page = pkv.DecodeOpts(0, 0, fake, 2, 0, None, None, fake, 20, d.block_size)
+    assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(per_page)) == 0
     call = lib.paged_decode_attention
     args = lambda opts, mcl=100: (ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, mcl, 0.0, opts, fake, 2,
                                   None, None, 0, None)

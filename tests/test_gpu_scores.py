@@ -86,6 +86,58 @@ def test_score_export(sc, fused):
     assert_close(c, got, oracle_attend(c, **okw), f"scores {sc['name']} outputs")
 
 
+ONE_KERNEL_CASES = [("full", 1), ("full", 32), ("window", 1), ("window", 5), ("pages", 32), ("pages", 1)]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["attention", "fused-step"])
+@pytest.mark.parametrize("mode,block", ONE_KERNEL_CASES, ids=[f"{m}-B{b}" for m, b in ONE_KERNEL_CASES])
+def test_score_export_one_kernel(mode, block, fused):
+    """Score export on the one-kernel path (64 segments of at most 40 units: no workspace), per
+    token, per page and per odd-sized entry, against the oracle; the cache is NaN-filled past
+    every context and, in the fused step, holds no copy of the new token."""
+    import paged_kv_cache_16_amd as pkv
+    B, Hq, Hkv, P = 16, 8, 4, 32
+    rng = np.random.default_rng(75 + block)
+    lens = [int(x) for x in rng.integers(1, 620, size=B)]
+    lens[3] = 1
+    log(f"one-kernel scores {mode} B={block} fused={fused}")
+    c = make_case(75, B=B, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", P=P, lens=lens)
+    kw, okw = {}, {}
+    if mode == "window":
+        kw, okw = dict(window=150, num_sinks=5), dict(window=150, sinks=5)
+    elif mode == "pages":
+        pl = synth.page_lists(lens, P, 5, 75).numpy()
+        kw, okw = dict(page_list=torch.as_tensor(pl).cuda()), dict(page_list=pl)
+    stride = (max(lens) + block - 1) // block + 3
+    assert pkv.workspace_size(c.gk, B, Hq, max(lens), scores=True, window=kw.get("window", 0),
+                              num_sinks=kw.get("num_sinks", 0), page_list=kw.get("page_list")) == 0
+    init = synth.normal((B, Hkv, stride), 75, "score-init", block, dtype="f32")
+    gs = init.clone().cuda()
+    if fused:
+        c.gk.fill_(float("nan"))
+        c.gv.fill_(float("nan"))
+        pre = synth.token_slots(c.bt, lens, P, last=[L - 1 for L in lens])
+        kp = torch.cat([c.K[b, :L - 1] for b, L in enumerate(lens)]).cuda()
+        vp = torch.cat([c.V[b, :L - 1] for b, L in enumerate(lens)]).cuda()
+        pkv.kv_cache_append(c.gk, c.gv, kp, vp, pre.cuda())
+        slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, P) for b, L in enumerate(lens)], dtype=torch.int32).cuda()
+        kn = torch.stack([c.K[b, L - 1] for b, L in enumerate(lens)]).cuda()
+        vn = torch.stack([c.V[b, L - 1] for b, L in enumerate(lens)]).cuda()
+        out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl,
+                                                     max_context_len=max(lens), scores=gs, score_block=block, **kw)
+    else:
+        out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
+                                              scores=gs, score_block=block, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.decode_scores(c.dtype, c.kpool, synth.raw_numpy(c.q), c.bt.numpy(), np.array(lens, np.int32),
+                               P=P, Hkv=Hkv, d=128, stride=stride, score=init.double().numpy(), block=block, **okw)
+    err = float(np.abs(gs.cpu().double().numpy() - ref).max())
+    log(f"    max|score err| = {err:.3e}")
+    assert err <= SCORE_TOL
+    got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    assert_close(c, got, oracle_attend(c, **okw), f"one-kernel scores {mode} outputs")
+
+
 def test_score_accumulates_over_steps():
     """Two calls on one array add two steps' scores; tokens outside the window keep theirs."""
     import paged_kv_cache_16_amd as pkv
