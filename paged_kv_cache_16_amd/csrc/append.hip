@@ -84,10 +84,14 @@ __device__ __forceinline__ float in_f32(const void* base, size_t idx) {
         return (float)__builtin_bit_cast(_Float16, h);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Max over the wave of two values side by side (their cross-lane steps overlap).
+__device__ __forceinline__ void wave_max2(float& a, float& b) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ta = __shfl_xor(a, off), tb = __shfl_xor(b, off);
+        a = fmaxf(a, ta);
+        b = fmaxf(b, tb);
+    }
 }
 
 template <class In, int D>
@@ -98,7 +102,23 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
     if (row >= p.num_tokens * p.kv_heads) return;
     const int64_t i = row / p.kv_heads;
     const int h = (int)(row - i * p.kv_heads);
+    // The row's K and V values do not depend on its slot: they are requested together with
+    // it, and the row maxima (cross-lane steps, which stay where they are written) come
+    // before the slot's checks, so the wave waits for one round trip instead of three.
+    float xk[PER], xv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        xk[e] = in_f32<In>(p.k_new, (size_t)row * D + lane + 64 * e);
+        xv[e] = in_f32<In>(p.v_new, (size_t)row * D + lane + 64 * e);
+    }
     const int64_t slot = p.slots[i];
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        ak = fmaxf(ak, fabsf(xk[e]));
+        av = fmaxf(av, fabsf(xv[e]));
+    }
+    wave_max2(ak, av);
     if (slot < 0) return;
     if (slot >= p.num_slots) {
         if (h == 0 && lane == 0) report(p.err, kDevSlot);
@@ -112,20 +132,12 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
     const size_t srow = ((size_t)blk * p.kv_heads + h) * p.block_size + t;
 #pragma unroll
     for (int is_v = 0; is_v < 2; ++is_v) {
-        const void* src = is_v ? p.v_new : p.k_new;
         char* pool = (char*)(is_v ? p.v_cache : p.k_cache);
-        float x[PER];
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            x[e] = in_f32<In>(src, (size_t)row * D + lane + 64 * e);
-            amax = fmaxf(amax, fabsf(x[e]));
-        }
-        amax = wave_max(amax);
+        const float amax = is_v ? av : ak;
         const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            float r = amax > 0.f ? rintf(x[e] * inv) : 0.f;
+            float r = amax > 0.f ? rintf((is_v ? xv[e] : xk[e]) * inv) : 0.f;
             r = fminf(fmaxf(r, -127.f), 127.f);
             const int xd = lane + 64 * e;
             size_t pos;
