@@ -456,17 +456,20 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
             for (int i = 0; i < PER; ++i) v[u][i] = op[(rk - base) * D + i];
         }
     };
+    int cnt = p.seg_count[g];
     fetch(0);
     const int nu = seq_units<MODE>(p, b);
-    int cnt = p.seg_count[g];
-    if (nu == 0) {
+    // one branch on both values (no short circuit): with the count tested only past the
+    // empty-sequence case, its load was issued after the first batch had returned
+    if ((nu == 0) | (cnt == 0)) {
+        if (nu == 0) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, 0.f);
-        if (lane == 0 && p.lse) p.lse[hrow] = kNegInf;
-        if (lane == 0 && p.row_lse2) p.row_lse2[hrow] = kNegInf;
+            for (int i = 0; i < PER; ++i) store_out(p.out, p.out_dtype, hrow * D + lane * PER + i, 0.f);
+            if (lane == 0 && p.lse) p.lse[hrow] = kNegInf;
+            if (lane == 0 && p.row_lse2) p.row_lse2[hrow] = kNegInf;
+        }
         return;
     }
-    if (cnt == 0) return;
     if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
     // online merge over the batches
     float M = kNegInf, Ls = 0.f;
