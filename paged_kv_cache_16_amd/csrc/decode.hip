@@ -90,9 +90,19 @@ void decode_split_kernel(DecodeParams p) {
     const int j = lane >> 4, c = lane & 15;
     const int G = p.group;
 
-    const int L_b = p.context_lens[b];
-    const SeqPlan sp = make_plan_len<MODE>(p, L_b);
     const int u_begin = split * p.units_per_split;
+    // Page list: the lane's entry does not depend on the context length, so it is requested
+    // together with it (one round trip before the block-table read instead of two).
+    // The load is unconditional (a lane past the list reads entry 0 and drops it): a load
+    // under a branch made the compiler wait for it before requesting the length.
+    const int L_b = p.context_lens[b];
+    int pg_lane = -1;
+    if constexpr (MODE == kPages) {
+        const int k = (u_begin + w + lane * kWaves) / (p.block_size >> 4);
+        const int pg = p.page_list[(size_t)b * p.pages_per_seq + (k < p.pages_per_seq ? k : 0)];
+        pg_lane = k < p.pages_per_seq ? pg : -1;
+    }
+    const SeqPlan sp = make_plan_len<MODE>(p, L_b);
     int u_end = u_begin + p.units_per_split;
     if (u_end > sp.n_units) u_end = sp.n_units;
 
@@ -121,7 +131,14 @@ void decode_split_kernel(DecodeParams p) {
     unsigned my_off = 0;
     if (lane < nk) {
         const int u = u_begin + w + lane * kWaves;
-        const int t0 = unit_token<MODE>(p, sp, b, u);
+        int t0;
+        if constexpr (MODE == kPages) {  // unit_token's page-list case, from the entry read above
+            const int per = p.block_size >> 4;
+            const int64_t tp = (int64_t)pg_lane * p.block_size + (int64_t)(u - (u / per) * per) * 16;
+            t0 = pg_lane >= 0 && tp < sp.L ? (int)tp : -1;
+        } else {
+            t0 = unit_token<MODE>(p, sp, b, u);
+        }
         if (t0 >= 0) {
             const int phys = p.block_table[(size_t)b * p.max_blocks + table_col(p, t0 / p.block_size)];
             if (phys >= 0 && phys < p.num_blocks) {
