@@ -256,6 +256,13 @@ static int pages_ok(const int32_t* pages, int npages) {
     return 1;
 }
 
+/* Index of the list entry holding logical page p, or -1. */
+static int page_entry(const int32_t* pages, int npages, int64_t p) {
+    for (int k = 0; k < npages; ++k)
+        if (pages[k] >= 0 && pages[k] == p) return k;
+    return -1;
+}
+
 static int common_args_ok(int dt, int64_t num_blocks, int P, int Hkv, int d, int B, int Hq,
                           int max_blocks, int window, int sinks, const int32_t* page_list,
                           int pps) {
@@ -450,9 +457,14 @@ int oracle_select_pages(const float* scores, int H, int64_t stride, const int32_
 
 /* Split partials and their log-sum-exp combination ([Novita] §關鍵技術 2: a
  * partition's running max and sum l are enough to merge it with others).
- * The attended tokens of (b, h), grouped by aligned 16-token unit (t / 16) in
- * ascending order, are cut into partitions of `units` consecutive units;
- * partition s gets m_s, l_s and the unnormalised o_s. Writes the partials
+ * The attended tokens of (b, h) are grouped into aligned 16-token units, which are
+ * enumerated and cut into partitions of `units` consecutive enumerated units;
+ * partition s gets m_s, l_s and the unnormalised o_s. The enumeration is the one the
+ * library's partial call documents: for full and window attention the units t / 16
+ * that hold attended tokens, ascending; for a page list every 16-token quarter of
+ * every list entry in list order, padding and pages past L included (entry k owns
+ * enumerated units k * P/16 .. (k + 1) * P/16 - 1), so a list's partitions depend on
+ * the list alone and some of them may be empty. Writes the partials
  * (o_part [B][Hq][S][d], m_part/l_part [B][Hq][S]; empty partitions: m = -inf,
  * l = 0, o = 0) when the pointers are non-NULL, and always the combined
  * out/lse. S = max_splits; more partitions than that is an argument error. */
@@ -480,7 +492,8 @@ int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, in
         if (L < 0 || (pages && !pages_ok(pages, pps))) { rc = ORC_ERR_PRECONDITION; break; }
         double* logits = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
         int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
-        if (!logits || !toks) { free(logits); free(toks); rc = ORC_ERR_NOMEM; break; }
+        int64_t* part = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+        if (!logits || !toks || !part) { free(logits); free(toks); free(part); rc = ORC_ERR_NOMEM; break; }
         for (int h = 0; h < Hq && rc == ORC_OK; ++h) {
             int64_t cnt = gather_logits(dt, num_blocks, P, Hkv, d, kpool, q, Hq, b, h,
                                         block_table + (size_t)b * max_blocks, max_blocks, L,
@@ -488,24 +501,28 @@ int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, in
             if (cnt < 0) { rc = ORC_ERR_PRECONDITION; break; }
             for (int s = 0; s < max_splits; ++s) { pm[s] = -INFINITY; pl[s] = 0.0; }
             memset(po, 0, sizeof(double) * (size_t)max_splits * d);
-            /* Assign each attended token to its partition: unit rank / units. */
+            /* Each attended token's partition: its enumerated unit / units. */
             int64_t unit_rank = -1, last_unit = -1;
             int kvh = h / G;
-            /* First pass: maxima per partition. */
             for (int64_t k = 0; k < cnt; ++k) {
-                int64_t u = toks[k] / 16;
-                if (u != last_unit) { ++unit_rank; last_unit = u; }
-                int64_t s = unit_rank / units;
-                if (s >= max_splits) { rc = ORC_ERR_ARG; break; }
-                if (logits[k] > pm[s]) pm[s] = logits[k];
+                int64_t t = toks[k], u;
+                if (pages) {
+                    int e = page_entry(pages, pps, t / P);
+                    u = (int64_t)e * (P / 16) + (t % P) / 16;
+                } else {
+                    if (t / 16 != last_unit) { ++unit_rank; last_unit = t / 16; }
+                    u = unit_rank;
+                }
+                part[k] = u / units;
+                if (part[k] >= max_splits) { rc = ORC_ERR_ARG; break; }
             }
             if (rc != ORC_OK) break;
+            /* First pass: maxima per partition. */
+            for (int64_t k = 0; k < cnt; ++k)
+                if (logits[k] > pm[part[k]]) pm[part[k]] = logits[k];
             /* Second pass: sums per partition. */
-            unit_rank = -1; last_unit = -1;
             for (int64_t k = 0; k < cnt; ++k) {
-                int64_t u = toks[k] / 16;
-                if (u != last_unit) { ++unit_rank; last_unit = u; }
-                int64_t s = unit_rank / units;
+                int64_t s = part[k];
                 double w = exp(logits[k] - pm[s]);
                 pl[s] += w;
                 int64_t t = toks[k];
@@ -536,6 +553,7 @@ int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, in
         }
         free(logits);
         free(toks);
+        free(part);
     }
     free(po); free(pm); free(pl);
     return rc;

@@ -314,6 +314,43 @@ def pin_split_combine(o):
             assert np.all(np.isneginf(mp[~live]))
 
 
+
+def pin_split_page_partitions(o):
+    """Page-list partitions follow the list: entry k owns enumerated units k*P/16 ..
+    (k+1)*P/16 - 1, padding and pages past L included, so some partitions are empty. With
+    q = 0 every logit is 0, so a partition's l is its token count, m is 0 and o[0] sums the
+    token ids the V rows carry (V[t][0] = t, V[t][1] = 1). Hand-worked, P = 32:
+      row 0, list [-1, 0, 3], L = 100: entry 0 (padding) -> units 0, 1; page 0 -> units 2
+      (tokens 0..15), 3 (16..31); page 3 -> unit 4 (96..99, the rest is past L), 5 (empty);
+      row 1, list [1, 5, -1], L = 40: page 1 -> unit 0 (32..39), 1 (48..63, past L); page 5
+      (past L) -> units 2, 3; padding -> 4, 5."""
+    B, P, d, Lmax = 2, 32, 64, 100
+    V = torch.zeros((B, Lmax, 1, d), dtype=torch.float32)
+    V[:, :, 0, 0] = torch.arange(Lmax, dtype=torch.float32)
+    V[:, :, 0, 1] = 1.0
+    pr = build(o, 15, B=B, Hq=1, Hkv=1, d=d, dtype="f32", P=P, lens=[100, 40],
+               q=torch.zeros((B, 1, d), dtype=torch.float32), V=V)
+    pl = np.array([[-1, 0, 3], [1, 5, -1]], np.int32)
+    # units per partition -> per row, per partition: (token count, sum of token ids)
+    expect = {
+        1: [[(0, 0), (0, 0), (16, 120), (16, 376), (4, 390), (0, 0)],
+            [(8, 284), (0, 0), (0, 0), (0, 0), (0, 0), (0, 0)]],
+        2: [[(0, 0), (32, 496), (4, 390)], [(8, 284), (0, 0), (0, 0)]],
+        3: [[(16, 120), (20, 766)], [(8, 284), (0, 0)]],
+    }
+    for units, rows in expect.items():
+        S = len(rows[0])
+        op, mp, lp, out, lse = o.decode_attention_split(
+            pr.dtype, pr.kpool, pr.vpool, synth.raw_numpy(pr.q), pr.bt.numpy(), np.array(pr.lens, np.int32),
+            P=P, Hkv=1, d=d, units=units, max_splits=S, page_list=pl)
+        for b in range(B):
+            for s_, (n, tsum) in enumerate(rows[b]):
+                assert lp[b, 0, s_] == n, (units, b, s_, lp[b, 0, s_], n)
+                if n:
+                    assert mp[b, 0, s_] == 0.0 and op[b, 0, s_, 0] == tsum and op[b, 0, s_, 1] == n
+                else:
+                    assert np.isneginf(mp[b, 0, s_])
+
 def scores(o, pr, stride, score=None, block=1, **kw):
     return o.decode_scores(pr.dtype, pr.kpool, synth.raw_numpy(pr.q), pr.bt.numpy(),
                            np.array(pr.lens, np.int32), P=pr.P, Hkv=pr.Hkv, d=pr.d, stride=stride,
@@ -624,7 +661,7 @@ def pin_empty(o):
 PINS = [pin_kv_bytes, pin_layout_golden, pin_layout_bijection, pin_append_roundtrip,
         pin_bruteforce, pin_permutation, pin_window_reductions, pin_identical_keys,
         pin_identical_values, pin_small_closed_forms, pin_peaked, pin_key_shift,
-        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_scores, pin_scores_block, pin_select_pages,
+        pin_gqa_grouping, pin_page_list_reductions, pin_split_combine, pin_split_page_partitions, pin_scores, pin_scores_block, pin_select_pages,
         pin_int8_quantise, pin_int8_attention, pin_ring_golden, pin_ring_pages_bruteforce,
         pin_ring_attention, pin_ring_reuse, pin_empty]
 

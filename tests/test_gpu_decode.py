@@ -413,18 +413,31 @@ def test_out_dtype_and_explicit_scale():
 
 
 def test_partial_and_combine_match_oracle_partitions():
+    """Partials of the partition path against the oracle's partitions, in full, window and
+    page-list mode. Page lists are cut by list entry (every 16-token quarter of every entry,
+    padding and pages past the context included), so the lists here hold padding, pages past
+    L and, with 32-token pages and 16-token partitions, pages split over two partitions."""
     import paged_kv_cache_16_amd as pkv
     lens = [333, 64, 0, 129]
     c = make_case(46, B=4, Hq=6, Hkv=1, d=128, dtype="bf16", P=16, lens=lens)
-    for kw, okw in ((dict(), dict()), (dict(window=100, num_sinks=3), dict(window=100, sinks=3))):
-        st = 64
-        op, mp, lp = pkv.paged_decode_attention_partial(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=333,
+    pl16 = np.array([[-1, 2, 7, 20, 25], [0, -1, 3, -1, -1], [0, 1, -1, -1, -1], [1, 4, 8, 9, -1]], np.int32)
+    lens32 = [333, 70, 129]
+    c32 = make_case(56, B=3, Hq=6, Hkv=1, d=128, dtype="bf16", P=32, lens=lens32)
+    pl32 = np.array([[-1, 0, 3, 10, 11], [1, -1, 2, 5, -1], [0, 4, -1, -1, -1]], np.int32)
+    cases = [(c, 64, dict(), dict()), (c, 64, dict(window=100, num_sinks=3), dict(window=100, sinks=3)),
+             (c, 64, dict(page_list=torch.as_tensor(pl16).cuda()), dict(page_list=pl16)),
+             (c32, 16, dict(page_list=torch.as_tensor(pl32).cuda()), dict(page_list=pl32)),
+             (c32, 48, dict(page_list=torch.as_tensor(pl32).cuda()), dict(page_list=pl32))]
+    for c, st, kw, okw in cases:
+        lens = c.lens
+        op, mp, lp = pkv.paged_decode_attention_partial(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
                                                         split_tokens=st, **kw)
         torch.cuda.synchronize()
         S = op.shape[2]
         ro, rm, rl, rout, rlse = oracle.decode_attention_split(
             c.dtype, c.kpool, c.vpool, synth.raw_numpy(c.q), c.bt.numpy(), np.array(lens, np.int32),
             P=c.P, Hkv=1, d=128, units=st // 16, max_splits=S, **okw)
+        log(f"    partitions P={c.P} split={st} S={S} {sorted(okw)}: live {int((rl > 0).sum())} of {rl.size}")
         mp_, lp_ = mp.cpu().numpy(), lp.cpu().numpy()
         live = rl > 0
         assert np.array_equal(live, lp_ > 0)
@@ -435,7 +448,7 @@ def test_partial_and_combine_match_oracle_partitions():
         assert max_err((o_[live] / lp_[live][:, None]), ro[live] / rl[live][:, None]) <= 2e-3
         out, lse = pkv.paged_decode_combine(op, mp, lp)
         torch.cuda.synchronize()
-        assert_close(c, (out.cpu().numpy(), lse.cpu().numpy()), (rout, rlse), f"combine {kw}")
+        assert_close(c, (out.cpu().numpy(), lse.cpu().numpy()), (rout, rlse), f"combine P={c.P} split={st} {sorted(okw)}")
 
 
 def test_status_codes():

@@ -24,6 +24,9 @@ MUTATIONS = [
     ("normaliser not shifted", "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k] - m);",
      "for (int64_t k = 0; k < cnt; ++k) z += exp(logits[k]);"),
     ("block index uses offset", "int64_t blk = bt_row[t / P];", "int64_t blk = bt_row[t % P];"),
+    ("page-list partitions ranked over attended units", "                if (pages) {\n                    int e = page_entry",
+     "                if (0) {\n                    int e = page_entry"),
+    ("page entry not scaled by units per page", "u = (int64_t)e * (P / 16) + (t % P) / 16;", "u = (int64_t)e + (t % P) / 16;"),
     ("combine weight inverted", "double w = exp(pm[s] - M);", "double w = exp(M - pm[s]);"),
     ("fp16 exponent bias", "v = ldexp((double)(f | 0x400), e - 25);", "v = ldexp((double)(f | 0x400), e - 24);"),
     ("bf16 wrong half", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
