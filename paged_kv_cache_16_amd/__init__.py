@@ -144,6 +144,57 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# Shape checks. The C ABI takes raw pointers and sizes, so a tensor smaller than the call
+# implies would be read or written past its end; every wrapper checks the tensors it passes
+# against the sizes it passes before anything is enqueued (ValueError, nothing launched).
+def _need(ok: bool, msg: str) -> None:
+    if not ok:
+        raise ValueError(msg)
+
+
+def _shape(t, name: str, shape) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must be shaped {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t, name: str, ndim: int, rows: int) -> None:
+    """t has ndim dimensions and at least `rows` rows (entries past them are never read)."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.dim() == ndim, f"{name} must have {ndim} dimension(s), got {t.dim()}")
+    _need(t.shape[0] >= rows, f"{name} must have at least {rows} rows, got {t.shape[0]}")
+
+
+def _cache_pair(k_cache, v_cache) -> None:
+    _need(isinstance(k_cache, torch.Tensor) and isinstance(v_cache, torch.Tensor), "caches must be tensors")
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype,
+          f"k_cache and v_cache must match, got {tuple(k_cache.shape)} {k_cache.dtype} and "
+          f"{tuple(v_cache.shape)} {v_cache.dtype}")
+
+
+def _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, out, lse, scores):
+    """Checks of a decode call's tensors against (B, Hq, d) taken from q."""
+    _cache_pair(k_cache, v_cache)
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be [batch, num_q_heads, head_dim]")
+    B, Hq, d = q.shape
+    _need(d == desc.head_dim, f"q's head_dim {d} differs from the cache's {desc.head_dim}")
+    _rows(block_table, "block_table", 2, B)
+    _need(block_table.shape[1] >= 1 or B == 0, "block_table needs at least one column")
+    _rows(context_lens, "context_lens", 1, B)
+    if page_list is not None:
+        _rows(page_list, "page_list", 2, B)
+        _need(page_list.shape[1] >= 1, "page_list needs at least one column")
+    if out is not None:
+        _shape(out, "out", (B, Hq, d))
+    if lse is not None:
+        _shape(lse, "lse", (B, Hq))
+    if scores is not None:
+        _need(isinstance(scores, torch.Tensor) and scores.dim() == 3,
+              "scores must be a [batch, num_kv_heads, stride] tensor")
+        _need(scores.shape[0] >= B and scores.shape[1] == desc.num_kv_heads,
+              f"scores must be [>= {B}, {desc.num_kv_heads}, stride], got {tuple(scores.shape)}")
+    return B, Hq, d
+
+
 def cache_desc(k_cache: torch.Tensor, input_dtype=None) -> CacheDesc:
     """Descriptor of a cache tensor. An INT8 cache is a torch.int8 tensor
     [num_blocks, num_kv_heads, block_size, head_dim + 4] holding the int8 data plane followed
@@ -198,9 +249,11 @@ def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, sc
 def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
     """Scatter k_new/v_new [N, Hkv, d] into the pools at slot_mapping[N] (int32, <0 = skip)."""
     desc = cache_desc(k_cache, k_new.dtype)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
+    _cache_pair(k_cache, v_cache)
+    _need(isinstance(slot_mapping, torch.Tensor) and slot_mapping.dim() == 1, "slot_mapping must be [N]")
     n = slot_mapping.numel()
+    _shape(k_new, "k_new", (n, desc.num_kv_heads, desc.head_dim))
+    _shape(v_new, "v_new", (n, desc.num_kv_heads, desc.head_dim))
     _check("kv_cache_append", _lib.kv_cache_append(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
@@ -248,7 +301,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
     probability, summed over the query heads of its kv head, is added into entry
     t // score_block (score_block = 1: per token; = the page size: per page)."""
     desc = cache_desc(k_cache, q.dtype)
-    B, Hq, d = q.shape
+    B, Hq, d = _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, out, lse, scores)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -279,7 +332,12 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
     slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
     scores: as in paged_decode_attention."""
     desc = cache_desc(k_cache, q.dtype)
-    B, Hq, d = q.shape
+    B, Hq, d = _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, out, lse, scores)
+    # one new token per sequence
+    _shape(k_new, "k_new", (B, desc.num_kv_heads, desc.head_dim))
+    _shape(v_new, "v_new", (B, desc.num_kv_heads, desc.head_dim))
+    _need(isinstance(slot_mapping, torch.Tensor) and slot_mapping.dim() == 1 and slot_mapping.numel() == B,
+          f"slot_mapping must be [{B}]")
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -291,8 +349,6 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if k_new.shape[0] != B or slot_mapping.numel() != B:
-        raise ValueError("one new token per sequence: k_new/v_new [B, Hkv, d], slot_mapping [B]")
     _check("paged_decode_append_attention", _lib.paged_decode_append_attention(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
@@ -310,15 +366,18 @@ def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_len
                                    o_part=None, m_part=None, l_part=None, ring_pages: int = 0):
     """Split-K partials (o [B,Hq,S,d], m [B,Hq,S], l [B,Hq,S], fp32) over explicit partitions."""
     desc = cache_desc(k_cache, q.dtype)
-    B, Hq, d = q.shape
+    B, Hq, d = _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, None, None, None)
     o = _opts(window, num_sinks, page_list, split_tokens, ring_pages=ring_pages)
     S = int(_lib.paged_decode_attention_num_splits(ctypes.byref(desc), B, max_context_len, ctypes.byref(o)))
     if S <= 0:
         raise ValueError("invalid partition request")
-    if o_part is None:
+    if o_part is None and m_part is None and l_part is None:
         o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device=q.device)
         m_part = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
         l_part = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _shape(o_part, "o_part", (B, Hq, S, d))
+    _shape(m_part, "m_part", (B, Hq, S))
+    _shape(l_part, "l_part", (B, Hq, S))
     _check("paged_decode_attention_partial", _lib.paged_decode_attention_partial(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(q, "q", input_dtype_of(k_cache, q)), _dev(block_table, "block_table", torch.int32),
@@ -331,7 +390,14 @@ def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_len
 def paged_decode_combine(o_part, m_part, l_part, *, out=None, out_dtype=torch.float32, lse=None,
                          want_lse: bool = True):
     """Log-sum-exp merge of split partials into (out [B,Hq,d], lse [B,Hq])."""
+    _need(isinstance(o_part, torch.Tensor) and o_part.dim() == 4, "o_part must be [batch, num_q_heads, splits, d]")
     B, Hq, S, d = o_part.shape
+    _shape(m_part, "m_part", (B, Hq, S))
+    _shape(l_part, "l_part", (B, Hq, S))
+    if out is not None:
+        _shape(out, "out", (B, Hq, d))
+    if lse is not None:
+        _shape(lse, "lse", (B, Hq))
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype, device=o_part.device)
     if lse is None and want_lse:
@@ -350,8 +416,10 @@ def select_pages(scores, context_lens, *, block_size: int, k: int, recent: int =
     if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous [batch, heads, stride] float32 tensor")
     B, H, stride = scores.shape
+    _rows(context_lens, "context_lens", 1, B)
     if page_list is None:
         page_list = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    _shape(page_list, "page_list", (B, k))
     _check("paged_select_pages", _lib.paged_select_pages(
         _dev(scores, "scores", torch.float32), H, stride, _dev(context_lens, "context_lens", torch.int32), B,
         int(block_size), int(k), int(recent), _dev(page_list, "page_list", torch.int32), _stream(scores)))

@@ -193,13 +193,15 @@ void decode_split_kernel(DecodeParams p) {
             mx = fmaxf(mx, fmaxf(x0[i], x1[i]));
         }
         if constexpr (SCORES) {
-            // lanes c < 8 hold the first copy of head c's column: tokens 4j .. 4j+3 of the unit
+            // lanes c < 8 hold the first copy of head c's column: tokens 4j .. 4j+3 of the unit.
+            // A unit skipped for an invalid block id (t0 = -1) stages -inf logits (keep = 0), so
+            // the score phase, which takes the unit's tokens from the plan, adds nothing for it.
             const int ux = w + X.slot * kWaves, uy = w + Y.slot * kWaves;
             if (c < 8 && c < G) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (X.t0 >= 0 && ux < kDirectMaxUnits) s_lg[ux][c][4 * j + i] = x0[i];
-                    if (Y.t0 >= 0 && uy < kDirectMaxUnits) s_lg[uy][c][4 * j + i] = x1[i];
+                    if (ux < kDirectMaxUnits) s_lg[ux][c][4 * j + i] = x0[i];
+                    if (uy < kDirectMaxUnits) s_lg[uy][c][4 * j + i] = x1[i];
                 }
             }
         }
@@ -286,7 +288,9 @@ void decode_split_kernel(DecodeParams p) {
         float l2[kMaxGroup];
 #pragma unroll
         for (int g = 0; g < kMaxGroup; ++g) l2[g] = g < G ? s_lse2[g] : 0.f;
-        // softmax mass of the 16 tokens of staged unit u, the heads summed in order
+        // softmax mass of the 16 tokens of staged unit u, the heads summed in order; a masked
+        // logit (-inf) adds exactly 0, also in a row whose normaliser is -inf (no token of it
+        // was read), where the difference would be NaN
         auto unit_mass = [&](int u, float (&m)[16]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) m[i] = 0.f;
@@ -294,7 +298,7 @@ void decode_split_kernel(DecodeParams p) {
             for (int g = 0; g < kMaxGroup; ++g)
                 if (g < G) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) m[i] += __builtin_amdgcn_exp2f(s_lg[u][g][i] - l2[g]);
+                    for (int i = 0; i < 16; ++i) m[i] += prob2(s_lg[u][g][i], l2[g]);
                 }
         };
         const int nu = sp.n_units < kDirectMaxUnits ? sp.n_units : kDirectMaxUnits;
@@ -309,7 +313,7 @@ void decode_split_kernel(DecodeParams p) {
                 float mass = 0.f;
 #pragma unroll
                 for (int g = 0; g < kMaxGroup; ++g)
-                    if (g < G) mass += __builtin_amdgcn_exp2f(s_lg[u][g][i] - l2[g]);
+                    if (g < G) mass += prob2(s_lg[u][g][i], l2[g]);
                 row[t] += mass;
             }
         } else if (MODE == kPages) {

@@ -169,6 +169,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Sum over the wave (uniform).
 __device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
+// Softmax probability 2^(x - lse2) of a log2-domain logit under its row's log2 normaliser. A
+// masked logit (-inf) gives exactly 0, whatever the normaliser: a row none of whose tokens was
+// read has lse2 = -inf, where the difference alone would be NaN.
+__device__ __forceinline__ float prob2(float x, float lse2) {
+    return x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - lse2);
+}
+
 // Packs two fp32 values into bf16 (round to nearest even, hardware conversion).
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;

@@ -293,6 +293,11 @@ void decode_stream_kernel(DecodeParams p) {
             if constexpr (SCORES) {
                 if ((lg_n + 1) * G * 16 > kLgFloats) flush();
                 if (rb.t0 < 0) {
+                    // no unit, or one skipped for an invalid block id: its slot holds -inf
+                    // logits, which the score kernels turn into exactly 0
+                    if (c < G)
+                        *reinterpret_cast<f32x4*>(lgb + (lg_n * G + c) * 16 + 4 * j) =
+                            f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
                     ++lg_n;
                     return;
                 }
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeParams p) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16);
             const float l2 = lse2[g];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mass[i] += __builtin_amdgcn_exp2f(x[i] - l2);
+            for (int i = 0; i < 4; ++i) mass[i] += prob2(x[i], l2);
         }
     }
     float* row = p.score + (size_t)seg * p.score_stride;
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(256) void score_block_kernel(DecodeParams p) {
                 for (int v4 = 0; v4 < 4; ++v4) {
                     const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16 + v4 * 4);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += __builtin_amdgcn_exp2f(x[i] - lse2[g]);
+                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += prob2(x[i], lse2[g]);
                 }
             }
         }
@@ -663,7 +668,7 @@ __global__ __launch_bounds__(256) void score_page_kernel(DecodeParams p) {
                 for (int v4 = 0; v4 < 4; ++v4) {
                     const f32x4 x = *reinterpret_cast<const f32x4*>(lg + g * 16 + v4 * 4);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += __builtin_amdgcn_exp2f(x[i] - lse2[g]);
+                    for (int i = 0; i < 4; ++i) m[v4 * 4 + i] += prob2(x[i], lse2[g]);
                 }
             }
         }

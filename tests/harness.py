@@ -6,6 +6,7 @@ device pools, and every comparison runs the two sides on those inputs.
 """
 from __future__ import annotations
 
+import os
 from types import SimpleNamespace
 
 import numpy as np
@@ -106,3 +107,59 @@ def assert_close(c, got, ref, what=""):
     assert e_out <= TOL[c.dtype], f"{what}: output error {e_out:.3e} > {TOL[c.dtype]}"
     assert e_lse <= LSE_TOL[c.dtype] * max(1.0, float(np.nanmax(np.abs(np.where(np.isfinite(rlse), rlse, 0))))), \
         f"{what}: lse error {e_lse:.3e}"
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size parity: the oracle per sequence, on a pool of host threads (the C oracle runs
+# outside the interpreter lock). One GPU's share of the host is 16 threads.
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_pool(dtype, K_rows, V_rows, *, n_tokens, P, Hkv, d, seed, tokens=None):
+    """One sequence of n_tokens logical tokens in an oracle pool. K_rows / V_rows ([m, Hkv, d],
+    CPU, the input dtype) are the rows of the tokens `tokens` (default: tokens 0 .. m-1); they
+    are appended through the oracle into a fresh pool (NaN-filled; 0xFF bytes for INT8) under a
+    seeded random block table, and every other token stays NaN, so it must never be read.
+    Returns (kpool, vpool, block_table [1, pages] numpy)."""
+    bt, nb = synth.block_tables([n_tokens], P, seed, "oracle-sequence", spare_blocks=1)
+    if dtype in oracle.INPUT_DTYPE:
+        kp = np.full(nb * Hkv * P * (d + 4), 0xFF, np.uint8)
+    else:
+        kp = np.full(nb * Hkv * P * d, NAN_BITS[dtype], dtype=np.float32 if dtype == "f32" else np.uint16)
+    vp = kp.copy()
+    t = np.arange(K_rows.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
+    assert t.size == K_rows.shape[0] == V_rows.shape[0] and (t.size == 0 or int(t.max()) < n_tokens)
+    if t.size:
+        slots = (bt[0].numpy().astype(np.int64)[t // P] * P + t % P).astype(np.int32)
+        oracle.kv_append(dtype, kp, vp, synth.raw_numpy(K_rows), synth.raw_numpy(V_rows), slots,
+                         P=P, Hkv=Hkv, d=d)
+    return kp, vp, bt.numpy()
+
+
+def oracle_sequence(dtype, K_rows, V_rows, evals, *, n_tokens, P, Hkv, d, seed, tokens=None):
+    """Attention of one sequence (rows and pool as in oracle_pool). evals: (q [1, Hq, d], L,
+    oracle kwargs) triples; returns one (out, lse) pair per triple."""
+    kp, vp, bt = oracle_pool(dtype, K_rows, V_rows, n_tokens=n_tokens, P=P, Hkv=Hkv, d=d, seed=seed, tokens=tokens)
+    return [oracle.decode_attention(dtype, kp, vp, synth.raw_numpy(q), bt, np.array([L], np.int32),
+                                    P=P, Hkv=Hkv, d=d, **okw) for q, L, okw in evals]
+
+
+def run_threads(fns):
+    """Runs the callables on ORACLE_THREADS host threads; results in order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=ORACLE_THREADS) as ex:
+        return list(ex.map(lambda f: f(), fns))
+
+
+def window_tokens(L, window, sinks):
+    """Token indices a window layer attends at context length L (sinks, then the window)."""
+    if window <= 0 or window >= L:
+        return np.arange(L)
+    e0 = min(sinks, L)
+    return np.concatenate([np.arange(e0), np.arange(max(e0, L - window), L)])
+
+
+def page_tokens(L, P, pages):
+    """Token indices of the listed pages below L, ascending."""
+    parts = [np.arange(p * P, min((p + 1) * P, L)) for p in sorted(int(x) for x in pages if x >= 0) if p * P < L]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)

@@ -468,95 +468,6 @@ def test_status_codes():
     assert e.value.status == 3
 
 
-# ---------------------------------------------------------------------------- full-size, sampled
-def _sampled_full_size(name, samples, *, window=0, sinks=0, pages=0, seed=7, fused=False):
-    """Runs the GPU on the full workload batch in the benchmark's launch configuration and
-    checks sampled sequences against the oracle, one sequence at a time. Inputs are drawn on
-    the GPU from per-sequence seeds; the sampled sequences' rows are drawn again and copied
-    to the host for the oracle. fused: the cache holds all but each sequence's last token and
-    the step is paged_decode_append_attention (the call the benchmark times); a plain
-    attention call afterwards reads the stored new rows back and must give the same bits."""
-    import paged_kv_cache_16_amd as pkv
-    w = synth.WORKLOADS[name]
-    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
-    if w.ctx_lo == w.ctx_hi:
-        lens = [w.ctx_lo] * B
-    else:
-        lens = synth.uniform_lengths(B, w.ctx_lo, w.ctx_hi, seed, name).tolist()
-    log(f"{name} full size B={B} sum(L)={sum(lens)}")
-    dev = torch.device("cuda")
-    tdt = synth.TORCH_DTYPE[w.dtype]
-    bt, nb = synth.block_tables(lens, P, seed, name)
-    gk = torch.empty((nb, Hkv, P, d), dtype=tdt, device=dev)
-    gv = torch.empty_like(gk)
-    qs = synth.normal((B, Hq, d), seed, name, "q", dtype=w.dtype)
-    page_list = synth.page_lists(lens, P, pages, seed, name) if pages else None
-
-    def rows(b, tag):
-        return synth.normal((lens[b], Hkv, d), seed, name, b, tag, dtype=w.dtype, device=dev)
-
-    gpl = None if page_list is None else page_list.to(dev)
-    gcl = torch.tensor(lens, dtype=torch.int32, device=dev)
-    kw = dict(max_context_len=max(lens), window=window, num_sinks=sinks, page_list=gpl)
-    if not fused:
-        for b, L in enumerate(lens):
-            sl = synth.token_slots(bt[b:b + 1], [L], P)
-            pkv.kv_cache_append(gk, gv, rows(b, "k"), rows(b, "v"), sl.to(dev))
-        out, lse = pkv.paged_decode_attention(qs.to(dev), gk, gv, bt.to(dev), gcl, **kw)
-    else:
-        kn, vn = [], []
-        for b, L in enumerate(lens):
-            kb, vb = rows(b, "k"), rows(b, "v")
-            sl = synth.token_slots(bt[b:b + 1], [L - 1], P)
-            pkv.kv_cache_append(gk, gv, kb[:L - 1].contiguous(), vb[:L - 1].contiguous(), sl.to(dev))
-            kn.append(kb[L - 1])
-            vn.append(vb[L - 1])
-        slots = torch.tensor([synth.slot_of(bt, b, L - 1, P) for b, L in enumerate(lens)], dtype=torch.int32,
-                             device=dev)
-        out, lse = pkv.paged_decode_append_attention(qs.to(dev), gk, gv, torch.stack(kn), torch.stack(vn), slots,
-                                                     bt.to(dev), gcl, **kw)
-        out2, lse2 = pkv.paged_decode_attention(qs.to(dev), gk, gv, bt.to(dev), gcl, **kw)
-        torch.cuda.synchronize()
-        assert torch.equal(out, out2) and torch.equal(lse, lse2), "stored new rows read back differ"
-    torch.cuda.synchronize()
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    del gk, gv
-    for b in samples:
-        L = lens[b]
-        Kb, Vb = rows(b, "k").cpu(), rows(b, "v").cpu()
-        c = make_case(seed, B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=w.dtype, P=P, lens=[L], q=qs[b:b + 1],
-                      K=Kb[None], V=Vb[None], gpu_side=False)
-        okw = dict(window=window, sinks=sinks)
-        if page_list is not None:
-            okw = dict(page_list=page_list[b:b + 1].numpy())
-        ref = oracle_attend(c, **okw)
-        assert_close(c, (out[b:b + 1], lse[b:b + 1]), ref, f"{name} seq {b}")
-
-
-def test_full_size_llama3_layer_sampled():
-    _sampled_full_size("llama3_8b_layer_bf16", samples=[0, 13, 31])
-
-
-def test_full_size_qwen_layer_sampled():
-    _sampled_full_size("qwen25_1p5b_28l_bf16", samples=[0, 63])
-
-
-def test_full_size_kvsparse_window_layer_sampled():
-    _sampled_full_size("llama3_8b_kvsparse_bf16", samples=[0, 7], window=512, sinks=4)
-
-
-def test_full_size_page_selected_sampled():
-    _sampled_full_size("mha7b_pagesel_f16", samples=[0, 15], pages=16)
-
-
-@pytest.mark.parametrize("name", ["llama3_8b_layer_bf16", "mha7b_pagesel_f16"])
-def test_full_size_fused_step_sampled(name):
-    """The benchmark's own step at full size: persistent kernel + combine (Llama-3-8B layer) and
-    the one-kernel path (page-selected MHA-7B), each storing the new rows itself."""
-    _sampled_full_size(name, samples=[0, 13, 31] if name.startswith("llama") else [0, 15],
-                       pages=16 if "pagesel" in name else 0, fused=True)
-
-
 def test_workspace_reuse():
     """One workspace serves any number of calls, which all give the same result: its
     contents on entry are ignored, also between calls whose plans differ (full and window

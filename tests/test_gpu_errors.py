@@ -53,6 +53,37 @@ def test_block_id_out_of_range(split):
     assert_close(c, (out[keep], lse[keep]), (ref[0][keep], ref[1][keep]), "untouched sequences")
 
 
+@pytest.mark.parametrize("block", [1, 16], ids=["per-token", "per-page"])
+@pytest.mark.parametrize("lens", [[300, 200, 90], [120, 100, 90]], ids=["work-split", "one-kernel"])
+def test_block_id_out_of_range_with_scores(lens, block):
+    """Score export while a unit of sequence 1 is skipped for an invalid block id (on the
+    work-split path and on the one-kernel path): the skipped unit adds nothing (its entries keep
+    their initial values), every score stays finite, and sequences 0 and 2 match the oracle."""
+    import oracle
+    import paged_kv_cache_16_amd as pkv
+    log(f"bad block id with score export, lens={lens}, score_block={block}")
+    c = make_case(92, B=3, Hq=8, Hkv=2, d=128, dtype="bf16", P=16, lens=lens)
+    stride = (max(lens) + block - 1) // block
+    init = synth.normal((c.B, c.Hkv, stride), 92, "score-init", dtype="f32")
+    ref = oracle.decode_scores(c.dtype, c.kpool, synth.raw_numpy(c.q), c.bt.numpy(), np.array(lens, np.int32),
+                               P=c.P, Hkv=c.Hkv, d=c.d, stride=stride, score=init.double().numpy(), block=block)
+    bt = c.bt.clone()
+    bt[1, 3] = c.nb + 7  # tokens 48..63 of sequence 1
+    c.gbt = bt.cuda()
+    sc = init.clone().cuda()
+    pkv.device_errors(clear=True)
+    pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens), scores=sc,
+                               score_block=block)
+    got = sc.cpu().numpy().astype(np.float64)
+    assert pkv.device_errors() & pkv.DEV_BLOCK_ID
+    assert np.isfinite(got).all()
+    lo, hi = 48 // block, (63 // block) + 1
+    assert np.array_equal(got[1, :, lo:hi], init.numpy()[1, :, lo:hi].astype(np.float64))
+    err = float(np.abs(got[[0, 2]] - ref[[0, 2]]).max())
+    log(f"    untouched sequences: max|score err| = {err:.3e}")
+    assert err <= 1e-5
+
+
 def test_slot_out_of_range():
     """Append slots past the pool: nothing is written and the bit is set, also in the fused step."""
     import paged_kv_cache_16_amd as pkv

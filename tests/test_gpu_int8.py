@@ -177,41 +177,3 @@ def test_int8_status_codes():
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.paged_decode_attention_partial(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=300, split_tokens=64)
     assert e.value.status == 3
-
-
-def test_int8_full_size_llama3_layer_sampled():
-    """The Llama-3-8B-shaped layer (32 sequences, contexts U[1024, 4096]) in an INT8 cache, in
-    the benchmark's launch configuration; two sampled sequences against the oracle."""
-    import paged_kv_cache_16_amd as pkv
-    name, seed = "llama3_8b_layer_bf16", 7
-    w = synth.WORKLOADS[name]
-    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
-    lens = synth.uniform_lengths(B, w.ctx_lo, w.ctx_hi, seed, name).tolist()
-    dev = torch.device("cuda")
-    bt, nb = synth.block_tables(lens, P, seed, name)
-    gk = pkv.new_cache(nb, Hkv, P, d, torch.int8)
-    gv = pkv.new_cache(nb, Hkv, P, d, torch.int8)
-    qs = synth.normal((B, Hq, d), seed, name, "q", dtype="bf16")
-
-    def rows(b, tag):
-        return synth.normal((lens[b], Hkv, d), seed, name, b, tag, dtype="bf16", device=dev)
-
-    for b, L in enumerate(lens):
-        pkv.kv_cache_append(gk, gv, rows(b, "k"), rows(b, "v"), synth.token_slots(bt[b:b + 1], [L], P).to(dev))
-    out, lse = pkv.paged_decode_attention(qs.to(dev), gk, gv, bt.to(dev),
-                                          torch.tensor(lens, dtype=torch.int32, device=dev), max_context_len=max(lens))
-    torch.cuda.synchronize()
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    del gk, gv
-    for b in (0, 31):
-        L = lens[b]
-        Kb, Vb = rows(b, "k").cpu(), rows(b, "v").cpu()
-        bt1, nb1 = synth.block_tables([L], P, seed, spare_blocks=1)
-        sl = synth.token_slots(bt1, [L], P)
-        kp = np.full(nb1 * Hkv * P * (d + 4), 0xFF, np.uint8)
-        vp = kp.copy()
-        oracle.kv_append("i8bf16", kp, vp, synth.raw_numpy(Kb), synth.raw_numpy(Vb), sl.numpy(), P=P, Hkv=Hkv, d=d)
-        ro, rl = oracle.decode_attention("i8bf16", kp, vp, synth.raw_numpy(qs[b:b + 1]), bt1.numpy(),
-                                         np.array([L], np.int32), P=P, Hkv=Hkv, d=d)
-        assert_close(SimpleNamespace(dtype="bf16"), (out[b:b + 1].astype(np.float64), lse[b:b + 1].astype(np.float64)),
-                     (ro, rl), f"int8 full size seq {b}")

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from harness import NAN_BITS, assert_close, log, max_err
+from harness import NAN_BITS, assert_close, log, max_err, oracle_sequence, window_tokens
 
 pytestmark = pytest.mark.gpu
 IN = {"i8bf16": "bf16", "i8f16": "f16"}
@@ -172,7 +172,7 @@ def test_ring_score_export():
 def test_full_size_kvsparse_ring_window_layer():
     """The KV-sparse Llama-3-8B shape's window layer (B=8, 32 q / 8 kv heads, d=128, bf16,
     L ~ U[7000, 30000], window 512 + 4 sinks) on a ring pool of 8 x 34 blocks: prefill of
-    L-1 tokens through the manager, one fused decode step, sampled sequences against the
+    L-1 tokens through the manager, one fused decode step, every sequence against the
     oracle."""
     import paged_kv_cache_16_amd as pkv
     name = "llama3_8b_kvsparse_bf16"
@@ -208,11 +208,11 @@ def test_full_size_kvsparse_ring_window_layer():
                                                  max_context_len=max(lens), window=512, num_sinks=4, ring_pages=R)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
-    for b in (0, 5, 7):
-        L = lens[b]
-        K, V = rows(b, "k").cpu()[None], rows(b, "v").cpu()[None]
-        ref_p = oracle_logical("bf16", qs[b:b + 1], K, V, [L], P=P, Hkv=Hkv, d=d, seed=seed)
-        ref = oracle.decode_attention("bf16", ref_p.kpool, ref_p.vpool, synth.raw_numpy(qs[b:b + 1]), ref_p.bt,
-                                      ref_p.lens, P=P, Hkv=Hkv, d=d, window=512, sinks=4)
+    for b, L in enumerate(lens):  # every sequence; the oracle holds only the attended tokens
+        toks = window_tokens(L, 512, 4)
+        idx = torch.as_tensor(toks, device="cuda")
+        ref = oracle_sequence("bf16", rows(b, "k")[idx].cpu(), rows(b, "v")[idx].cpu(),
+                              [(qs[b:b + 1], L, dict(window=512, sinks=4))], n_tokens=L, P=P, Hkv=Hkv, d=d,
+                              seed=seed, tokens=toks)[0]
         assert_close(_tol_case("bf16"), (out[b:b + 1], lse[b:b + 1]), ref, f"{name} ring seq {b}")
     bm.close()

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from harness import assert_close, log, make_case, oracle_attend
+from harness import assert_close, log, make_case, oracle_attend, oracle_pool, run_threads
 
 pytestmark = pytest.mark.gpu
 SCORE_TOL = 1e-5
@@ -157,7 +157,7 @@ def test_score_accumulates_over_steps():
 
 def test_score_export_full_size_llama3_layer():
     """Full Llama-3-8B-shaped layer (the benchmark's shape and launch configuration): every
-    (sequence, kv head) row of scores sums to G, and two sampled sequences match the oracle."""
+    (sequence, kv head) row of scores sums to G, and every sequence matches the oracle."""
     import paged_kv_cache_16_amd as pkv
     name, seed = "llama3_8b_layer_bf16", 7
     w = synth.WORKLOADS[name]
@@ -185,11 +185,16 @@ def test_score_export_full_size_llama3_layer():
     assert np.abs(sums - G).max() <= 1e-4
     got = gs.cpu().double().numpy()
     del gk, gv
-    for b in (0, 31):
-        L = lens[b]
-        c = make_case(seed, B=1, Hq=Hq, Hkv=Hkv, d=d, dtype=w.dtype, P=P, lens=[L], q=qs[b:b + 1],
-                      K=rows(b, "k").cpu()[None], V=rows(b, "v").cpu()[None], gpu_side=False)
-        ref = _oracle_scores(c, stride, torch.zeros((1, Hkv, stride)), {})
+
+    def one(b, kb, vb):  # the oracle's scores of sequence b, from zero
+        kp, _, bt1 = oracle_pool(w.dtype, kb, vb, n_tokens=lens[b], P=P, Hkv=Hkv, d=d, seed=seed)
+        return oracle.decode_scores(w.dtype, kp, synth.raw_numpy(qs[b:b + 1]), bt1, np.array([lens[b]], np.int32),
+                                    P=P, Hkv=Hkv, d=d, stride=stride)
+
+    tasks = [lambda b=b, kb=rows(b, "k").cpu(), vb=rows(b, "v").cpu(): one(b, kb, vb) for b in range(B)]
+    worst = 0.0
+    for b, ref in enumerate(run_threads(tasks)):  # every sequence
         err = float(np.abs(got[b:b + 1] - ref).max())
-        log(f"    seq {b}: max|score err| = {err:.3e}")
-        assert err <= SCORE_TOL
+        worst = max(worst, err)
+        assert err <= SCORE_TOL, f"seq {b}: max|score err| = {err:.3e}"
+    log(f"    every sequence: max|score err| = {worst:.3e}")
