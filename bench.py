@@ -5,14 +5,19 @@ Default workload: one Llama-3-8B-shaped attention layer at decode time — batch
 32 query / 8 kv heads (GQA 4), head_dim 128, bf16 cache, 16-token blocks, context
 lengths drawn uniformly from [1024, 4096], random block tables. One step is the whole
 hot path over one batch: paged_decode_append_attention, i.e. the append of the 32 new
-tokens fused into the persistent split-K attention kernel, then the log-sum-exp combine. Several replica caches (own pools, tables, queries)
-are cycled so that consecutive steps never find their K/V in the 256 MB last-level
-cache; every replica has the same context lengths, so the bytes per step are fixed.
+tokens fused into the persistent split-K attention kernel, then the log-sum-exp combine.
+Several replica caches (own pools, tables, queries) are cycled so that consecutive steps
+never find their K/V in the 256 MB last-level cache; every replica has the same context
+lengths, so the bytes per step are fixed.
 
-Prints one JSON line. value = algorithmic KV bytes per step (the attended tokens' K and
-V rows, sum(L) * 2 * Hkv * d * 2 bytes) / wall time per step. roofline = the split
-kernel alone: the same bytes / its mean duration from HIP events recorded on the
-launch stream around every 8th timed launch (--event-every).
+Prints one JSON line. value = algorithmic KV bytes per step (the attended tokens' K and V
+rows, sum(L) * 2 * Hkv * d * 2 bytes) / wall time per step, over the timed steps, which run
+with no event records at all. roofline = the main attention kernel alone: the same bytes /
+its mean duration, from HIP events the library records on its launch stream around the
+kernel, in a separate loop of at least 50 launches after the timed region. cpu_baseline =
+the oracle timed on the host (one thread, and one GPU's share of host threads).
+
+--workload selects one of the other four workloads (report lines with the same fields).
 """
 from __future__ import annotations
 
@@ -30,11 +35,13 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode-attention KV GB/s and % of HBM peak; decode steps/s per layer"
 HBM_PEAK_GBS = 8000.0
+ORACLE_THREADS = 16  # host threads of one GPU's share of the box (at most nproc)
+MIN_EVENT_LAUNCHES = 50
 
-
-# The sources that define the measured kernel and its launch (grid, split plan): a change to
+# The sources that define the measured kernels and their launch (grid, split plan): a change to
 # any of them invalidates the committed HBM counters.
-KERNEL_SOURCES = ("api.hip", "pkv_device.h", "pkv_internal.h", "pkv_plan.h", "stream.hip")
+KERNEL_SOURCES = ("api.hip", "append.hip", "decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_plan.h",
+                  "stream.hip")
 
 
 def kernel_source_hash() -> str:
@@ -49,12 +56,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, split_tokens: int):
-    """HBM bytes per launch of the main kernel from the committed rocprofv3 --pmc summary,
-    or None when no summary matches the current kernel sources."""
-    if split_tokens:
-        return None
-    path = os.path.join(ROOT, "profiles", f"decode_stream_kernel_{workload}_traffic.json")
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 --pmc record
+    (profiles/<kernel>_<workload>_traffic.json), or None when none matches the current kernel
+    sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -75,11 +81,10 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--seed", type=int, default=2026)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU baseline: run the oracle on whole sequences of the workload until "
-                         "this much oracle time is spent (0 = skip)")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="record the kernel's HIP events on every n-th call only: an event pair costs "
-                         "the step a few microseconds of queue work, so the step clock runs without most")
+                    help="CPU baseline: oracle time to spend single-threaded on a sample of the workload "
+                         "(0 = skip)")
+    ap.add_argument("--event-launches", type=int, default=100,
+                    help="launches of the separate event-timed loop after the timed region (at least 50)")
     ap.add_argument("--no-graph", action="store_true", help="multi-layer modes: skip the HIP-graph timing")
     ap.add_argument("--scores", action="store_true",
                     help="default workload: every step also exports the decode-time KV scores "
@@ -167,6 +172,51 @@ class HipEvents:
         self.lib.hipEventDestroy(h)
 
 
+def host_info() -> dict:
+    """The host's logical CPU count and CPU model, as this process sees them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def event_loop(call, n: int, hip) -> list:
+    """Runs call(timing) n times, each launch with its own event pair that the library records
+    on its launch stream right around the main attention kernel; returns the durations (ms),
+    sorted."""
+    import torch
+    evs = [(hip.create(), hip.create()) for _ in range(n)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    ms = sorted(hip.elapsed_ms(a, b) for a, b in evs)
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    return ms
+
+
+def roofline(kernel: str, bytes_per_launch: int, ms: list, traffic, probe) -> dict:
+    """The roofline object of one kernel: algorithmic bytes per launch / mean event duration."""
+    mean = statistics.fmean(ms)
+    q = lambda f: ms[min(len(ms) - 1, int(f * len(ms)))]
+    achieved = bytes_per_launch / (mean * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_unit": "bytes per launch",
+         "bytes_per_launch": bytes_per_launch, "mean_us": round(mean * 1e3, 3), "p10_us": round(q(0.1) * 1e3, 3),
+         "p50_us": round(q(0.5) * 1e3, 3), "p90_us": round(q(0.9) * 1e3, 3), "samples": len(ms),
+         "timing": "separate loop after the timed region, one event pair per launch"}
+    if probe:
+        r.update(read_probe_gbs=probe["gbs"], frac_of_read_probe=round(achieved / probe["gbs"], 4), read_probe=probe)
+    return r
+
+
 def build_replica(w, lens, seed, r, dev, kv_dtype=None):
     """One replica of the workload's caches and step inputs. kv_dtype "int8": an INT8 cache
     filled by the quantising append from the same rows."""
@@ -199,61 +249,165 @@ def build_replica(w, lens, seed, r, dev, kv_dtype=None):
     return rep
 
 
-ORACLE_THREADS = 16  # host threads one GPU's share of the machine runs on
+# ---------------------------------------------------------------------------------- CPU baseline
+# The oracle as it stands (plain fp64 C), timed on the host on a bounded sample of the same
+# workload: single-threaded, then the same sample as one oracle call per sequence on a pool of
+# host threads (the C oracle runs outside the interpreter lock). Only the attention calls are
+# timed; building the oracle's pools is not.
+def _oracle_seq(dtype, K_rows, V_rows, n_tokens, P, Hkv, d, seed, tokens=None):
+    """An oracle pool holding one sequence's rows (of `tokens`, default 0 .. m-1), under a
+    seeded table. Returns (kpool, vpool, block_table [1, pages])."""
+    import numpy as np
+    import synth
+    import oracle
+    bt, nb = synth.block_tables([n_tokens], P, seed, "cpu-baseline")
+    raw_t = np.float32 if dtype == "f32" else np.uint16
+    kp = np.zeros(nb * Hkv * P * d, raw_t)
+    vp = np.zeros_like(kp)
+    t = np.arange(K_rows.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
+    slots = (bt[0].numpy().astype(np.int64)[t // P] * P + t % P).astype(np.int32)
+    oracle.kv_append(dtype, kp, vp, synth.raw_numpy(K_rows), synth.raw_numpy(V_rows), slots, P=P, Hkv=Hkv, d=d)
+    return kp, vp, bt.numpy()
 
 
-def cpu_baseline(w, lens, seed, reps, seconds, dev):
-    """Times the oracle, as it is, on whole sequences of the workload (replica 0, then 1, ...)
-    until `seconds` of oracle time are spent. Only the attention call is timed. The same
-    sequences are then run again with one oracle call per sequence on a pool of host threads
-    (the C oracle runs outside the interpreter lock), timed as a whole."""
+def _time_calls(builders, budget_s):
+    """builders: callables that prepare one oracle call (untimed) and return it. Prepares and
+    times the calls one by one until budget_s is spent (at least one); then runs the same calls on
+    the thread pool, timed as a whole. Returns (n_done, single_s, parallel_s, threads)."""
     from concurrent.futures import ThreadPoolExecutor
+    fns, single = [], 0.0
+    for build in builders:
+        if fns and single >= budget_s:
+            break
+        fn = build()
+        t0 = time.perf_counter()
+        fn()
+        single += time.perf_counter() - t0
+        fns.append(fn)
+    threads = max(1, min(ORACLE_THREADS, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda f: f(), fns))
+        par = time.perf_counter() - t0
+    return len(fns), single, par, threads
 
+
+def cpu_baseline(w, args, dev, lens=None):
+    """The oracle's time on a bounded sample of workload w, scaled to the workload's own unit:
+    per attention call (one layer of the batch) for single-layer workloads, per layer-step and
+    per decode step for multi-layer ones. value = algorithmic K/V bytes / oracle seconds (GB/s,
+    one thread)."""
     import numpy as np
     import torch
 
     import oracle
     import synth
 
-    P, d, Hkv = w.block_size, w.head_dim, w.kv_heads
-    total_s, total_bytes, total_tokens, nseq = 0.0, 0, 0, 0
-    calls = []
-    for r, rep in enumerate(reps):
+    B, P, d, Hkv, Hq = w.batch, w.block_size, w.head_dim, w.kv_heads, w.q_heads
+    seed, budget = args.seed, args.cpu_seconds
+    bpt = w.kv_bytes_per_token()
+    if lens is None:
+        lens = [w.ctx_lo] * B if w.ctx_lo == w.ctx_hi else \
+            synth.uniform_lengths(B, w.ctx_lo, w.ctx_hi, seed, w.name).tolist()
+    if w.steps > 1:
+        lens = [L + 1 for L in lens]  # the first decode step (cached context plus the new token)
+
+    def rows(b, tag, n):
+        return synth.normal((n, Hkv, d), seed, w.name, "cpu", b, tag, dtype=w.dtype, device=dev).cpu()
+
+    def seq_call(b, L, okw=None, tokens=None):
+        """A timed closure: the oracle's attention over sequence b (its pool built now)."""
+        okw = okw or {}
+        n = len(tokens) if tokens is not None else L
+        idx = None if tokens is None else torch.as_tensor(tokens)
+        K, V = rows(b, "k", L), rows(b, "v", L)
+        if idx is not None:
+            K, V = K[idx], V[idx]
+        kp, vp, bt = _oracle_seq(w.dtype, K, V, L, P, Hkv, d, seed, tokens)
+        q = synth.raw_numpy(synth.normal((1, Hq, d), seed, w.name, "cpu", b, "q", dtype=w.dtype))
+        cl = np.array([L], np.int32)
+        assert n == K.shape[0]
+        return lambda: oracle.decode_attention(w.dtype, kp, vp, q, bt, cl, P=P, Hkv=Hkv, d=d, **okw)
+
+    info = host_info()
+    res = {"unit": "GB/s", "kind": "oracle", **info}
+    if w.pages_per_step:  # whole calls: every sequence over its page list
+        pl = synth.page_lists(lens, P, w.pages_per_step, seed, w.name, "cpu").numpy()
+        calls = []
         for b, L in enumerate(lens):
-            if total_s >= seconds:
-                break
-            kb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "k", dtype=w.dtype, device=dev)
-            vb = synth.normal((L - 1, Hkv, d), seed, w.name, r, b, "v", dtype=w.dtype, device=dev)
-            kb = torch.cat([kb, rep["k_new"][b:b + 1]]).cpu()
-            vb = torch.cat([vb, rep["v_new"][b:b + 1]]).cpu()
-            bt, nb = synth.block_tables([L], P, seed, "cpu", r, b)
-            kp = np.zeros(nb * Hkv * P * d, np.uint16)
-            vp = np.zeros_like(kp)
-            oracle.kv_append(w.dtype, kp, vp, synth.raw_numpy(kb), synth.raw_numpy(vb),
-                             synth.token_slots(bt, [L], P).numpy(), P=P, Hkv=Hkv, d=d)
-            q = synth.raw_numpy(rep["q"][b:b + 1].cpu())
-            call = (kp, vp, q, bt.numpy(), np.array([L], np.int32))
-            calls.append(call)
+            toks = np.concatenate([np.arange(p * P, min((p + 1) * P, L)) for p in pl[b] if p >= 0])
+            calls.append(seq_call(b, L, dict(page_list=pl[b:b + 1]), toks))
+        call_bytes = B * w.pages_per_step * P * bpt
+        reps = []
+        t_single = 0.0
+        while not reps or t_single < budget:
             t0 = time.perf_counter()
-            oracle.decode_attention(w.dtype, *call, P=P, Hkv=Hkv, d=d)
-            total_s += time.perf_counter() - t0
-            total_bytes += L * w.kv_bytes_per_token()
-            total_tokens += L
-            nseq += 1
-    threads = max(1, min(ORACLE_THREADS, os.cpu_count() or 1))
-    with ThreadPoolExecutor(max_workers=threads) as ex:
+            for fn in calls:
+                fn()
+            reps.append(time.perf_counter() - t0)
+            t_single += reps[-1]
+        _, _, par, threads = _time_calls([lambda fn=fn: fn for fn in calls], 0.0)
+        per_call = statistics.fmean(reps)
+        res.update(value=round(call_bytes / per_call / 1e9, 4), cores=1, seconds_per_call=round(per_call, 4),
+                   sample=f"{len(reps)} whole calls ({B} sequences x {w.pages_per_step} pages of {P} tokens, "
+                          f"all {Hq} heads), single-threaded fp64 C oracle, {t_single:.2f} s",
+                   parallel={"value": round(call_bytes / par / 1e9, 4), "unit": "GB/s", "cores": threads,
+                             "seconds_per_call": round(par, 4),
+                             "sample": f"one whole call, one oracle call per sequence on {threads} host threads"})
+        return res
+    if w.name == "tiny_mha_f32":  # whole calls
+        fn = seq_call(0, lens[0])
+        reps, t_single = [], 0.0
+        while not reps or t_single < min(budget, 2.0):
+            t0 = time.perf_counter()
+            fn()
+            reps.append(time.perf_counter() - t0)
+            t_single += reps[-1]
+        per_call = statistics.fmean(reps)
+        call_bytes = sum(lens) * bpt
+        res.update(value=round(call_bytes / per_call / 1e9, 4), cores=1, seconds_per_call=round(per_call, 6),
+                   sample=f"{len(reps)} whole calls (1 sequence of {lens[0]} tokens, {Hq} heads), "
+                          f"single-threaded fp64 C oracle, {t_single:.2f} s")
+        return res
+    # sequences of the workload (full attention), sampled in order until the budget is spent
+    builders = [lambda b=b, L=L: seq_call(b, L) for b, L in enumerate(lens)]
+    seq_bytes = [L * bpt for L in lens]
+    done, single, par, threads = _time_calls(builders, budget if not w.window_layers else budget / 2)
+    sb = sum(seq_bytes[:done])
+    rate1, rate_p = sb / single, sb / par
+    full_call = sum(lens) * bpt  # one full layer of the batch
+    res.update(value=round(rate1 / 1e9, 4), cores=1,
+               sample=f"{done} whole sequences ({sum(lens[:done])} tokens, all {Hq} query heads, full attention) "
+                      f"of the workload, one oracle call each, single-threaded fp64 C oracle, {single:.2f} s; "
+                      f"per-call figures scale this rate to the whole batch",
+               parallel={"value": round(rate_p / 1e9, 4), "unit": "GB/s", "cores": threads, "seconds": round(par, 3),
+                         "sample": f"the same sequences, one oracle call per sequence on {threads} host threads, "
+                                   f"timed as a whole"})
+    if w.layers == 1:
+        res["seconds_per_call"] = round(full_call / rate1, 4)
+        res["parallel"]["seconds_per_call"] = round(full_call / rate_p, 4)
+        return res
+    n_full = w.layers - len(w.window_layers)
+    per_full = full_call / rate1
+    res["seconds_per_layer_step"] = round(per_full, 4) if not w.window_layers else None
+    if w.window_layers:  # window layer-steps timed whole: every sequence, window + sinks
+        wcalls = []
+        for b, L in enumerate(lens):
+            toks = np.concatenate([np.arange(min(w.sinks, L)), np.arange(max(min(w.sinks, L), L - w.window), L)])
+            wcalls.append(seq_call(b, L, dict(window=w.window, sinks=w.sinks), toks))
         t0 = time.perf_counter()
-        list(ex.map(lambda call: oracle.decode_attention(w.dtype, *call, P=P, Hkv=Hkv, d=d), calls))
-        par_s = time.perf_counter() - t0
-    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{nseq} whole sequences ({total_tokens} tokens, all {w.q_heads} query heads, "
-                       f"full attention) of the same workload, one oracle call each, "
-                       f"single-threaded fp64 C oracle, {total_s:.2f} s of oracle time",
-                seconds=round(total_s, 3),
-                parallel=dict(value=round(total_bytes / par_s / 1e9, 4), unit="GB/s", cores=threads,
-                              seconds=round(par_s, 3),
-                              sample="the same sequences, one oracle call per sequence on a pool of "
-                                     f"{threads} host threads, timed as a whole"))
+        for fn in wcalls:
+            fn()
+        per_win = time.perf_counter() - t0
+        res["seconds_per_full_layer_step"] = round(per_full, 4)
+        res["seconds_per_window_layer_step"] = round(per_win, 4)
+        res["seconds_per_step"] = round(n_full * per_full + len(w.window_layers) * per_win, 3)
+        res["sample"] += (f"; window layer-step: the {B} window calls (window {w.window} + {w.sinks} sinks) "
+                          f"timed whole")
+    else:
+        res["seconds_per_step"] = round(w.layers * per_full, 3)
+        res["sample"] += f"; lengths at the first decode step ({min(lens)}..{max(lens)})"
+    return res
 
 
 def _layer_caches(w, lens, P, seed, dev, tag, bt, nb=None, slots=None):
@@ -323,6 +477,124 @@ def _policy_setup(w, base, steps, P, bt, nb, dev):
                 host_us=host_us)
 
 
+def run_layer(w, args, dev):
+    """Single-layer workloads (the default Llama-3-8B-shaped layer and its variants, and the
+    tiny MHA check): one decode step of the layer per timed step."""
+    import itertools
+
+    import torch
+
+    import paged_kv_cache_16_amd as pkv
+    import synth
+
+    variant = args.context > 0 or args.tp_share > 1
+    if variant:
+        if w.kv_heads % args.tp_share:
+            print(f"bench.py: {w.kv_heads} kv heads do not split {args.tp_share} ways", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, kv_heads=w.kv_heads // args.tp_share, q_heads=w.q_heads // args.tp_share)
+        if args.tp_share > 1 and args.replicas == 8:
+            args.replicas = 16
+    if args.context > 0:
+        lens = [args.context] * w.batch
+    elif w.ctx_lo == w.ctx_hi:
+        lens = [w.ctx_lo] * w.batch
+    else:
+        lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
+    kv_bytes = sum(lens) * w.kv_bytes_per_token()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    reps = [build_replica(w, lens, args.seed, r, dev, args.kv_dtype) for r in range(args.replicas)]
+    if args.kv_dtype == "int8":  # K and V: d int8 bytes + one fp32 scale per token and kv head
+        kv_bytes = sum(lens) * 2 * w.kv_heads * (w.head_dim + 4)
+    torch.cuda.synchronize()
+    B, Hq, d = w.batch, w.q_heads, w.head_dim
+    mcl = max(lens)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens, scores=args.scores)
+    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scores = torch.zeros((B, w.kv_heads, mcl), dtype=torch.float32, device=dev) if args.scores else None
+    hip = HipEvents()
+
+    def step(rep, ev=None):
+        # one decode step of the layer: append of the 32 new tokens + attention, fused
+        pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
+                                          rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
+                                          split_tokens=args.split_tokens, out=out, lse=lse,
+                                          workspace=workspace, timing=ev, scores=scores)
+
+    for i in range(args.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the main kernel alone: a separate loop, one event pair per launch, replicas cycled on
+    ctr = itertools.count(args.steps)
+    kern_ms = event_loop(lambda ev: step(reps[next(ctr) % len(reps)], ev),
+                         max(MIN_EVENT_LAUNCHES, args.event_launches), hip)
+    probe = read_probe_gbs(args.read_probe_mib, dev) if args.read_probe_mib > 0 else None
+
+    dt = {"bf16": "BF16", "f16": "F16", "f32": "F32"}[w.dtype]
+    if args.kv_dtype == "int8":
+        kname = f"decode_stream_kernel<I8B,{d},full>"
+    elif args.split_tokens:
+        kname = f"decode_split_kernel<{dt},{d},full>"
+    else:
+        kname = f"decode_stream_kernel<{dt},{d},full,fused append>"
+    plain = not (args.scores or args.kv_dtype or variant or args.split_tokens)
+    step_desc = ("paged_decode_append_attention: append of the new tokens fused into the persistent split "
+                 "kernel, then the LSE combine")
+    if args.kv_dtype == "int8":
+        step_desc = ("paged_decode_append_attention on an INT8 cache: quantising append of the new tokens, "
+                     "then the persistent split kernel and the LSE combine")
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": args.kv_dtype or w.dtype,
+            "context": (f"all {lens[0]}" if len(set(lens)) == 1 else f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}")
+            + f", sum {sum(lens)}, max {mcl}",
+            "tp_share": args.tp_share,
+            "replicas": args.replicas, "split_tokens": args.split_tokens,
+            "step": step_desc + (", plus the decode-time KV score export" if args.scores else ""),
+            "kv_dtype": args.kv_dtype or w.dtype,
+            "parallelism": "single GPU",
+        },
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": roofline(kname, kv_bytes, kern_ms,
+                             measured_traffic("decode_stream_kernel", w.name) if plain else None, probe),
+    }
+    return res, lens, variant
+
+
 def run_multilayer(w, args, dev):
     """Decode steps over all layers: per layer, append of the batch's new tokens and attention
     (window + sinks on the window layers); the context advances once per step after the last
@@ -371,49 +643,57 @@ def run_multilayer(w, args, dev):
                      dtype=torch.uint8, device=dev)
     hip = HipEvents()
 
-    every = max(1, args.event_every)
-
-    def step(s, evs=None, s_i=0):
-        # events on the layers with (s_i + layer) % every == 0, so the sample rotates over layers
+    def step(s, layer_timing=None):
         for li, ly in enumerate(layers):
-            ev = evs[li] if evs is not None and (s_i + li) % every == 0 else None
             pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], ly["slots"][s],
                                               ly["bt"], lens_s[s], max_context_len=mcl, window=ly["window"],
                                               num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
-                                              workspace=ws, timing=ev, ring_pages=ly["ring"])
+                                              workspace=ws, ring_pages=ly["ring"],
+                                              timing=layer_timing(li) if layer_timing else None)
 
     reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
     for s in range(min(steps, 4)):
         step(s)
     torch.cuda.synchronize()
-    evs = [[(hip.create(), hip.create()) for _ in layers] for _ in range(reps * steps)]
     t0 = time.perf_counter()
-    i = 0
     for _ in range(reps):
         for s in range(steps):
-            step(s, evs[i], i)
-            i += 1
+            step(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     n_steps = reps * steps
     bytes_total = 0
-    full_us, win_us = [], []
     for s_i in range(n_steps):
         s = s_i % steps
-        for li, ly in enumerate(layers):
+        for ly in layers:
             if ly["window"]:
                 att = sum(min(L + s, ly["window"] + min(w.sinks, L + s)) for L in base)
             else:
                 att = sum(L + s for L in base)
             bytes_total += att * w.kv_bytes_per_token()
-            if (s_i + li) % every:
-                continue
-            us = hip.elapsed_ms(*evs[s_i][li]) * 1e3
-            (win_us if ly["window"] else full_us).append(us)
-    for e in evs:
-        for a, b in e:
-            hip.destroy(a)
-            hip.destroy(b)
+
+    # the kernels alone: a separate loop of whole steps, every layer's main kernel between its
+    # own event pair (steps cycled from the first)
+    ev_steps = max(1, -(-MIN_EVENT_LAUNCHES // max(1, w.layers - len(w.window_layers))))
+    ev_steps = max(ev_steps, min(steps, 4))
+    evs = [[(hip.create(), hip.create()) for _ in layers] for _ in range(ev_steps)]
+    for i in range(ev_steps):
+        step(i % steps, layer_timing=lambda li, i=i: evs[i][li])
+    torch.cuda.synchronize()
+    full_s, win_s = [], []  # (bytes, ms) per launch
+    for i in range(ev_steps):
+        s = i % steps
+        for li, ly in enumerate(layers):
+            ms = hip.elapsed_ms(*evs[i][li])
+            if ly["window"]:
+                att = sum(min(L + s, ly["window"] + min(w.sinks, L + s)) for L in base)
+                win_s.append((att * w.kv_bytes_per_token(), ms))
+            else:
+                full_s.append((sum(L + s for L in base) * w.kv_bytes_per_token(), ms))
+            hip.destroy(evs[i][li][0])
+            hip.destroy(evs[i][li][1])
+    full_us = [m * 1e3 for _, m in full_s]
+    win_us = [m * 1e3 for _, m in win_s]
     step_ms = elapsed * 1e3 / n_steps
     graph_ms = None
     if not args.no_graph:
@@ -454,6 +734,17 @@ def run_multilayer(w, args, dev):
         "attention_us_window_layer_mean": round(statistics.fmean(win_us), 2) if win_us else None,
         "hbm_frac_of_peak": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBS, 4),
     }
+    dt = {"bf16": "BF16", "f16": "F16", "f32": "F32"}[w.dtype]
+    if full_s:
+        res["roofline"] = roofline(f"decode_stream_kernel<{dt},{d},full,fused append>",
+                                   int(statistics.fmean(b for b, _ in full_s)), sorted(m for _, m in full_s),
+                                   None if policy else measured_traffic("decode_stream_kernel", w.name), None)
+        res["roofline"]["note"] = "full layers; bytes_per_launch is the mean over the sampled steps"
+    if win_s:
+        res["roofline_window_layer"] = roofline(
+            f"decode_split_kernel<{dt},{d},window,one kernel,fused append>",
+            int(statistics.fmean(b for b, _ in win_s)), sorted(m for _, m in win_s),
+            None if policy else measured_traffic("decode_split_kernel", w.name + "_window"), None)
     blk_bytes = 2 * Hkv * P * d * synth.DTYPE_BYTES[w.dtype]  # K and V of one block
     n_win = len(w.window_layers)
     res["kv_pool_bytes"] = w.layers * nb * blk_bytes
@@ -530,15 +821,18 @@ def run_page_selected(w, args, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    every = max(1, args.event_every)
-    evs = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)]
-    sevs = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)] if loop else None
     t0 = time.perf_counter()
     for i in range(args.steps):
-        on = i % every == 0
-        step(i, evs[i // every] if on else None, sevs[i // every] if on and loop else None)
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the kernels alone: a separate loop, one event pair per launch
+    n_ev = max(MIN_EVENT_LAUNCHES, args.event_launches)
+    evs = [(hip.create(), hip.create()) for _ in range(n_ev)]
+    sevs = [(hip.create(), hip.create()) for _ in range(n_ev)] if loop else None
+    for i in range(n_ev):
+        step(i, evs[i], sevs[i] if loop else None)
+    torch.cuda.synchronize()
     kern = sorted(hip.elapsed_ms(a, b) for a, b in evs)
     sel = sorted(hip.elapsed_ms(a, b) for a, b in sevs) if loop else []
     for a, b in evs + (sevs or []):
@@ -565,6 +859,9 @@ def run_page_selected(w, args, dev):
         **({"closed_loop": "per-page score export + paged_select_pages each step",
             "select_pages_us_mean": round(statistics.fmean(sel) * 1e3, 3),
             "select_pages_us_p50": round(sel[len(sel) // 2] * 1e3, 3)} if loop else {}),
+        "roofline": roofline(f"decode_split_kernel<F16,{d},pages,one kernel,fused append"
+                             + (",scores>" if loop else ">"), att_bytes, kern,
+                             None if loop else measured_traffic("decode_split_kernel", w.name), None),
     }
 
 
@@ -578,7 +875,7 @@ def main():
 
     import torch
 
-    import paged_kv_cache_16_amd as pkv
+    import paged_kv_cache_16_amd  # noqa: F401  (fails loudly when the library is not built)
     import synth
 
     if not torch.cuda.is_available():
@@ -587,129 +884,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
+    lens, baseline_ok = None, True
     if w.layers > 1:
-        print(json.dumps(run_multilayer(w, args, dev)), flush=True)
-        return
-    if w.pages_per_step:
-        print(json.dumps(run_page_selected(w, args, dev)), flush=True)
-        return
-    variant = args.context > 0 or args.tp_share > 1
-    if variant:
-        if w.kv_heads % args.tp_share:
-            print(f"bench.py: {w.kv_heads} kv heads do not split {args.tp_share} ways", file=sys.stderr)
-            sys.exit(2)
-        w = dataclasses.replace(w, kv_heads=w.kv_heads // args.tp_share, q_heads=w.q_heads // args.tp_share)
-        if args.tp_share > 1 and args.replicas == 8:
-            args.replicas = 16
-    if args.context > 0:
-        lens = [args.context] * w.batch
+        res = run_multilayer(w, args, dev)
+        baseline_ok = not args.policy
+    elif w.pages_per_step:
+        res = run_page_selected(w, args, dev)
+        baseline_ok = not args.loop
     else:
-        lens = synth.uniform_lengths(w.batch, w.ctx_lo, w.ctx_hi, args.seed, w.name).tolist()
-    kv_bytes = sum(lens) * w.kv_bytes_per_token()
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    reps = [build_replica(w, lens, args.seed, r, dev, args.kv_dtype) for r in range(args.replicas)]
-    if args.kv_dtype == "int8":  # K and V: d int8 bytes + one fp32 scale per token and kv head
-        kv_bytes = sum(lens) * 2 * w.kv_heads * (w.head_dim + 4)
-    torch.cuda.synchronize()
-    B, Hq, d = w.batch, w.q_heads, w.head_dim
-    mcl = max(lens)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.workspace_size(reps[0]["k"], B, Hq, mcl, split_tokens=args.split_tokens, scores=args.scores)
-    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    scores = torch.zeros((B, w.kv_heads, mcl), dtype=torch.float32, device=dev) if args.scores else None
-    hip = HipEvents()
-
-    def step(rep, ev=None):
-        # one decode step of the layer: append of the 32 new tokens + attention, fused
-        pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
-                                          rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
-                                          split_tokens=args.split_tokens, out=out, lse=lse,
-                                          workspace=workspace, timing=ev, scores=scores)
-
-    for i in range(args.warmup):
-        step(reps[i % len(reps)])
-    torch.cuda.synchronize()
-
-    # HIP events recorded by the library on the launch stream, right around the main kernel,
-    # on every event_every-th step of the timed region.
-    every = max(1, args.event_every)
-    events = [(hip.create(), hip.create()) for _ in range(0, args.steps, every)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(reps[i % len(reps)], events[i // every] if i % every == 0 else None)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    kern_ms = sorted(hip.elapsed_ms(a, b) for a, b in events)
-    for a, b in events:
-        hip.destroy(a)
-        hip.destroy(b)
-    kern_mean = statistics.fmean(kern_ms)
-    q = lambda f: kern_ms[min(len(kern_ms) - 1, int(f * len(kern_ms)))]
-    achieved = kv_bytes / (kern_mean * 1e-3) / 1e9
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    probe = read_probe_gbs(args.read_probe_mib, dev) if args.read_probe_mib > 0 else None
-
-    res = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-            "head_dim": w.head_dim, "block_size": w.block_size, "cache_dtype": w.dtype,
-            "context": (f"all {args.context}" if args.context > 0 else f"U[{w.ctx_lo},{w.ctx_hi}] seed {args.seed}")
-            + f", sum {sum(lens)}, max {mcl}",
-            "tp_share": args.tp_share,
-            "replicas": args.replicas, "split_tokens": args.split_tokens,
-            "step": ("paged_decode_append_attention: append of the 32 new tokens fused into the "
-                     "persistent split kernel, then the LSE combine" if args.kv_dtype != "int8" else
-                     "paged_decode_append_attention on an INT8 cache: quantising append of the 32 new "
-                     "tokens, then the persistent split kernel and the LSE combine")
-                    + (", plus the decode-time KV score export" if args.scores else ""),
-            "kv_dtype": args.kv_dtype or w.dtype,
-            "parallelism": "single GPU",
-        },
-        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-        "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
-        "kv_bytes_per_step": kv_bytes,
-        "roofline": {
-            "bound": "hbm", "kernel": ("decode_stream_kernel<I8B,128,full>" if args.kv_dtype == "int8" else
-                                       "decode_stream_kernel<BF16,128,full,fused append>")
-            if args.split_tokens == 0 else "decode_split_kernel<BF16,128,full>",
-            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (args.scores or args.kv_dtype or variant) else measured_traffic(w.name, args.split_tokens),
-            "traffic_unit": "bytes per launch",
-            "bytes_per_launch": kv_bytes, "mean_us": round(kern_mean * 1e3, 3),
-            "p10_us": round(q(0.1) * 1e3, 3), "p50_us": round(q(0.5) * 1e3, 3),
-            "p90_us": round(q(0.9) * 1e3, 3), "samples": len(kern_ms),
-            "read_probe_gbs": probe["gbs"] if probe else None,
-            "frac_of_read_probe": round(achieved / probe["gbs"], 4) if probe else None,
-            "read_probe": probe,
-        },
-    }
-    if args.cpu_seconds > 0 and not args.kv_dtype and not variant:
-        res["cpu_baseline"] = cpu_baseline(w, lens, args.seed, reps, args.cpu_seconds, dev)
+        res, lens, variant = run_layer(w, args, dev)
+        baseline_ok = not (args.kv_dtype or variant or args.scores or args.split_tokens)
+    if args.cpu_seconds > 0 and baseline_ok:
+        res["cpu_baseline"] = cpu_baseline(w, args, dev, lens)
     print(json.dumps(res), flush=True)
 
 

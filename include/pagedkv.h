@@ -33,9 +33,9 @@
  *     every buffer (including workspaces); the library never allocates or frees
  *     device memory (the host block manager's own host memory is allocated by
  *     pkv_bm_create and freed by pkv_bm_destroy) and keeps no state between calls
- *     other than the device error word (pkv_device_errors) and per-device
- *     properties it asks the runtime for once (compute units, occupancy, LDS
- *     size), so calls are reentrant.
+ *     other than the device error word (pkv_device_errors), a thread's profiling
+ *     events (pkv_profile_events) and per-device properties it asks the runtime for once (compute units,
+ *     occupancy), so calls are reentrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *     enqueued asynchronously; no entry point other than pkv_device_errors
  *     synchronises the host.
@@ -165,8 +165,6 @@ typedef struct {
     int32_t split_tokens;    /* 0: automatic work split (see paged_decode_attention).
                                 Otherwise fixed split-K partitions of this many tokens,
                                 rounded up to a multiple of 16 and clamped to [16, 4096]. */
-    void* timing_start;      /* nullable hipEvent_t: recorded on the stream right before the */
-    void* timing_stop;       /* main attention kernel, and right after it (profiling hook) */
     float* score_acc;        /* nullable: score export, see above (device) */
     int32_t score_stride;    /* row length of score_acc */
     int32_t score_block;     /* tokens per score entry; 0 or 1: one entry per token */
@@ -428,6 +426,14 @@ int64_t pkv_bm_context_len(const pkv_block_manager* bm, int32_t seq_id);
 /* Blocks of group g held by all sequences (the sum of pkv_policy_blocks over them); -1 for
  * a bad group. */
 int64_t pkv_bm_blocks_in_use(const pkv_block_manager* bm, int32_t group);
+
+/* Profiling hook (measurement only). Sets, for the calling host thread, two hipEvent_t
+ * handles (passed as void*) that every later decode call of that thread (paged_decode_attention,
+ * _append_attention, _partial) records on its stream right before its main attention
+ * kernel and right after it; (NULL, NULL) clears them. This per-thread pair is the one piece of
+ * state the library keeps for the caller. The records add queue work to every call, so the hook
+ * stays clear outside measurement. Always returns PKV_OK. */
+pkv_status pkv_profile_events(void* start_event, void* stop_event);
 
 /* Device error word. The kernels set these bits when they skip work whose device-side
  * precondition does not hold (they never fault on it):

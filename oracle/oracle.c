@@ -508,6 +508,7 @@ int oracle_decode_attention_split(int dt, int64_t num_blocks, int P, int Hkv, in
                 int64_t t = toks[k], u;
                 if (pages) {
                     int e = page_entry(pages, pps, t / P);
+                    if (e < 0) { rc = ORC_ERR_ARG; break; } /* an attended token lies on a listed page */
                     u = (int64_t)e * (P / 16) + (t % P) / 16;
                 } else {
                     if (t / 16 != last_unit) { ++unit_rank; last_unit = t / 16; }

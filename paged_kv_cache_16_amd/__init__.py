@@ -23,7 +23,7 @@ __all__ = [
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
     "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks", "device_errors",
-    "read_probe",
+    "read_probe", "profile_events",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -49,9 +49,8 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("window", _i32), ("num_sinks", _i32), ("page_list", _vp),
-                ("pages_per_seq", _i32), ("split_tokens", _i32), ("timing_start", _vp),
-                ("timing_stop", _vp), ("score_acc", _vp), ("score_stride", _i32), ("score_block", _i32),
-                ("ring_pages", _i32)]
+                ("pages_per_seq", _i32), ("split_tokens", _i32), ("score_acc", _vp), ("score_stride", _i32),
+                ("score_block", _i32), ("ring_pages", _i32)]
 
 
 class LayerGroup(ctypes.Structure):
@@ -109,6 +108,8 @@ _lib.pkv_device_errors.restype = ctypes.c_int
 _lib.pkv_device_errors.argtypes = [_vp, _i32, _vp]
 _lib.pkv_read_probe.restype = ctypes.c_int
 _lib.pkv_read_probe.argtypes = [_vp, ctypes.c_size_t, _i32, _vp, ctypes.c_size_t, _vp, _vp]
+_lib.pkv_profile_events.restype = ctypes.c_int
+_lib.pkv_profile_events.argtypes = [_vp, _vp]
 _lib.pkv_status_string.restype = ctypes.c_char_p
 _lib.pkv_status_string.argtypes = [ctypes.c_int]
 
@@ -228,12 +229,10 @@ def new_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int
     return torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
 
 
-def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, scores=None,
+def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, scores=None,
           score_block=1, ring_pages=0) -> DecodeOpts:
-    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, None, None, 0,
+    o = DecodeOpts(int(window), int(num_sinks), None, 0, int(split_tokens), None, 0,
                    int(score_block), int(ring_pages))
-    if timing is not None:
-        o.timing_start, o.timing_stop = int(timing[0]), int(timing[1])
     if page_list is not None:
         o.page_list = _dev(page_list, "page_list", torch.int32)
         o.pages_per_seq = page_list.shape[1]
@@ -244,6 +243,20 @@ def _opts(window=0, num_sinks=0, page_list=None, split_tokens=0, timing=None, sc
         o.score_acc = _dev(scores, "scores", torch.float32)
         o.score_stride = scores.shape[2]
     return o
+
+
+def profile_events(start=None, stop=None) -> None:
+    """Profiling hook: raw hipEvent_t handles (ints) that this thread's later decode calls record
+    around their main attention kernel; profile_events() clears them."""
+    _lib.pkv_profile_events(None if start is None else int(start), None if stop is None else int(stop))
+
+
+def _set_timing(timing) -> None:
+    # a call's timing=(start, stop) sets the thread's hook for that call; timing=None clears it
+    if timing is None:
+        _lib.pkv_profile_events(None, None)
+    else:
+        _lib.pkv_profile_events(int(timing[0]), int(timing[1]))
 
 
 def kv_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping) -> None:
@@ -296,7 +309,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
     ring_pages > 0: block_table holds a window layer's ring rows (BlockManager.block_table of a
     window group, with window/num_sinks of that group).
 
-    timing: optional pair of raw hipEvent_t handles recorded around the main kernel.
+    timing: optional pair of raw hipEvent_t handles recorded around the main kernel (the
+    library's per-thread profiling hook, set for this call).
     scores: optional [B, Hkv, stride] float32 tensor; every attended token's softmax
     probability, summed over the query heads of its kv head, is added into entry
     t // score_block (score_block = 1: per token; = the page size: per page)."""
@@ -306,13 +320,14 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block, ring_pages)
+    o = _opts(window, num_sinks, page_list, split_tokens, scores, score_block, ring_pages)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _set_timing(timing)
     _check("paged_decode_attention", _lib.paged_decode_attention(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(q, "q", input_dtype_of(k_cache, q)), _dev(block_table, "block_table", torch.int32),
@@ -342,13 +357,14 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         out = torch.empty((B, Hq, d), dtype=out_dtype or torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    o = _opts(window, num_sinks, page_list, split_tokens, timing, scores, score_block, ring_pages)
+    o = _opts(window, num_sinks, page_list, split_tokens, scores, score_block, ring_pages)
     ws_bytes = int(_lib.paged_decode_attention_workspace_size(ctypes.byref(desc), B, Hq, max_context_len,
                                                               ctypes.byref(o)))
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _set_timing(timing)
     _check("paged_decode_append_attention", _lib.paged_decode_append_attention(
         ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),

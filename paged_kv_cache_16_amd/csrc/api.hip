@@ -39,6 +39,8 @@ constexpr int kStreamChunkMin = 2;       // minimum units per wave in the persis
                                          // problems spread over many waves (one wave streams only
                                          // a few GB/s, so bandwidth comes from wave count)
 constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
+constexpr long long kMaxStreamWaves = 2048;  // most waves of a persistent launch (MI355X: 256 CUs x
+                                             // 4 SIMDs, two per SIMD over page lists)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
 constexpr int kDirectShortUnits = 8;     // at most this many units per sequence: one kernel
 constexpr int kDirectWideUnits = kDirectMaxUnits;  // ... or this many, with at least kDirectWideSegments
@@ -84,7 +86,6 @@ struct Plan {
     // how paged_decode_attention runs: one kernel, fixed partitions + combine, or the
     // persistent kernel + combine
     enum Path { kDirect, kPartitions, kStream } path = kDirect;
-    int kmax = 0;       // stream path: partial slots per segment
     int chunk_min = 0;  // stream path: minimum units per wave
     int lead = 0;       // stream path: virtual units charged at each segment start
     int unit_bytes = 0;  // K and V bytes of one 16-token unit of one kv head
@@ -131,7 +132,6 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
         const int span = pl.units_bound + pl.lead;  // flat positions of the longest segment
         pl.chunk_min = kStreamChunkMin;
         while ((span + pl.chunk_min - 1) / pl.chunk_min + 1 > kMaxSlots) pl.chunk_min *= 2;
-        pl.kmax = (span + pl.chunk_min - 1) / pl.chunk_min + 1;
     }
 }
 
@@ -228,17 +228,18 @@ struct StreamWs {
     size_t o_off, m_off, l_off, cnt_off, logits_off, lse2_off, total;
 };
 
-// Stream-path workspace: partial slots and per-segment counts; with score export also the
-// masked logits of every attended unit ([B*Hkv][units_bound][G][16] fp32) and the rows'
-// log2 normalisers ([B][Hq]).
-StreamWs stream_ws(int batch, int kv_heads, int group, int kmax, int head_dim, bool scores, int units_bound) {
+// Stream-path workspace: partial slots (kSegSlots per segment plus one overflow slot per wave,
+// G rows each) and per-segment (piece count, first wave); with score export also the masked
+// logits of every attended unit ([B*Hkv][units_bound][G][16] fp32) and the rows' log2
+// normalisers ([B][Hq]).
+StreamWs stream_ws(int batch, int kv_heads, int group, long long waves, int head_dim, bool scores, int units_bound) {
     StreamWs w;
-    const size_t rows = (size_t)batch * kv_heads * kmax * group;
+    const size_t rows = ((size_t)batch * kv_heads * kSegSlots + (size_t)waves) * group;
     w.o_off = 0;
     w.m_off = align_up(rows * head_dim * sizeof(float));
     w.l_off = w.m_off + align_up(rows * sizeof(float));
     w.cnt_off = w.l_off + align_up(rows * sizeof(float));
-    w.logits_off = w.cnt_off + align_up((size_t)batch * kv_heads * sizeof(int32_t));
+    w.logits_off = w.cnt_off + align_up((size_t)batch * kv_heads * 2 * sizeof(int32_t));
     w.lse2_off = w.logits_off;
     w.total = w.logits_off;
     if (scores) {
@@ -256,6 +257,34 @@ WsLayout ws_layout(int batch, int q_heads, int splits, int head_dim) {
     w.l_off = w.m_off + align_up(rows * sizeof(float));
     w.total = w.l_off + align_up(rows * sizeof(float));
     return w;
+}
+
+// Waves the persistent kernel launches for this plan on the current device (0 if the device
+// cannot be queried). One wave per SIMD, except over page lists: each wave keeps a unit or more
+// of loads in flight, so 4 waves per CU already hold what the memory needs (more only queue),
+// and fewer, longer shares spend less of the kernel on per-share set-up and even out the finish
+// times. Page lists keep two waves per SIMD, whose second wave hides their longer set-up per run
+// (measured both ways on the benchmark shapes; INT8 caches moved to one wave per SIMD once
+// their loads were counted exactly: 44.5 -> 43.0 us per step).
+// The most waves a launch of this plan can have on any device (at least one unit per wave,
+// at most kMaxStreamWaves): sizes the workspace's overflow slots without asking the device.
+long long stream_wave_bound(const Plan& pl, const pkv_cache_desc* d, int batch) {
+    const long long n_bound = (long long)batch * d->num_kv_heads * (pl.units_bound + pl.lead);
+    long long waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
+    waves = (waves + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
+    return waves < kMaxStreamWaves ? waves : kMaxStreamWaves;
+}
+
+long long stream_waves(const Plan& pl, const pkv_cache_desc* d, int batch) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const long long resident =
+        (long long)device_cus(dev) * device_occupancy(dev, kdt(d), d->head_dim, pl.mode) * kStreamWaves;
+    long long waves = stream_wave_bound(pl, d, batch);
+    if (waves > resident) waves = resident / kStreamWaves * kStreamWaves;
+    if (pl.mode != kPages && waves > (long long)device_cus(dev) * kSimdsPerCu)
+        waves = (long long)device_cus(dev) * kSimdsPerCu / kStreamWaves * kStreamWaves;
+    return waves;
 }
 
 pkv_status check_decode_args(const pkv_cache_desc* d, const void* k, const void* v, const void* q,
@@ -315,6 +344,7 @@ pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_
 
 }  // namespace
 
+
 extern "C" {
 
 pkv_status kv_cache_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache, const void* k_new,
@@ -349,8 +379,8 @@ size_t paged_decode_attention_workspace_size(const pkv_cache_desc* desc, int32_t
     if (pl.path == Plan::kDirect) return 0;
     if (pl.path == Plan::kStream) {
         if (num_q_heads % desc->num_kv_heads) return 0;
-        return stream_ws(batch, desc->num_kv_heads, num_q_heads / desc->num_kv_heads, pl.kmax, desc->head_dim,
-                         opts && opts->score_acc, pl.units_bound)
+        return stream_ws(batch, desc->num_kv_heads, num_q_heads / desc->num_kv_heads, stream_wave_bound(pl, desc, batch),
+                         desc->head_dim, opts && opts->score_acc, pl.units_bound)
             .total;
     }
     return ws_layout(batch, num_q_heads, pl.num_splits, desc->head_dim).total;
@@ -365,6 +395,10 @@ int32_t paged_decode_attention_num_splits(const pkv_cache_desc* desc, int32_t ba
 }  // extern "C"
 
 namespace {
+
+// The calling thread's profiling events (pkv_profile_events), recorded around the main kernel.
+thread_local hipEvent_t t_profile_start = nullptr;
+thread_local hipEvent_t t_profile_stop = nullptr;
 
 struct FusedAppend {
     void* k_cache;
@@ -401,8 +435,8 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     p.out = out;
     p.lse = lse_out;
     const hipStream_t s = (hipStream_t)stream;
-    hipEvent_t ev0 = opts ? (hipEvent_t)opts->timing_start : nullptr;
-    hipEvent_t ev1 = opts ? (hipEvent_t)opts->timing_stop : nullptr;
+    hipEvent_t ev0 = t_profile_start;
+    hipEvent_t ev1 = t_profile_stop;
 
     // Validate the workspace and finish the launch parameters before anything is enqueued.
     const bool scores = opts && opts->score_acc;
@@ -423,25 +457,14 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
     }
     if (pl.path == Plan::kStream) {
         const int G = num_q_heads / desc->num_kv_heads;
-        const StreamWs wl = stream_ws(batch, desc->num_kv_heads, G, pl.kmax, desc->head_dim, scores, pl.units_bound);
-        if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
         const long long n_bound = (long long)batch * desc->num_kv_heads * (pl.units_bound + pl.lead);
         if (n_bound > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
-        const long long resident =
-            (long long)device_cus(dev) * device_occupancy(dev, kdt(desc), desc->head_dim, pl.mode) * kStreamWaves;
-        waves = (n_bound + pl.chunk_min - 1) / pl.chunk_min;
-        if (waves > resident) waves = resident;
-        // One wave per SIMD, except over page lists: each wave keeps a unit or more of loads in
-        // flight, so 4 waves per CU already hold what the memory needs (more only queue), and
-        // fewer, longer shares spend less of the kernel on per-share set-up and even out the
-        // finish times. Page lists keep two waves per SIMD, whose second wave hides their longer
-        // set-up per run (measured both ways on the benchmark shapes; INT8 caches moved to one
-        // wave per SIMD once their loads were counted exactly: 44.5 -> 43.0 us per step).
-        if (pl.mode != kPages && waves > (long long)device_cus(dev) * kSimdsPerCu)
-            waves = (long long)device_cus(dev) * kSimdsPerCu;
-        waves = (waves + kStreamWaves - 1) / kStreamWaves * kStreamWaves;
+        waves = stream_waves(pl, desc, batch);
+        if (waves <= 0) return PKV_ERR_HIP;
+        const StreamWs wl =
+            stream_ws(batch, desc->num_kv_heads, G, stream_wave_bound(pl, desc, batch), desc->head_dim, scores,
+                      pl.units_bound);
+        if (workspace_bytes < wl.total) return PKV_ERR_WORKSPACE;
         p.o_part = (float*)((char*)workspace + wl.o_off);
         p.m_part = (float*)((char*)workspace + wl.m_off);
         p.l_part = (float*)((char*)workspace + wl.l_off);
@@ -449,7 +472,6 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.batch = batch;
         p.waves_total = (int)waves;
         p.chunk_min = pl.chunk_min;
-        p.kmax = pl.kmax;
         p.seg_lead = pl.lead;
         if (scores) {
             p.logits = (float*)((char*)workspace + wl.logits_off);
@@ -569,8 +591,17 @@ pkv_status paged_decode_attention_partial(const pkv_cache_desc* desc, const void
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
-    return hip_status(launch_decode(kdt(desc), desc->head_dim, pl.mode, false, p, batch,
-                                    (hipStream_t)stream));
+    const hipStream_t s = (hipStream_t)stream;
+    if (t_profile_start && hipEventRecord(t_profile_start, s) != hipSuccess) return PKV_ERR_HIP;
+    st = hip_status(launch_decode(kdt(desc), desc->head_dim, pl.mode, false, p, batch, s));
+    if (st == PKV_OK && t_profile_stop && hipEventRecord(t_profile_stop, s) != hipSuccess) return PKV_ERR_HIP;
+    return st;
+}
+
+pkv_status pkv_profile_events(void* start_event, void* stop_event) {
+    t_profile_start = (hipEvent_t)start_event;
+    t_profile_stop = (hipEvent_t)stop_event;
+    return PKV_OK;
 }
 
 pkv_status paged_decode_combine(const float* o_part, const float* m_part, const float* l_part, int32_t batch,

@@ -14,7 +14,9 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8B = 3, kI8H = 4 };
 constexpr int kWaves = 4;           // wavefronts per workgroup of the split kernel
 constexpr int kStreamWaves = 4;    // wavefronts per workgroup of the persistent kernel
 constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
-constexpr int kMaxSlots = 512;      // partial slots per segment the stream combine handles
+constexpr int kMaxSlots = 512;      // most pieces a segment is cut into on the persistent path
+constexpr int kSegSlots = 8;        // partial slots held per segment (its first pieces); later
+                                    // pieces go to one overflow slot per wave
 constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
 constexpr int kDirectMaxUnits = 40;  // units per segment the one-kernel path takes (and stages
                                      // logits for, with score export)
@@ -73,10 +75,9 @@ struct DecodeParams {
     int32_t batch;
     int32_t waves_total;   // waves launched
     int32_t chunk_min;     // minimum units per wave
-    int32_t kmax;          // partial slots per (sequence, kv head) segment
     int32_t seg_lead;      // virtual units charged at the start of every segment (run set-up)
     unsigned* err;         // device error word
-    int32_t* seg_count;    // [B*Hkv]: partials written for the segment; 0 = final row written
+    int32_t* seg_count;    // [B*Hkv][2]: pieces of the segment (0 = final row written), first piece's wave
     // fused decode step only: the batch's new rows ([B][Hkv][D]) and their slots ([B])
     char* k_cache_w;
     char* v_cache_w;

@@ -12,9 +12,12 @@
 // A wave keeps three units of K/V loads in flight (a 4-deep ring of register buffers) and
 // carries the pipeline across segment boundaries. At the end of its part of a segment it
 // writes either the finished, normalised row (when it holds the whole segment) or an
-// (o, m, l) partial into slot  w - first_wave(segment); the wave holding a segment's last
-// unit records how many partials the segment has. The combine kernel then merges them by
+// (o, m, l) partial: piece k = w - first_wave(segment) goes to the segment's own slot k when
+// k < kSegSlots, else to wave w's overflow slot (a piece k >= 1 is the first run of its wave,
+// so a wave fills at most one overflow slot). The wave holding a segment's last unit records
+// the piece count and the first wave. The combine kernel then merges the pieces by
 // log-sum-exp ([Novita] §關鍵技術 2: partial softmax results merge through max and sum).
+// Workspace rows: (B * Hkv * kSegSlots + waves) x G, whatever the context lengths.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_plan.h"
@@ -396,22 +399,26 @@ void decode_stream_kernel(DecodeParams p) {
             if constexpr (SCORES) {
                 if (j == 0 && c < 8 && head < G) p.row_lse2[hrow] = l_tot > 0.f ? m_run + __log2f(l_tot) : kNegInf;
             }
-            if (lane == 0) p.seg_count[seg] = 0;
+            if (lane == 0) p.seg_count[2 * seg] = 0;
         } else {
             const int s_g = f_run - v0;  // flat index of the segment's first position
-            const int k_slot = wave - s_g / C;
-            if (k_slot < p.kmax) {
-                const size_t row = ((size_t)seg * p.kmax + k_slot) * G + head;
-                if (writer) {
+            const int w0 = s_g / C;      // the wave holding it
+            const int k = wave - w0;     // this piece's index within the segment
+            const size_t slot = k < kSegSlots ? (size_t)seg * kSegSlots + k
+                                              : (size_t)B * Hkv * kSegSlots + wave;
+            const size_t row = slot * G + head;
+            if (writer) {
 #pragma unroll
-                    for (int a = 0; a < NACC; ++a)
-                        *reinterpret_cast<f32x4*>(p.o_part + row * D + T::acc_dim(a, j, c)) = acc[a];
-                }
-                if (j == 0 && c < 8 && head < G) {
-                    p.m_part[row] = m_run;  // log2 units, read only by the stream combine
-                    p.l_part[row] = l_tot;
-                }
-                if (lane == 0 && last) p.seg_count[seg] = k_slot + 1;
+                for (int a = 0; a < NACC; ++a)
+                    *reinterpret_cast<f32x4*>(p.o_part + row * D + T::acc_dim(a, j, c)) = acc[a];
+            }
+            if (j == 0 && c < 8 && head < G) {
+                p.m_part[row] = m_run;  // log2 units, read only by the stream combine
+                p.l_part[row] = l_tot;
+            }
+            if (lane == 0 && last) {
+                p.seg_count[2 * seg] = k + 1;
+                p.seg_count[2 * seg + 1] = w0;
             }
         }
         f_run += cntv;
@@ -443,26 +450,28 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
     const int lane = threadIdx.x;
     const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
-    const size_t base = (size_t)g * p.kmax * G + head;  // partial row of slot k: base + k * G
-    const float* op = p.o_part + base * D + lane * PER;
-    // Slots come in batches of KB, fetched whole: every slot below kmax is addressable, and
-    // the slots past the count are dropped by selection (their contents are stale, never
-    // multiplied in). The first batch is requested before the count and the context length
-    // arrive, so that the three loads share one round trip.
-    constexpr int KB = 8;  // one wave per SIMD leaves at most ~7 pieces per segment at 4k contexts
+    // Pieces come in batches of KB, fetched whole; those past the count are dropped by selection
+    // (their slots hold stale values, never multiplied in). The first batch is the segment's own
+    // slots, so it is requested before the count and the context length arrive and the three
+    // loads share one round trip; later batches sit in the overflow slots of waves w0 + k.
+    constexpr int KB = kSegSlots;  // one wave per SIMD leaves at most ~7 pieces per segment at 4k contexts
+    const size_t base = (size_t)g * KB * G + head;  // piece k < KB: row base + k * G
+    const size_t ovf = (size_t)p.batch * p.kv_heads * KB * G + head;  // piece k >= KB: row ovf + (w0 + k) * G
     float lv[KB], mv[KB], v[KB][PER];
-    auto fetch = [&](int k) {
+    auto fetch = [&](auto row_of) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
-            const size_t rk = base + (size_t)(k + u < p.kmax ? k + u : 0) * G;
+            const size_t rk = row_of(u);
             lv[u] = p.l_part[rk];
             mv[u] = p.m_part[rk];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) v[u][i] = op[(rk - base) * D + i];
+            for (int i = 0; i < PER; ++i) v[u][i] = p.o_part[rk * D + lane * PER + i];
         }
     };
-    int cnt = p.seg_count[g];
-    fetch(0);
+    int cnt = p.seg_count[2 * g];
+    int w0 = p.seg_count[2 * g + 1];
+    w0 = w0 < 0 ? 0 : (w0 >= p.waves_total ? p.waves_total - 1 : w0);  // in range by construction
+    fetch([&](int u) { return base + (size_t)u * G; });
     const int nu = seq_units<MODE>(p, b);
     // one branch on both values (no short circuit): with the count tested only past the
     // empty-sequence case, its load was issued after the first batch had returned
@@ -475,7 +484,8 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
         }
         return;
     }
-    if (cnt > p.kmax) cnt = p.kmax;  // never larger by construction; keeps every read in bounds
+    // never past the last wave by construction; keeps every read in bounds
+    if (cnt > p.waves_total - w0) cnt = p.waves_total - w0;
     // online merge over the batches
     float M = kNegInf, Ls = 0.f;
     float o[PER];
@@ -506,7 +516,12 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
         }
         k += KB;
         if (k >= cnt) break;
-        fetch(k);
+        // pieces k .. k + KB - 1 in the overflow slots of waves w0 + k + u (a slot past the last
+        // wave belongs to no piece of the count: the last wave's is read instead, and dropped)
+        fetch([&](int u) {
+            const int wv = w0 + k + u < p.waves_total ? w0 + k + u : p.waves_total - 1;
+            return ovf + (size_t)wv * G;
+        });
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll

@@ -116,26 +116,26 @@ def test_score_export_validation(pkv):
     d = _desc(pkv)
     fake = ctypes.c_void_p(256)  # never dereferenced
     plain = pkv.DecodeOpts(0, 0, None, 0, 0)
-    scored = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 4096)
+    scored = pkv.DecodeOpts(0, 0, None, 0, 0, fake, 4096)
     ws0 = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(plain))
     ws1 = lib.paged_decode_attention_workspace_size(ctypes.byref(d), 32, 32, 4096, ctypes.byref(scored))
     # logits of every unit and head: 32 seq x 8 kv heads x 256 units x 4 heads x 16 tokens x 4 B
     assert ws1 - ws0 >= 32 * 8 * 256 * 4 * 16 * 4
     # the one-kernel path exports scores itself, so a tiny problem still needs no workspace ...
     assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(plain)) == 0
-    small = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 20)
+    small = pkv.DecodeOpts(0, 0, None, 0, 0, fake, 20)
     assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(small)) == 0
     # ... except over a page list with entries other than single tokens or whole pages
-    odd = pkv.DecodeOpts(0, 0, fake, 2, 0, None, None, fake, 20, 5)
+    odd = pkv.DecodeOpts(0, 0, fake, 2, 0, fake, 20, 5)
     assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(odd)) > 0
-    per_page = pkv.DecodeOpts(0, 0, fake, 2, 0, None, None, fake, 20, d.block_size)
+    per_page = pkv.DecodeOpts(0, 0, fake, 2, 0, fake, 20, d.block_size)
     assert lib.paged_decode_attention_workspace_size(ctypes.byref(d), 2, 32, 20, ctypes.byref(per_page)) == 0
     call = lib.paged_decode_attention
     args = lambda opts, mcl=100: (ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, mcl, 0.0, opts, fake, 2,
                                   None, None, 0, None)
-    split = pkv.DecodeOpts(0, 0, None, 0, 64, None, None, fake, 4096)
+    split = pkv.DecodeOpts(0, 0, None, 0, 64, fake, 4096)
     assert call(*args(ctypes.byref(split))) == 4        # scores with fixed partitions
-    short = pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 99)
+    short = pkv.DecodeOpts(0, 0, None, 0, 0, fake, 99)
     assert call(*args(ctypes.byref(short))) == 2        # stride below the context bound
     part = lib.paged_decode_attention_partial
     assert part(ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, 100, 0.0, ctypes.byref(scored),
@@ -162,5 +162,5 @@ def test_select_pages_validation(pkv):
     args = lambda opts: (ctypes.byref(d), fake, fake, fake, fake, 8, fake, 2, 32, 100, 0.0, opts, fake, 2,
                          None, None, 0, None)
     # per-page entries: 100 tokens in pages of 16 need 7 entries
-    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 6, 16)))) == 2
-    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, None, None, fake, 7, -2)))) == 2
+    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, fake, 6, 16)))) == 2
+    assert call(*args(ctypes.byref(pkv.DecodeOpts(0, 0, None, 0, 0, fake, 7, -2)))) == 2
