@@ -110,6 +110,9 @@ def parse():
     ap.add_argument("--read-probe-mib", type=int, default=2048,
                     help="after the timed region, time the library's read-rate probe over this many MiB "
                          "(0: skip); the roofline then also gives achieved / probe")
+    ap.add_argument("--noalloc", action="store_true",
+                    help="default workload: time paged_decode_attention_noalloc (append + attention through "
+                         "the library's scratch) instead of the fused step")
     return ap.parse_args()
 
 
@@ -526,6 +529,14 @@ def run_layer(w, args, dev):
     hip = HipEvents()
 
     def step(rep, ev=None):
+        if args.noalloc:  # the append, then attention over the library's own scratch
+            pkv.kv_cache_append(rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"])
+            pkv.profile_events(*(ev or (None, None)))
+            pkv.paged_decode_attention_noalloc(rep["q"], rep["k"], rep["v"], rep["bt"], rep["cl"],
+                                               max_context_len=mcl, split_tokens=args.split_tokens, out=out,
+                                               lse=lse, scores=scores)
+            pkv.profile_events()
+            return
         # one decode step of the layer: append of the 32 new tokens + attention, fused
         pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
                                           rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
@@ -555,13 +566,15 @@ def run_layer(w, args, dev):
     elif args.split_tokens:
         kname = f"decode_split_kernel<{dt},{d},full>"
     else:
-        kname = f"decode_stream_kernel<{dt},{d},full,fused append>"
-    plain = not (args.scores or args.kv_dtype or variant or args.split_tokens)
+        kname = f"decode_stream_kernel<{dt},{d},full" + (">" if args.noalloc else ",fused append>")
+    plain = not (args.scores or args.kv_dtype or variant or args.split_tokens or args.noalloc)
     step_desc = ("paged_decode_append_attention: append of the new tokens fused into the persistent split "
                  "kernel, then the LSE combine")
     if args.kv_dtype == "int8":
         step_desc = ("paged_decode_append_attention on an INT8 cache: quantising append of the new tokens, "
                      "then the persistent split kernel and the LSE combine")
+    if args.noalloc:
+        step_desc = "kv_cache_append, then paged_decode_attention_noalloc (workspace in the library's scratch)"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -893,7 +906,7 @@ def main():
         baseline_ok = not args.loop
     else:
         res, lens, variant = run_layer(w, args, dev)
-        baseline_ok = not (args.kv_dtype or variant or args.scores or args.split_tokens)
+        baseline_ok = not (args.kv_dtype or variant or args.scores or args.split_tokens or args.noalloc)
     if args.cpu_seconds > 0 and baseline_ok:
         res["cpu_baseline"] = cpu_baseline(w, args, dev, lens)
     print(json.dumps(res), flush=True)

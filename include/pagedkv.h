@@ -33,8 +33,9 @@
  *     every buffer (including workspaces); the library never allocates or frees
  *     device memory (the host block manager's own host memory is allocated by
  *     pkv_bm_create and freed by pkv_bm_destroy) and keeps no state between calls
- *     other than the device error word (pkv_device_errors), a thread's profiling
- *     events (pkv_profile_events) and per-device properties it asks the runtime for once (compute units,
+ *     other than the device error word (pkv_device_errors), the scratch of
+ *     paged_decode_attention_noalloc, a thread's profiling events (pkv_profile_events)
+ *     and per-device properties it asks the runtime for once (compute units,
  *     occupancy), so calls are reentrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *     enqueued asynchronously; no entry point other than pkv_device_errors
@@ -84,7 +85,9 @@ typedef enum {
     PKV_ERR_MODE = 4,        /* window and page_list both set, or a bad sparsity field */
     PKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
     PKV_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
-    PKV_ERR_NO_BLOCKS = 7    /* block manager: a pool has too few free blocks (nothing changed) */
+    PKV_ERR_NO_BLOCKS = 7,   /* block manager: a pool has too few free blocks (nothing changed) */
+    PKV_ERR_SCRATCH = 8      /* paged_decode_attention_noalloc: the call needs more workspace than
+                                its fixed scratch holds (nothing launched) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
@@ -265,6 +268,31 @@ pkv_status paged_decode_append_attention(const pkv_cache_desc* desc /* host */,
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* paged_decode_attention_noalloc — paged_decode_attention for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results, validation and error codes as paged_decode_attention,
+ * without the workspace: the call's workspace is a scratch array inside the library, one per
+ * device, held from the first call on that device until the process ends. The call allocates
+ * and frees nothing. The scratch holds 32 MiB (33554432 bytes); a call whose
+ * paged_decode_attention_workspace_size(...) exceeds that returns PKV_ERR_SCRATCH before
+ * anything is enqueued (the Llama-3-8B-shaped layer of 32 sequences up to 4096 tokens needs
+ * about 8 MiB, 24 MiB with score export). Every call on a device shares that device's scratch
+ * and leaves its contents behind (nothing in it needs to start at zero): calls that overlap in
+ * time on one device, on different streams or from different threads, race and give wrong
+ * results; calls ordered on one stream are safe. */
+pkv_status paged_decode_attention_noalloc(const pkv_cache_desc* desc /* host */,
+                                          const void* k_cache, const void* v_cache,
+                                          const void* q,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens,
+                                          int32_t batch, int32_t num_q_heads,
+                                          int32_t max_context_len,
+                                          float scale,
+                                          const pkv_decode_opts* opts /* host, nullable */,
+                                          void* out, pkv_dtype out_dtype,
+                                          float* lse_out,
+                                          void* stream);
+
 /* Bytes of workspace paged_decode_attention needs for these arguments (0 when
  * the call would need none). Returns 0 as well for arguments that the call
  * would reject; pure host function. */
@@ -429,7 +457,7 @@ int64_t pkv_bm_blocks_in_use(const pkv_block_manager* bm, int32_t group);
 
 /* Profiling hook (measurement only). Sets, for the calling host thread, two hipEvent_t
  * handles (passed as void*) that every later decode call of that thread (paged_decode_attention,
- * _append_attention, _partial) records on its stream right before its main attention
+ * _append_attention, _noalloc, _partial) records on its stream right before its main attention
  * kernel and right after it; (NULL, NULL) clears them. This per-thread pair is the one piece of
  * state the library keeps for the caller. The records add queue work to every call, so the hook
  * stays clear outside measurement. Always returns PKV_OK. */

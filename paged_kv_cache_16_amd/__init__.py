@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention",
+    "kv_cache_append", "paged_decode_attention", "paged_decode_append_attention", "paged_decode_attention_noalloc",
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
     "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks", "device_errors",
@@ -69,6 +69,9 @@ _lib.paged_decode_append_attention.restype = ctypes.c_int
 _lib.paged_decode_append_attention.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                                _i32, _i32, _f32, _P_OPTS, _vp, ctypes.c_int, _vp, _vp, _sz,
                                                _vp]
+_lib.paged_decode_attention_noalloc.restype = ctypes.c_int
+_lib.paged_decode_attention_noalloc.argtypes = [_P_DESC, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                                _P_OPTS, _vp, ctypes.c_int, _vp, _vp]
 _lib.paged_decode_attention_workspace_size.restype = _sz
 _lib.paged_decode_attention_workspace_size.argtypes = [_P_DESC, _i32, _i32, _i32, _P_OPTS]
 _lib.paged_decode_attention_num_splits.restype = _i32
@@ -334,6 +337,29 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, *, ma
         block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq,
         int(max_context_len), float(scale), ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
         _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # the library's per-device scratch for paged_decode_attention_noalloc
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, context_lens, *, max_context_len: int,
+                                   out, lse=None, scale: float = 0.0, window: int = 0, num_sinks: int = 0,
+                                   page_list=None, split_tokens: int = 0, scores=None, score_block: int = 1,
+                                   ring_pages: int = 0):
+    """paged_decode_attention without a workspace: the library's own per-device scratch serves
+    instead, so the call allocates nothing (out, and lse if wanted, are the caller's). Calls that
+    overlap in time on one device race on that scratch. Returns (out, lse)."""
+    desc = cache_desc(k_cache, q.dtype)
+    B, Hq, d = _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, out, lse, scores)
+    _need(out is not None, "out is required (the call allocates nothing)")
+    o = _opts(window, num_sinks, page_list, split_tokens, scores, score_block, ring_pages)
+    _check("paged_decode_attention_noalloc", _lib.paged_decode_attention_noalloc(
+        ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(q, "q", input_dtype_of(k_cache, q)), _dev(block_table, "block_table", torch.int32),
+        block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq,
+        int(max_context_len), float(scale), ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
+        _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(q)))
     return out, lse
 
 

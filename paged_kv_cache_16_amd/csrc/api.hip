@@ -344,6 +344,33 @@ pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_
 
 }  // namespace
 
+// Scratch of paged_decode_attention_noalloc: the workspace of its calls, in a fixed device
+// array instead of caller memory. Each device holds its own copy for the life of the process,
+// shared by every call on that device (overlapping calls race); nothing in it has to start at
+// zero, since every call writes each value it reads first. Host code never uses the array's name
+// as an address (in host code it is a stand-in, not device memory): the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::atomic<uintptr_t> g_scratch[64];  // per device: 0 = not looked up yet, 1 = unavailable
+
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    uintptr_t v = g_scratch[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        v = (e == hipSuccess && ptr) ? (uintptr_t)ptr : 1;
+        g_scratch[dev].store(v, std::memory_order_relaxed);  // racing first calls store the same value
+    }
+    return v == 1 ? nullptr : reinterpret_cast<void*>(v);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -552,6 +579,24 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc, const void* k_cach
                        workspace_bytes, stream, nullptr);
 }
 
+pkv_status paged_decode_attention_noalloc(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                                          const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                          int32_t max_context_len, float scale, const pkv_decode_opts* opts,
+                                          void* out, pkv_dtype out_dtype, float* lse_out, void* stream) {
+    // the same validation as paged_decode_attention first, so its errors come out unchanged
+    pkv_status st = check_decode_args(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens,
+                                      batch, num_q_heads, max_context_len, opts);
+    if (st != PKV_OK) return st;
+    const size_t need = paged_decode_attention_workspace_size(desc, batch, num_q_heads, max_context_len, opts);
+    if (need > kScratchBytes) return PKV_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && !(ws = scratch_ptr())) return PKV_ERR_HIP;
+    return decode_impl(desc, k_cache, v_cache, q, block_table, max_blocks_per_seq, context_lens, batch,
+                       num_q_heads, max_context_len, scale, opts, out, out_dtype, lse_out, ws,
+                       ws ? kScratchBytes : 0, stream, nullptr);
+}
+
 pkv_status paged_decode_append_attention(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
                                          const void* k_new, const void* v_new, const int32_t* slot_mapping,
                                          const void* q, const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -645,6 +690,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case PKV_ERR_HIP: return "HIP launch error";
         case PKV_ERR_NO_BLOCKS: return "too few free blocks";
+        case PKV_ERR_SCRATCH: return "the call needs more workspace than the no-allocation scratch holds";
     }
     return "unknown status";
 }
