@@ -528,6 +528,12 @@ def run_layer(w, args, dev):
     scores = torch.zeros((B, w.kv_heads, mcl), dtype=torch.float32, device=dev) if args.scores else None
     hip = HipEvents()
 
+    # each replica's step checked and marshalled once: a timed step is one library call
+    prepared = {id(rep): pkv.prepare_decode_append_attention(
+        rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"], rep["bt"], rep["cl"],
+        max_context_len=mcl, split_tokens=args.split_tokens, out=out, lse=lse, workspace=workspace,
+        scores=scores) for rep in reps}
+
     def step(rep, ev=None):
         if args.noalloc:  # the append, then attention over the library's own scratch
             pkv.kv_cache_append(rep["k"], rep["v"], rep["k_new"], rep["v_new"], rep["slots"])
@@ -538,10 +544,11 @@ def run_layer(w, args, dev):
             pkv.profile_events()
             return
         # one decode step of the layer: append of the 32 new tokens + attention, fused
-        pkv.paged_decode_append_attention(rep["q"], rep["k"], rep["v"], rep["k_new"], rep["v_new"],
-                                          rep["slots"], rep["bt"], rep["cl"], max_context_len=mcl,
-                                          split_tokens=args.split_tokens, out=out, lse=lse,
-                                          workspace=workspace, timing=ev, scores=scores)
+        if ev is not None:
+            pkv.profile_events(*ev)
+        prepared[id(rep)]()
+        if ev is not None:
+            pkv.profile_events()
 
     for i in range(args.warmup):
         step(reps[i % len(reps)])
@@ -656,13 +663,19 @@ def run_multilayer(w, args, dev):
                      dtype=torch.uint8, device=dev)
     hip = HipEvents()
 
+    # every (step, layer) call checked and marshalled once: a timed layer-step is one library call
+    prepared = [[pkv.prepare_decode_append_attention(
+        ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], ly["slots"][s], ly["bt"], lens_s[s],
+        max_context_len=mcl, window=ly["window"], num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
+        workspace=ws, ring_pages=ly["ring"]) for ly in layers] for s in range(steps)]
+
     def step(s, layer_timing=None):
-        for li, ly in enumerate(layers):
-            pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s], ly["slots"][s],
-                                              ly["bt"], lens_s[s], max_context_len=mcl, window=ly["window"],
-                                              num_sinks=w.sinks if ly["window"] else 0, out=out, lse=lse,
-                                              workspace=ws, ring_pages=ly["ring"],
-                                              timing=layer_timing(li) if layer_timing else None)
+        for li, call in enumerate(prepared[s]):
+            if layer_timing:
+                pkv.profile_events(*layer_timing(li))
+            call()
+        if layer_timing:
+            pkv.profile_events()
 
     reps = max(1, args.steps // (w.layers * steps)) if steps > 1 else max(4, args.steps // 8)
     for s in range(min(steps, 4)):
@@ -711,11 +724,20 @@ def run_multilayer(w, args, dev):
     graph_ms = None
     if not args.no_graph:
         # The same steps replayed from HIP graphs: one graph per decode step holding every layer.
+        # (captured through the plain wrapper: a prepared call is bound to the stream current when
+        # it was prepared, and capture runs on a stream of its own)
+        def step_on_current_stream(s):
+            for ly in layers:
+                pkv.paged_decode_append_attention(ly["q"], ly["k"], ly["v"], ly["kn"][s], ly["vn"][s],
+                                                  ly["slots"][s], ly["bt"], lens_s[s], max_context_len=mcl,
+                                                  window=ly["window"], num_sinks=w.sinks if ly["window"] else 0,
+                                                  out=out, lse=lse, workspace=ws, ring_pages=ly["ring"])
+
         graphs = []
         for s in range(steps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(s)
+                step_on_current_stream(s)
             graphs.append(g)
         torch.cuda.synchronize()
         for g in graphs[:4]:
@@ -816,15 +838,23 @@ def run_page_selected(w, args, dev):
                          dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
+    # each list's step (the loop's one step) checked and marshalled once
+    if not loop:
+        prepared = [pkv.prepare_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
+                                                        page_list=lst, out=out, lse=lse, workspace=ws) for lst in lists]
+    else:
+        prepared = [pkv.prepare_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
+                                                        page_list=plist, out=out, lse=lse, workspace=ws,
+                                                        scores=gscores, score_block=P)]
+
     def step(i, ev=None, sev=None):
+        if ev is not None:
+            pkv.profile_events(*ev)
+        prepared[i % len(prepared)]()
+        if ev is not None:
+            pkv.profile_events()
         if not loop:
-            pkv.paged_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
-                                              page_list=lists[i % n_lists], out=out, lse=lse, workspace=ws,
-                                              timing=ev)
             return
-        pkv.paged_decode_append_attention(q, gk, gv, kn, vn, slots, gbt, cl, max_context_len=max(lens),
-                                          page_list=plist, out=out, lse=lse, workspace=ws, timing=ev,
-                                          scores=gscores, score_block=P)
         if sev is not None:
             hip.record(sev[0], stream)
         pkv.select_pages(gscores, cl, block_size=P, k=w.pages_per_step, recent=1, page_list=plist)

@@ -23,7 +23,7 @@ __all__ = [
     "paged_decode_attention_partial",
     "paged_decode_combine", "workspace_size", "num_splits", "kv_cache_bytes", "status_string",
     "select_pages", "new_cache", "BlockManager", "ring_pages", "policy_blocks", "device_errors",
-    "read_probe", "profile_events",
+    "read_probe", "profile_events", "prepare_decode_append_attention", "PreparedCall",
     "PagedKVError", "LIB_PATH",
 ]
 
@@ -363,15 +363,11 @@ def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, context_len
     return out, lse
 
 
-def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table,
-                                  context_lens, *, max_context_len: int, scale: float = 0.0,
-                                  window: int = 0, num_sinks: int = 0, page_list=None,
-                                  split_tokens: int = 0, out=None, out_dtype=None, lse=None,
-                                  workspace=None, want_lse: bool = True, timing=None, scores=None,
-                                  score_block: int = 1, ring_pages: int = 0):
-    """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
-    slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
-    scores: as in paged_decode_attention."""
+def _fused_args(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table, context_lens, max_context_len,
+                scale, window, num_sinks, page_list, split_tokens, out, out_dtype, lse, workspace, want_lse, scores,
+                score_block, ring_pages):
+    """Checks and marshals a paged_decode_append_attention call: (C arguments, out, lse, tensors
+    to keep alive)."""
     desc = cache_desc(k_cache, q.dtype)
     B, Hq, d = _decode_shapes(desc, q, k_cache, v_cache, block_table, context_lens, page_list, out, lse, scores)
     # one new token per sequence
@@ -390,16 +386,63 @@ def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mappin
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
+            _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", input_dtype_of(k_cache, q)),
+            _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), B, Hq, int(max_context_len), float(scale),
+            ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
+            _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q))
+    keep = (desc, o, q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table, context_lens, page_list, scores,
+            workspace)
+    return args, out, lse, keep
+
+
+def paged_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table,
+                                  context_lens, *, max_context_len: int, scale: float = 0.0,
+                                  window: int = 0, num_sinks: int = 0, page_list=None,
+                                  split_tokens: int = 0, out=None, out_dtype=None, lse=None,
+                                  workspace=None, want_lse: bool = True, timing=None, scores=None,
+                                  score_block: int = 1, ring_pages: int = 0):
+    """One decode step of one layer: append of row b of k_new/v_new ([B, Hkv, d]) at
+    slot_mapping[b] (position context_lens[b] - 1), then attention. Returns (out, lse).
+    scores: as in paged_decode_attention."""
+    args, out, lse, _ = _fused_args(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table, context_lens,
+                                    max_context_len, scale, window, num_sinks, page_list, split_tokens, out,
+                                    out_dtype, lse, workspace, want_lse, scores, score_block, ring_pages)
     _set_timing(timing)
-    _check("paged_decode_append_attention", _lib.paged_decode_append_attention(
-        ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(k_new, "k_new", input_dtype_of(k_cache, k_new)), _dev(v_new, "v_new", input_dtype_of(k_cache, k_new)),
-        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", input_dtype_of(k_cache, q)),
-        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
-        _dev(context_lens, "context_lens", torch.int32), B, Hq, int(max_context_len), float(scale),
-        ctypes.byref(o), _dev(out, "out"), DTYPE_CODE[out.dtype],
-        _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_n, _stream(q)))
+    _check("paged_decode_append_attention", _lib.paged_decode_append_attention(*args))
     return out, lse
+
+
+class PreparedCall:
+    """A decode call checked and marshalled once, for loops that repeat it: each call makes the
+    one library call again, with the same tensors (their contents at that time) on the stream
+    that was current when it was prepared, and returns (out, lse). It holds its tensors (and the
+    workspace) alive."""
+    __slots__ = ("_fn", "_args", "_name", "out", "lse", "_keep")
+
+    def __init__(self, name, fn, args, out, lse, keep):
+        self._name, self._fn, self._args, self.out, self.lse, self._keep = name, fn, args, out, lse, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise PagedKVError(self._name, st)
+        return self.out, self.lse
+
+
+def prepare_decode_append_attention(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table, context_lens,
+                                    *, max_context_len: int, scale: float = 0.0, window: int = 0,
+                                    num_sinks: int = 0, page_list=None, split_tokens: int = 0, out=None,
+                                    out_dtype=None, lse=None, workspace=None, want_lse: bool = True, scores=None,
+                                    score_block: int = 1, ring_pages: int = 0) -> PreparedCall:
+    """paged_decode_append_attention checked and marshalled once (same arguments); calling the
+    result runs the step. The workspace, out and lse are allocated here when not given."""
+    args, out, lse, keep = _fused_args(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_table, context_lens,
+                                       max_context_len, scale, window, num_sinks, page_list, split_tokens, out,
+                                       out_dtype, lse, workspace, want_lse, scores, score_block, ring_pages)
+    return PreparedCall("paged_decode_append_attention", _lib.paged_decode_append_attention, args, out, lse, keep)
 
 
 def paged_decode_attention_partial(q, k_cache, v_cache, block_table, context_lens, *,

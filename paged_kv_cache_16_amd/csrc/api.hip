@@ -42,7 +42,8 @@ constexpr int kSimdsPerCu = 4;         // SIMD units per compute unit (CDNA)
 constexpr long long kMaxStreamWaves = 2048;  // most waves of a persistent launch (MI355X: 256 CUs x
                                              // 4 SIMDs, two per SIMD over page lists)
 constexpr int kRunSetupBytes = 24576;   // streaming time per wave of one run's set-up, in bytes
-constexpr int kDirectShortUnits = 8;     // at most this many units per sequence: one kernel
+constexpr int kDirectShortUnits = 16;    // at most this many units per sequence: one kernel (a wave's
+                                         // 4-unit load ring holds every unit of a segment)
 constexpr int kDirectWideUnits = kDirectMaxUnits;  // ... or this many, with at least kDirectWideSegments
 constexpr int kDirectWideSegments = 64;  // (sequence, kv head) segments, so no merge launch is needed
 constexpr int kMinUnitsPerSplit = 2 * kWaves;  // one pair of 16-token units per wave

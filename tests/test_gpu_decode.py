@@ -476,11 +476,11 @@ def test_workspace_reuse():
     lens = [1500, 333, 4000, 2, 0, 129]
     c = make_case(48, B=6, Hq=16, Hkv=4, d=128, dtype="bf16", P=16, lens=lens)
     n = pkv.workspace_size(c.gk, 6, 16, max(lens))
-    n_w = pkv.workspace_size(c.gk, 6, 16, max(lens), window=300, num_sinks=4)
+    n_w = pkv.workspace_size(c.gk, 6, 16, max(lens), window=1000, num_sinks=4)
     assert n > 0 and n_w > 0
     ws = torch.full((max(n, n_w),), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
     ref = oracle_attend(c)
-    ref_w = oracle_attend(c, window=300, sinks=4)
+    ref_w = oracle_attend(c, window=1000, sinks=4)
     outs = []
     for _ in range(3):
         out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
@@ -488,7 +488,7 @@ def test_workspace_reuse():
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)))
         out, lse = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens),
-                                              window=300, num_sinks=4, workspace=ws)
+                                              window=1000, num_sinks=4, workspace=ws)
         torch.cuda.synchronize()
         assert_close(c, (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)), ref_w,
                      "workspace reuse, window")
@@ -638,7 +638,7 @@ def test_graph_replay_fused_step():
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
-    ws2 = torch.empty(pkv.workspace_size(c.gk, B, Hq, max(lens), window=300, num_sinks=4), dtype=torch.uint8,
+    ws2 = torch.empty(pkv.workspace_size(c.gk, B, Hq, max(lens), window=1000, num_sinks=4), dtype=torch.uint8,
                       device="cuda")
     for i in range(4):
         out.fill_(float("nan"))
@@ -647,6 +647,32 @@ def test_graph_replay_fused_step():
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {i} differs from the eager step"
         # eager work between replays, on another workspace and with another plan
-        pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens), window=300,
+        pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=max(lens), window=1000,
                                    num_sinks=4, workspace=ws2)
         torch.cuda.synchronize()
+
+
+def test_prepared_call_equals_wrapper():
+    """prepare_decode_append_attention (checked and marshalled once, one library call per step)
+    gives the wrapper's result bit for bit, call after call, and follows the tensors' contents."""
+    import paged_kv_cache_16_amd as pkv
+    lens = [1500, 333, 4000, 2, 0, 129]
+    B, Hq, Hkv = 6, 16, 4
+    c = make_case(57, B=B, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", P=16, lens=lens)
+    slots = torch.tensor([synth.slot_of(c.bt, b, L - 1, c.P) if L > 0 else -1 for b, L in enumerate(lens)],
+                         dtype=torch.int32).cuda()
+    kn = torch.stack([c.K[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    vn = torch.stack([c.V[b, max(L - 1, 0)] for b, L in enumerate(lens)]).cuda()
+    ref = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl, max_context_len=4000)
+    call = pkv.prepare_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl, max_context_len=4000)
+    for _ in range(3):
+        out, lse = call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+    assert_close(c, (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)), oracle_attend(c),
+                 "prepared call")
+    c.gq.mul_(0.5)  # new contents of the same tensor: the prepared call sees them
+    ref2 = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn, vn, slots, c.gbt, c.gcl, max_context_len=4000)
+    out2, lse2 = call()
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref2[0]) and torch.equal(lse2, ref2[1]) and not torch.equal(out2, ref[0])

@@ -29,7 +29,7 @@ def _both(c, **kw):
     B, Hq, d = c.gq.shape
     mcl = max(c.lens)
     n_ws = pkv.workspace_size(c.gk, B, Hq, mcl, window=kw.get("window", 0), num_sinks=kw.get("num_sinks", 0),
-                              scores=kw.get("scores"))
+                              split_tokens=kw.get("split_tokens", 0), scores=kw.get("scores"))
     assert n_ws > 0, "the case is meant to need a workspace"
     ws = torch.full((n_ws,), 0x5A, dtype=torch.uint8, device="cuda")
     out_w, lse_w = pkv.paged_decode_attention(c.gq, c.gk, c.gv, c.gbt, c.gcl, max_context_len=mcl, workspace=ws,
@@ -54,7 +54,7 @@ def test_noalloc_equals_workspace_entry_point():
         # the persistent path (Llama-3-8B-shaped heads), then smaller problems over the same scratch
         dict(seed=101, B=6, Hq=32, Hkv=8, lens=[1500, 333, 4000, 2, 0, 129], kw={}),
         dict(seed=102, B=3, Hq=16, Hkv=4, lens=[900, 300, 50], kw={}),
-        dict(seed=103, B=2, Hq=12, Hkv=2, lens=[700, 20], kw=dict(window=100, num_sinks=4)),
+        dict(seed=103, B=2, Hq=12, Hkv=2, lens=[2700, 20], kw=dict(window=1000, num_sinks=4)),
         dict(seed=104, B=2, Hq=8, Hkv=2, lens=[500, 64], kw=dict(split_tokens=64)),
     ]
     for cs in cases:
@@ -70,7 +70,7 @@ def test_noalloc_equals_workspace_entry_point():
 def test_noalloc_score_export():
     """Score export through the scratch (the logits live there too), twice in a row, the second
     call smaller."""
-    for seed, B, lens in ((111, 4, [3000, 1200, 17, 2049]), (112, 2, [600, 90])):
+    for seed, B, lens in ((111, 4, [3000, 1200, 17, 2049]), (112, 2, [900, 90])):
         c = make_case(seed, B=B, Hq=32, Hkv=8, d=128, dtype="bf16", P=16, lens=lens)
         stride = max(lens)
         init = synth.normal((B, 8, stride), seed, "score-init", dtype="f32").cuda()
