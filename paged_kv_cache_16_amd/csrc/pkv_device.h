@@ -30,77 +30,75 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 // dtype tags -----------------------------------------------------------------------------
 // kBytes / kE: bytes and elements of one cache element / 16-byte chunk. In: the type of q
-// and of the MFMA operands. kQ8: an INT8 cache (int8 data plane + fp32 row-scale plane).
+// (and of the new rows and 2-byte outputs). Mma: the type of the MFMA operands. kQ8: an INT8
+// cache (int8 data plane + fp32 row-scale plane).
 struct F32 {
     static constexpr int kBytes = 4;
     static constexpr int kE = 4;  // elements per 16-byte chunk
     static constexpr bool kQ8 = false;
     using In = F32;
+    using Mma = F32;
 };
 struct F16 {
     static constexpr int kBytes = 2;
     static constexpr int kE = 8;
     static constexpr bool kQ8 = false;
     using In = F16;
+    using Mma = F16;
 };
 struct BF16 {
     static constexpr int kBytes = 2;
     static constexpr int kE = 8;
     static constexpr bool kQ8 = false;
     using In = BF16;
+    using Mma = BF16;
 };
-// INT8 caches with bf16 / fp16 inputs. A 16-byte chunk holds 16 elements; converted, it is
-// exactly two chunks of the input type (int8 values are exact in bf16 and fp16).
+// INT8 caches with bf16 / fp16 inputs. A 16-byte chunk holds 16 elements; widened, it is
+// exactly two fp16 chunks (int8 values are exact in fp16), and the MFMAs run in fp16 for either
+// input type: a bf16 query is converted once per run (exact for |q| in [2^-14, 65504], the
+// bf16 values fp16 holds; smaller ones round toward zero by less than 2^-24).
 struct I8B {
     static constexpr int kBytes = 1;
     static constexpr int kE = 16;
     static constexpr bool kQ8 = true;
     using In = BF16;
+    using Mma = F16;
 };
 struct I8H {
     static constexpr int kBytes = 1;
     static constexpr int kE = 16;
     static constexpr bool kQ8 = true;
     using In = F16;
+    using Mma = F16;
 };
 
-// Sign-extended byte k (0..3) of w, as a float.
-__device__ __forceinline__ float sbyte_f32(unsigned w, int k) {
-    // the builtin is typed unsigned; its bits are the sign-extended byte
-    return (float)(int)__builtin_amdgcn_sbfe(w, 8 * k, 8);
-}
-// 16 int8 values -> two chunks of 8 bf16 / fp16 (elements 0..7, 8..15), exact.
-template <class In>
-__device__ __forceinline__ void widen_i8(const u32x4& c, u32x4& lo, u32x4& hi);
-template <>
-__device__ __forceinline__ void widen_i8<BF16>(const u32x4& c, u32x4& lo, u32x4& hi) {
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 16 int8 values -> two chunks of 8 fp16 (elements 0..7, 8..15), exact. A byte x becomes
+// k = x + 128 (its sign bit flipped); the fp16 with bits 0x6400 | k is 1024 + k (exponent 10,
+// unit spacing), and 1024 + k - 1152 = x exactly: one byte permute builds two such halves and
+// one packed fp16 subtraction finishes them.
+__device__ __forceinline__ void widen_i8_f16(const u32x4& c, u32x4& lo, u32x4& hi) {
+    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     unsigned o[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        // bf16 of a small integer = the upper half of its fp32 bits (the low half is zero);
-        // one byte permute joins the upper halves of two values
-        const unsigned f0 = __float_as_uint(sbyte_f32(c[w], 0)), f1 = __float_as_uint(sbyte_f32(c[w], 1));
-        const unsigned f2 = __float_as_uint(sbyte_f32(c[w], 2)), f3 = __float_as_uint(sbyte_f32(c[w], 3));
-        o[2 * w] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-        o[2 * w + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+        const unsigned k = c[w] ^ 0x80808080u;
+        // result bytes: selector 0..3 take bytes of k, 4 takes a 0x64 byte
+        const unsigned a = __builtin_amdgcn_perm(0x64646464u, k, 0x04010400u);  // halves 0x64k0, 0x64k1
+        const unsigned b = __builtin_amdgcn_perm(0x64646464u, k, 0x04030402u);  // halves 0x64k2, 0x64k3
+        o[2 * w] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, a) + bias);
+        o[2 * w + 1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, b) + bias);
     }
     lo = u32x4{o[0], o[1], o[2], o[3]};
     hi = u32x4{o[4], o[5], o[6], o[7]};
 }
-template <>
-__device__ __forceinline__ void widen_i8<F16>(const u32x4& c, u32x4& lo, u32x4& hi) {
-    unsigned o[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const _Float16 h0 = (_Float16)sbyte_f32(c[w], 0), h1 = (_Float16)sbyte_f32(c[w], 1);
-        const _Float16 h2 = (_Float16)sbyte_f32(c[w], 2), h3 = (_Float16)sbyte_f32(c[w], 3);
-        o[2 * w] = (unsigned)__builtin_bit_cast(unsigned short, h0) |
-                   ((unsigned)__builtin_bit_cast(unsigned short, h1) << 16);
-        o[2 * w + 1] = (unsigned)__builtin_bit_cast(unsigned short, h2) |
-                       ((unsigned)__builtin_bit_cast(unsigned short, h3) << 16);
-    }
-    lo = u32x4{o[0], o[1], o[2], o[3]};
-    hi = u32x4{o[4], o[5], o[6], o[7]};
+
+// Two bf16 values (one dword) -> two fp16 values (one dword), rounding toward zero: exact for
+// the bf16 values fp16 holds.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w) {
+    const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -128,10 +128,12 @@ template <class DT, int D, int MODE, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
     static_assert(!(DT::kQ8 && FUSED), "INT8 caches take the separate quantising append");
-    using TI = typename DT::In;               // q and MFMA operand type
+    using TI = typename DT::In;               // q type
+    using TM = typename DT::Mma;              // MFMA operand type
+    static_assert(TI::kE == TM::kE, "q chunks and operand chunks line up");
     constexpr int NC = D / (4 * TI::kE);      // operand chunks per lane (q, widened K/V)
     constexpr int NCC = D / (4 * DT::kE);     // cache chunks per lane (K, V)
-    using T = Tile<TI, NC>;
+    using T = Tile<TM, NC>;
     constexpr int NACC = T::kAcc;
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * kStreamWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -225,8 +227,13 @@ void decode_stream_kernel(DecodeParams p) {
                 // widened INT8 chunk m of lane group j holds dims 64m + 16j .. +15: operand
                 // chunks 2m and 2m + 1 take q's dims 64m + 16j .. +7 and .. +15
 #pragma unroll
-                for (int kk = 0; kk < NC; ++kk)
+                for (int kk = 0; kk < NC; ++kk) {
                     q[kk] = load16(qrow + ((kk >> 1) * 64 + 16 * j + 8 * (kk & 1)) * TI::kBytes);
+                    if constexpr (!__is_same(TI, TM)) {  // a bf16 query for fp16 MFMAs
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) q[kk][w] = bf16x2_to_f16x2(q[kk][w]);
+                    }
+                }
             } else {
 #pragma unroll
                 for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qrow + (kk * 4 * TI::kE + j * TI::kE) * TI::kBytes);
@@ -310,8 +317,8 @@ void decode_stream_kernel(DecodeParams p) {
                 u32x4 kt[NC], vt[NC];
 #pragma unroll
                 for (int m = 0; m < NCC; ++m) {
-                    widen_i8<TI>(rb.k[m], kt[2 * m], kt[2 * m + 1]);
-                    widen_i8<TI>(rb.v[m], vt[2 * m], vt[2 * m + 1]);
+                    widen_i8_f16(rb.k[m], kt[2 * m], kt[2 * m + 1]);
+                    widen_i8_f16(rb.v[m], vt[2 * m], vt[2 * m + 1]);
                 }
                 unit(rb, kt, vt);
             } else {
