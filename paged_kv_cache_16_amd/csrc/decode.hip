@@ -216,8 +216,12 @@ void decode_split_kernel(DecodeParams p) {
             p1[i] = __builtin_amdgcn_exp2f(x1[i] - m_use);
         }
         l_run = l_run * alpha + ((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w));
+        // after the first units the running max rarely moves: when no lane's did (alpha = 1
+        // everywhere) the accumulators are left as they are
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
 #pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+            for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+        }
         if (!unit_full(sp, X.t0)) T::mask_v(X.v, keep0);
         if (!unit_full(sp, Y.t0)) T::mask_v(Y.v, keep1);
         T::pv(acc, X.v, p0, upper);

@@ -285,8 +285,12 @@ void decode_stream_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
             l_run = l_run * alpha + ((pr.x + pr.y) + (pr.z + pr.w));
+            // after the first units the running max rarely moves: when no lane's did (alpha = 1
+            // everywhere) the accumulators are left as they are
+            if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
 #pragma unroll
-            for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+                for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+            }
             if (!unit_full(sp, rb.t0)) T::mask_v(vt, keep);
             if constexpr (DT::kQ8) {
                 // V's row scales enter through P (a masked token's scale is never multiplied)
