@@ -576,7 +576,7 @@ def run_layer(w, args, dev):
         kname = f"decode_split_kernel<{dt},{d},full,one kernel" + (">" if args.noalloc else ",fused append>")
     else:
         kname = f"decode_stream_kernel<{dt},{d},full" + (">" if args.noalloc else ",fused append>")
-    plain = not (args.scores or args.kv_dtype or variant or args.split_tokens or args.noalloc)
+    plain = not (args.scores or variant or args.split_tokens or args.noalloc)
     step_desc = ("paged_decode_append_attention: append of the new tokens fused into the persistent split "
                  "kernel, then the LSE combine")
     if args.kv_dtype == "int8":
@@ -612,7 +612,8 @@ def run_layer(w, args, dev):
         "steps_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "kv_bytes_per_step": kv_bytes,
         "roofline": roofline(kname, kv_bytes, kern_ms,
-                             measured_traffic(kname.split("<")[0], w.name) if plain else None, probe),
+                             measured_traffic(kname.split("<")[0], w.name + ("_int8" if args.kv_dtype else ""))
+                             if plain else None, probe),
     }
     return res, lens, variant
 
