@@ -65,7 +65,11 @@
  * contiguous 16-byte load, and the 64 lanes of a wavefront read 1 KiB of
  * consecutive bytes per load. The order is a bijection on each sub-tile, so the
  * pool size equals that of a dense [num_blocks][num_kv_heads][block_size][head_dim]
- * array; only kv_cache_append writes it and only the attention calls read it.
+ * array. The order is the library's: only kv_cache_append and the fused decode step
+ * (paged_decode_append_attention) write a pool, and only the attention calls read it; a
+ * prefill or any other writer goes through kv_cache_append. (The dense order was built and
+ * timed too: V then has to be turned on chip, through LDS, into the matrix instruction's
+ * operand order, and the Llama-3-8B-shaped decode step took 65.8 us against 60.2 us.)
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
