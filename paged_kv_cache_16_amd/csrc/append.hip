@@ -5,34 +5,27 @@
 // attention reads it; with a paged cache ([primer] §4.1) the destination is the slot
 // block * P + offset of a physical block that need not be contiguous with the others.
 //
-// One thread moves one 16-byte chunk of one (token, kv head) row. The K chunk lands as a
-// whole 16-byte chunk of the lane-chunk layout; the V chunk's elements are spread over
-// the sub-tile (each V chunk of the layout interleaves 4 tokens), so they are stored one
-// element at a time. Bytes are copied, never converted.
+// A few tokens: one thread moves one 16-byte chunk of one (token, kv head) row. Many tokens:
+// one wave per 16 tokens and kv head, which writes whole sub-tiles when the tokens fill one.
+// Bytes are copied, never converted.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
+// Moves chunk qc of token i's (kv head h) row: the K chunk lands as a whole 16-byte chunk of
+// the lane-chunk layout; the V chunk's elements are spread over the sub-tile (each V chunk of
+// the layout interleaves 4 tokens), so they are stored one element at a time.
 template <class DT>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+__device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t i, int h, int qc, bool report_slot) {
     constexpr int E = DT::kE;
     constexpr int ES = DT::kBytes;
     constexpr int R = E / 4;
     const int D = p.head_dim;
-    const int chunks = D / E;
-    const int64_t per_token = (int64_t)p.kv_heads * chunks;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= p.num_tokens * per_token) return;
-    const int64_t i = gid / per_token;
-    const int rem = (int)(gid - i * per_token);
-    const int h = rem / chunks;
-    const int qc = rem - h * chunks;
-
     const int64_t slot = p.slots[i];
     if (slot < 0) return;
     if (slot >= p.num_slots) {
-        if (rem == 0) report(p.err, kDevSlot);
+        if (report_slot) report(p.err, kDevSlot);
         return;
     }
     const int64_t blk = slot / p.block_size;
@@ -65,6 +58,83 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         } else {
             *reinterpret_cast<unsigned*>(vbase + (chunk * E + pos) * 4) = vv[e];
         }
+    }
+}
+
+// One thread per 16-byte chunk of a (token, kv head) row: few tokens (a decode step).
+template <class DT>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+    const int chunks = p.head_dim / DT::kE;
+    const int64_t per_token = (int64_t)p.kv_heads * chunks;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= p.num_tokens * per_token) return;
+    const int64_t i = gid / per_token;
+    const int rem = (int)(gid - i * per_token);
+    const int h = rem / chunks;
+    append_chunk<DT>(p, i, h, rem - h * chunks, rem == 0);
+}
+
+// Many tokens (a prefill, or a long append): one wave per (16 consecutive input tokens, kv head).
+// When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots s0 .. s0 + 15 with
+// s0 a multiple of 16), the wave writes the sub-tile's chunks whole: a K chunk is 8 (fp32: 4)
+// dims of one token, taken with one 16-byte load; a V chunk holds 4 tokens x 2 (fp32: 1) dims,
+// gathered from the 4 rows in 2- or 4-byte loads; every store is a 16-byte chunk, 1 KiB per wave
+// instruction. Other groups store chunk by chunk as append_kernel does.
+template <class DT>
+__global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
+    constexpr int E = DT::kE;
+    constexpr int ES = DT::kBytes;
+    constexpr int R = E / 4;
+    const int D = p.head_dim;
+    const int lane = threadIdx.x;
+    const int h = blockIdx.y;
+    const int64_t i0 = (int64_t)blockIdx.x * 16;
+    const int nt = p.num_tokens - i0 < 16 ? (int)(p.num_tokens - i0) : 16;
+    const int my_slot = lane < nt ? p.slots[i0 + lane] : -1;
+    const int s0 = __builtin_amdgcn_readfirstlane(my_slot);
+    const unsigned long long run = __ballot(lane < 16 && (long long)my_slot == (long long)s0 + lane);
+    const bool tile = nt == 16 && s0 >= 0 && (s0 & 15) == 0 && (long long)s0 + 15 < p.num_slots && run == 0xffffull;
+    if (!tile) {
+        const int chunks = D / E;
+        for (int job = lane; job < nt * chunks; job += 64)
+            append_chunk<DT>(p, i0 + job / chunks, h, job % chunks, job % chunks == 0 && h == 0);
+        return;
+    }
+    const int64_t blk = s0 / p.block_size;
+    const int t = (int)(s0 - blk * p.block_size);  // a multiple of 16
+    const size_t sub = (((size_t)blk * p.kv_heads + h) * p.block_size + t) * (size_t)D;
+    const size_t row_stride = (size_t)p.kv_heads * D;  // elements between consecutive tokens' rows
+    const char* krows = (const char*)p.k_new + ((size_t)i0 * p.kv_heads + h) * D * ES;
+    const char* vrows = (const char*)p.v_new + ((size_t)i0 * p.kv_heads + h) * D * ES;
+    const int j = lane >> 4, c = lane & 15;
+    const int nc = D / (4 * E);  // chunk groups per sub-tile
+    for (int kk = 0; kk < nc; ++kk) {
+        // K chunk kk * 64 + lane: token c, dims kk*4E + j*E .. + E - 1
+        const u32x4 kv = load16(krows + ((size_t)c * row_stride + kk * 4 * E + j * E) * ES);
+        *reinterpret_cast<u32x4*>((char*)p.k_cache + (sub + ((size_t)kk * 64 + lane) * E) * ES) = kv;
+        // V chunk kk * 64 + lane: position (n % R) * 4 + i holds token 4j + i, dim 16n + c,
+        // n = kk * R + position / 4
+        unsigned w[4];
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // dword q: positions 2q, 2q + 1
+                unsigned short e2[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int pos = 2 * q + hh;
+                    const int n = kk * R + pos / 4, i = pos % 4;
+                    e2[hh] = *reinterpret_cast<const unsigned short*>(
+                        vrows + ((size_t)(4 * j + i) * row_stride + 16 * n + c) * 2);
+                }
+                w[q] = (unsigned)e2[0] | ((unsigned)e2[1] << 16);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)  // position q: token 4j + q, dim 16 kk + c
+                w[q] = *reinterpret_cast<const unsigned*>(vrows + ((size_t)(4 * j + q) * row_stride + 16 * kk + c) * 4);
+        }
+        *reinterpret_cast<u32x4*>((char*)p.v_cache + (sub + ((size_t)kk * 64 + lane) * E) * ES) =
+            u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
@@ -153,6 +223,10 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
     }
 }
 
+// Appends of at least this many tokens take the sub-tile kernel (a decode step's few tokens, one
+// per sequence, never fill a sub-tile).
+constexpr int64_t kAppendTileMin = 64;
+
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s) {
     if (dtype == kI8B || dtype == kI8H) {
         const int64_t rows = p.num_tokens * p.kv_heads;
@@ -166,10 +240,21 @@ hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s) {
             p.head_dim == 64 ? append_q8_kernel<F16, 64><<<g, b, 0, s>>>(p) : append_q8_kernel<F16, 128><<<g, b, 0, s>>>(p);
         return hipGetLastError();
     }
+    if (p.num_tokens <= 0) return hipSuccess;
+    if (p.num_tokens >= kAppendTileMin) {
+        const int64_t groups = (p.num_tokens + 15) / 16;
+        if (groups > 0x7fffffff || p.kv_heads > 65535) return hipErrorInvalidValue;
+        const dim3 g((unsigned)groups, (unsigned)p.kv_heads), b(64);
+        switch (dtype) {
+            case kF32: append_tile_kernel<F32><<<g, b, 0, s>>>(p); break;
+            case kF16: append_tile_kernel<F16><<<g, b, 0, s>>>(p); break;
+            default: append_tile_kernel<BF16><<<g, b, 0, s>>>(p); break;
+        }
+        return hipGetLastError();
+    }
     const int E = dtype == kF32 ? 4 : 8;
     const int64_t threads = p.num_tokens * p.kv_heads * (p.head_dim / E);
     const int64_t blocks = (threads + 255) / 256;
-    if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     switch (dtype) {
         case kF32: append_kernel<F32><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p); break;

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import synth
-from harness import (TOL, assert_close, gpu_attend, log, make_case, max_err, oracle_attend,
-                     raw_bytes)
+from harness import (NAN_BITS, TOL, assert_close, gpu_attend, log, make_case, max_err,
+                     oracle_attend, raw_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +80,53 @@ def test_append_skips_negative_and_out_of_range_slots():
     torch.cuda.synchronize()
     assert np.array_equal(raw_bytes(c.gk), before_k)
     assert np.array_equal(raw_bytes(c.gv), before_v)
+
+
+@pytest.mark.parametrize("dtype,P,d", [("bf16", 16, 128), ("f16", 32, 64), ("f32", 32, 128)])
+def test_append_long_runs_whole_and_partial_sub_tiles(dtype, P, d):
+    """Appends of 64 tokens or more go 16 tokens at a time: a group whose slots fill one 16-token
+    sub-tile in order is written as whole chunks, every other group chunk by chunk. Groups here:
+    whole sub-tiles (a block's first or second half), consecutive but unaligned slots, a -1 inside
+    an aligned run, an aligned run in reverse order, a slot past the pool, scattered slots and a
+    partial last group. Both pools must equal the oracle's append bit for bit (the slot past the
+    pool skipped and reported)."""
+    import paged_kv_cache_16_amd as pkv
+    Hkv, nb = 2, 24
+    n_slots = nb * P
+    rng = np.random.default_rng(77 + P + d)
+    groups = [
+        list(range(3 * P, 3 * P + 16)),                          # whole sub-tile (a block's first)
+        list(range(5 * P + P - 16, 5 * P + P)),                  # a block's last sub-tile
+        list(range(7 * P + 4, 7 * P + 20)),                      # consecutive, not aligned
+        [9 * P + k if k != 6 else -1 for k in range(16)],        # aligned run with a hole
+        list(range(11 * P + 15, 11 * P - 1, -1)),                # aligned slots in reverse
+        [13 * P + k if k != 9 else n_slots + 3 for k in range(16)],  # one slot past the pool
+        [int(x) for x in rng.choice(np.arange(15 * P, 19 * P), 16, replace=False)],  # scattered
+        list(range(0, 16)),                                      # whole sub-tile of block 0
+        list(range((nb - 1) * P, (nb - 1) * P + 16)),            # the pool's last block
+        list(range(21 * P, 21 * P + 5)),                         # partial last group
+    ]
+    slots = [x for g in groups for x in g]
+    N = len(slots)
+    assert N >= 64 and len({x for x in slots if x >= 0}) == sum(1 for x in slots if x >= 0)
+    log(f"append long run {dtype} P={P} d={d} N={N}")
+    kn = synth.normal((N, Hkv, d), 70, "kn-long", dtype=dtype)
+    vn = synth.normal((N, Hkv, d), 70, "vn-long", dtype=dtype)
+    n_el = nb * Hkv * P * d
+    raw_t = np.float32 if dtype == "f32" else np.uint16
+    kpool = np.full(n_el, NAN_BITS[dtype], dtype=raw_t)
+    vpool = np.full(n_el, NAN_BITS[dtype], dtype=raw_t)
+    oracle.kv_append(dtype, kpool, vpool, synth.raw_numpy(kn), synth.raw_numpy(vn),
+                     np.array([x if x < n_slots else -1 for x in slots], np.int32), P=P, Hkv=Hkv, d=d)
+    tdt = synth.TORCH_DTYPE[dtype]
+    gk = torch.full((nb, Hkv, P, d), float("nan"), dtype=tdt, device="cuda")
+    gv = torch.full((nb, Hkv, P, d), float("nan"), dtype=tdt, device="cuda")
+    pkv.device_errors(clear=True)
+    pkv.kv_cache_append(gk, gv, kn.cuda(), vn.cuda(), torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bytes(gk), kpool.view(np.uint8))
+    assert np.array_equal(raw_bytes(gv), vpool.view(np.uint8))
+    assert pkv.device_errors() == pkv.DEV_SLOT
 
 
 def test_decode_step_append_then_attend():
