@@ -6,7 +6,8 @@
 // block * P + offset of a physical block that need not be contiguous with the others.
 //
 // A few tokens: one thread moves one 16-byte chunk of one (token, kv head) row. Many tokens:
-// one wave per 16 tokens and kv head, which writes whole sub-tiles when the tokens fill one.
+// one wave per 16 tokens, kv head and 64 chunks, which writes whole sub-tiles when the tokens
+// fill one.
 // Bytes are copied, never converted.
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -74,12 +75,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     append_chunk<DT>(p, i, h, rem - h * chunks, rem == 0);
 }
 
-// Many tokens (a prefill, or a long append): one wave per (16 consecutive input tokens, kv head).
-// When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots s0 .. s0 + 15 with
-// s0 a multiple of 16), the wave writes the sub-tile's chunks whole: a K chunk is 8 (fp32: 4)
-// dims of one token, taken with one 16-byte load; a V chunk holds 4 tokens x 2 (fp32: 1) dims,
-// gathered from the 4 rows in 2- or 4-byte loads; every store is a 16-byte chunk, 1 KiB per wave
-// instruction. Other groups store chunk by chunk as append_kernel does.
+// Many tokens (a prefill, or a long append): one wave per (16 consecutive input tokens, kv head,
+// group of 64 chunks). When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots
+// s0 .. s0 + 15 with s0 a multiple of 16), the wave writes its 64 chunks of the sub-tile whole:
+// a K chunk is 8 (fp32: 4) dims of one token, taken with one 16-byte load; a V chunk holds
+// 4 tokens x 2 (fp32: 1) dims, gathered from the 4 rows in 2- or 4-byte loads; every store is a
+// 16-byte chunk, 1 KiB per wave instruction. Other groups store chunk by chunk as append_kernel
+// does, the group's waves sharing the chunks.
 template <class DT>
 __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
     constexpr int E = DT::kE;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
     const bool tile = nt == 16 && s0 >= 0 && (s0 & 15) == 0 && (long long)s0 + 15 < p.num_slots && run == 0xffffull;
     if (!tile) {
         const int chunks = D / E;
-        for (int job = lane; job < nt * chunks; job += 64)
+        for (int job = blockIdx.z * 64 + lane; job < nt * chunks; job += 64 * gridDim.z)
             append_chunk<DT>(p, i0 + job / chunks, h, job % chunks, job % chunks == 0 && h == 0);
         return;
     }
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
     const char* krows = (const char*)p.k_new + ((size_t)i0 * p.kv_heads + h) * D * ES;
     const char* vrows = (const char*)p.v_new + ((size_t)i0 * p.kv_heads + h) * D * ES;
     const int j = lane >> 4, c = lane & 15;
-    const int nc = D / (4 * E);  // chunk groups per sub-tile
-    for (int kk = 0; kk < nc; ++kk) {
+    {
+        const int kk = blockIdx.z;  // this wave's quarter of the sub-tile's chunks
         // K chunk kk * 64 + lane: token c, dims kk*4E + j*E .. + E - 1
         const u32x4 kv = load16(krows + ((size_t)c * row_stride + kk * 4 * E + j * E) * ES);
         *reinterpret_cast<u32x4*>((char*)p.k_cache + (sub + ((size_t)kk * 64 + lane) * E) * ES) = kv;
@@ -244,7 +246,8 @@ hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s) {
     if (p.num_tokens >= kAppendTileMin) {
         const int64_t groups = (p.num_tokens + 15) / 16;
         if (groups > 0x7fffffff || p.kv_heads > 65535) return hipErrorInvalidValue;
-        const dim3 g((unsigned)groups, (unsigned)p.kv_heads), b(64);
+        // z: the sub-tile's chunk groups (D / (4 E) of them), one wave each
+        const dim3 g((unsigned)groups, (unsigned)p.kv_heads, (unsigned)(p.head_dim / (dtype == kF32 ? 16 : 32))), b(64);
         switch (dtype) {
             case kF32: append_tile_kernel<F32><<<g, b, 0, s>>>(p); break;
             case kF16: append_tile_kernel<F16><<<g, b, 0, s>>>(p); break;
