@@ -74,21 +74,20 @@ struct I8H {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// 16 int8 values -> two chunks of 8 fp16 (elements 0..7, 8..15), exact. A byte x becomes
-// k = x + 128 (its sign bit flipped); the fp16 with bits 0x6400 | k is 1024 + k (exponent 10,
-// unit spacing), and 1024 + k - 1152 = x exactly: one byte permute builds two such halves and
-// one packed fp16 subtraction finishes them.
-__device__ __forceinline__ void widen_i8_f16(const u32x4& c, u32x4& lo, u32x4& hi) {
-    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+// 16 int8 values -> two chunks of 8 fp16 (elements 0..7, 8..15) holding x + kI8Bias, exact.
+// A byte x becomes k = x + 128 (its sign bit flipped); the fp16 with bits 0x6400 | k is
+// 1024 + k = x + 1152 (exponent 10, unit spacing): one byte permute builds two such halves.
+// The constant offset is taken out after the products, once per head (attention subtracts
+// kI8Bias * sum(q) from each logit and kI8Bias * sum(p) from each output element).
+constexpr float kI8Bias = 1152.0f;
+__device__ __forceinline__ void widen_i8_f16_biased(const u32x4& c, u32x4& lo, u32x4& hi) {
     unsigned o[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const unsigned k = c[w] ^ 0x80808080u;
         // result bytes: selector 0..3 take bytes of k, 4 takes a 0x64 byte
-        const unsigned a = __builtin_amdgcn_perm(0x64646464u, k, 0x04010400u);  // halves 0x64k0, 0x64k1
-        const unsigned b = __builtin_amdgcn_perm(0x64646464u, k, 0x04030402u);  // halves 0x64k2, 0x64k3
-        o[2 * w] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, a) + bias);
-        o[2 * w + 1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, b) + bias);
+        o[2 * w] = __builtin_amdgcn_perm(0x64646464u, k, 0x04010400u);      // halves 0x64k0, 0x64k1
+        o[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, k, 0x04030402u);  // halves 0x64k2, 0x64k3
     }
     lo = u32x4{o[0], o[1], o[2], o[3]};
     hi = u32x4{o[4], o[5], o[6], o[7]};

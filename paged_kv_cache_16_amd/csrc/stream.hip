@@ -239,7 +239,21 @@ void decode_stream_kernel(DecodeParams p) {
                 for (int kk = 0; kk < NC; ++kk) q[kk] = load16(qrow + (kk * 4 * TI::kE + j * TI::kE) * TI::kBytes);
             }
         }
+        // INT8: the widened K carries kI8Bias on every element, so a logit comes out high by
+        // kI8Bias * sum_d q[d] for its head: the fp16 query as the products take it, summed
+        // over the lane's dims and then over the 4 lanes of the head's column.
+        float qbias = 0.f;
+        if constexpr (DT::kQ8) {
+            float qs = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NC; ++kk) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) qs += f16_lo_f32(q[kk][w]) + f16_hi_f32(q[kk][w]);
+            }
+            qbias = kI8Bias * xor32_sum(xor16_sum(qs));
+        }
         float m_run = kNegInf, l_run = 0.f;
+        float pv_run = 0.f;  // INT8: running sum of the P operand (p times V's row scale)
         f32x4 acc[NACC];
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[a] = zero4();
@@ -268,7 +282,7 @@ void decode_stream_kernel(DecodeParams p) {
             float mx = kNegInf;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float si = DT::kQ8 ? s[i] * rb.ks[i] : s[i];  // dequantised logit
+                const float si = DT::kQ8 ? (s[i] - qbias) * rb.ks[i] : s[i];  // dequantised logit
                 x[i] = (keep >> i) & 1 ? si * qk_scale : kNegInf;
                 mx = fmaxf(mx, x[i]);
             }
@@ -291,14 +305,16 @@ void decode_stream_kernel(DecodeParams p) {
 #pragma unroll
                 for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
             }
-            if (!unit_full(sp, rb.t0)) T::mask_v(vt, keep);
             if constexpr (DT::kQ8) {
-                // V's row scales enter through P (a masked token's scale is never multiplied)
+                // V's row scales enter through P (a masked token's scale is never multiplied).
+                // A masked token's P is 0 and its widened V finite, so its V needs no masking.
                 f32x4 pv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pv[i] = (keep >> i) & 1 ? pr[i] * rb.vs[i] : 0.f;
+                pv_run = pv_run * alpha + ((pv.x + pv.y) + (pv.z + pv.w));
                 T::pv(acc, vt, pv, upper);
             } else {
+                if (!unit_full(sp, rb.t0)) T::mask_v(vt, keep);
                 T::pv(acc, vt, pr, upper);
             }
             m_run = m_new;
@@ -321,8 +337,8 @@ void decode_stream_kernel(DecodeParams p) {
                 u32x4 kt[NC], vt[NC];
 #pragma unroll
                 for (int m = 0; m < NCC; ++m) {
-                    widen_i8_f16(rb.k[m], kt[2 * m], kt[2 * m + 1]);
-                    widen_i8_f16(rb.v[m], vt[2 * m], vt[2 * m + 1]);
+                    widen_i8_f16_biased(rb.k[m], kt[2 * m], kt[2 * m + 1]);
+                    widen_i8_f16_biased(rb.v[m], vt[2 * m], vt[2 * m + 1]);
                 }
                 unit(rb, kt, vt);
             } else {
@@ -391,6 +407,13 @@ void decode_stream_kernel(DecodeParams p) {
         if constexpr (SCORES) flush();
         // End of the run: the finished row, or a partial for the combine.
         const float l_tot = xor32_sum(xor16_sum(l_run));
+        if constexpr (DT::kQ8) {
+            // the widened V's offset: every output element of a head is high by kI8Bias times
+            // the sum of that head's P operand
+            const float vbias = kI8Bias * xor32_sum(xor16_sum(pv_run));
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) acc[a] -= vbias;
+        }
         const int head = T::acc_head(c);
         const bool writer = head < G && T::acc_owner(c);
         const bool last = u0 + cnt == nu;
