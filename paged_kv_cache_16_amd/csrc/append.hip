@@ -75,20 +75,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     append_chunk<DT>(p, i, h, rem - h * chunks, rem == 0);
 }
 
-// Many tokens (a prefill, or a long append): one wave per (16 consecutive input tokens, kv head,
-// group of 64 chunks). When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots
+// Many tokens (a prefill, or a long append): one workgroup per (16 consecutive input tokens,
+// kv head), one wave per group of 64 chunks of the sub-tile (D / 4E waves: the waves read the
+// quarters of the same 128-byte lines together). When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots
 // s0 .. s0 + 15 with s0 a multiple of 16), the wave writes its 64 chunks of the sub-tile whole:
 // a K chunk is 8 (fp32: 4) dims of one token, taken with one 16-byte load; a V chunk holds
-// 4 tokens x 2 (fp32: 1) dims, gathered from the 4 rows in 2- or 4-byte loads; every store is a
-// 16-byte chunk, 1 KiB per wave instruction. Other groups store chunk by chunk as append_kernel
-// does, the group's waves sharing the chunks.
+// 4 tokens x 2 (fp32: 1) dims, read back from the 16 rows' block staged in LDS (one 16-byte load
+// per lane); every store is a 16-byte chunk, 1 KiB per wave instruction. Other groups store chunk
+// by chunk as append_kernel does, the group's waves sharing the chunks.
 template <class DT>
-__global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
+__global__ __launch_bounds__(512) void append_tile_kernel(AppendParams p) {
     constexpr int E = DT::kE;
     constexpr int ES = DT::kBytes;
     constexpr int R = E / 4;
     const int D = p.head_dim;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int kk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the wave's 64 chunks of the sub-tile
     const int h = blockIdx.y;
     const int64_t i0 = (int64_t)blockIdx.x * 16;
     const int nt = p.num_tokens - i0 < 16 ? (int)(p.num_tokens - i0) : 16;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
     const bool tile = nt == 16 && s0 >= 0 && (s0 & 15) == 0 && (long long)s0 + 15 < p.num_slots && run == 0xffffull;
     if (!tile) {
         const int chunks = D / E;
-        for (int job = blockIdx.z * 64 + lane; job < nt * chunks; job += 64 * gridDim.z)
+        for (int job = threadIdx.x; job < nt * chunks; job += blockDim.x)
             append_chunk<DT>(p, i0 + job / chunks, h, job % chunks, job % chunks == 0 && h == 0);
         return;
     }
@@ -110,12 +112,22 @@ __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
     const char* vrows = (const char*)p.v_new + ((size_t)i0 * p.kv_heads + h) * D * ES;
     const int j = lane >> 4, c = lane & 15;
     {
-        const int kk = blockIdx.z;  // this wave's quarter of the sub-tile's chunks
         // K chunk kk * 64 + lane: token c, dims kk*4E + j*E .. + E - 1
         const u32x4 kv = load16(krows + ((size_t)c * row_stride + kk * 4 * E + j * E) * ES);
         *reinterpret_cast<u32x4*>((char*)p.k_cache + (sub + ((size_t)kk * 64 + lane) * E) * ES) = kv;
-        // V chunk kk * 64 + lane: position (n % R) * 4 + i holds token 4j + i, dim 16n + c,
-        // n = kk * R + position / 4
+        // V: the wave's 64 chunks hold tokens 0..15 x dims kk*4E .. kk*4E + 4E - 1, the same
+        // 64 bytes of each token's row. Lane (token l / 4, quarter l % 4) loads 16 of them into
+        // LDS (rows 80 bytes apart), and lane (j, c) reads back the elements of its chunk:
+        // position (n % R) * 4 + i holds token 4j + i, dim 16n + c, n = kk * R + position / 4,
+        // which is local dim 16 * (position / 4) + c of the block.
+        __shared__ __attribute__((aligned(16))) unsigned char vblks[8][16 * 80];
+        unsigned char* vblk = vblks[kk];
+        {
+            const int tk = lane >> 2, qt = lane & 3;
+            *reinterpret_cast<u32x4*>(vblk + tk * 80 + qt * 16) =
+                load16(vrows + ((size_t)tk * row_stride + kk * 4 * E + qt * E) * ES);
+        }
+        __syncthreads();  // every wave of the group takes this path (the same slots decide it)
         unsigned w[4];
         if constexpr (ES == 2) {
 #pragma unroll
@@ -124,16 +136,15 @@ __global__ __launch_bounds__(64) void append_tile_kernel(AppendParams p) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int pos = 2 * q + hh;
-                    const int n = kk * R + pos / 4, i = pos % 4;
-                    e2[hh] = *reinterpret_cast<const unsigned short*>(
-                        vrows + ((size_t)(4 * j + i) * row_stride + 16 * n + c) * 2);
+                    e2[hh] = *reinterpret_cast<const unsigned short*>(vblk + (4 * j + pos % 4) * 80 +
+                                                                      (16 * (pos / 4) + c) * 2);
                 }
                 w[q] = (unsigned)e2[0] | ((unsigned)e2[1] << 16);
             }
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)  // position q: token 4j + q, dim 16 kk + c
-                w[q] = *reinterpret_cast<const unsigned*>(vrows + ((size_t)(4 * j + q) * row_stride + 16 * kk + c) * 4);
+                w[q] = *reinterpret_cast<const unsigned*>(vblk + (4 * j + q) * 80 + c * 4);
         }
         *reinterpret_cast<u32x4*>((char*)p.v_cache + (sub + ((size_t)kk * 64 + lane) * E) * ES) =
             u32x4{w[0], w[1], w[2], w[3]};
@@ -246,8 +257,8 @@ hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t s) {
     if (p.num_tokens >= kAppendTileMin) {
         const int64_t groups = (p.num_tokens + 15) / 16;
         if (groups > 0x7fffffff || p.kv_heads > 65535) return hipErrorInvalidValue;
-        // z: the sub-tile's chunk groups (D / (4 E) of them), one wave each
-        const dim3 g((unsigned)groups, (unsigned)p.kv_heads, (unsigned)(p.head_dim / (dtype == kF32 ? 16 : 32))), b(64);
+        // one wave per 64-chunk group of the sub-tile (D / (4 E) of them)
+        const dim3 g((unsigned)groups, (unsigned)p.kv_heads), b(64 * (unsigned)(p.head_dim / (dtype == kF32 ? 16 : 32)));
         switch (dtype) {
             case kF32: append_tile_kernel<F32><<<g, b, 0, s>>>(p); break;
             case kF16: append_tile_kernel<F16><<<g, b, 0, s>>>(p); break;
