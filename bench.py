@@ -40,7 +40,7 @@ MIN_EVENT_LAUNCHES = 50
 
 # The sources that define the measured kernels and their launch (grid, split plan): a change to
 # any of them invalidates the committed HBM counters.
-KERNEL_SOURCES = ("api.hip", "append.hip", "decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_plan.h",
+KERNEL_SOURCES = ("api.hip", "append.hip", "decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_plan.h", "pkv_q8.h",
                   "stream.hip")
 
 

@@ -11,6 +11,7 @@
 // Bytes are copied, never converted.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_q8.h"
 
 namespace pkv {
 
@@ -151,32 +152,8 @@ __global__ __launch_bounds__(512) void append_tile_kernel(AppendParams p) {
     }
 }
 
-// INT8 cache ([primer] §4.2: the int8 KV cache halves the bytes per token). One wavefront
-// quantises one (token, kv head) row of K and of V: amax = max |x| in fp32 (a wave-wide
-// max), scale = amax / 127, q = rint(x * (127 / amax)) clamped to [-127, 127], both
-// divisions correctly rounded in fp32, a zero row giving scale 0 and q = 0 (symmetric, one
-// scale per row, so no earlier token is ever re-quantised). The bytes go to the row's
-// lane-chunk positions (16 elements per chunk) and the scale to the pool's fp32 scale
-// plane [num_blocks][Hkv][P], which follows the data plane.
-template <class In>
-__device__ __forceinline__ float in_f32(const void* base, size_t idx) {
-    const unsigned short h = reinterpret_cast<const unsigned short*>(base)[idx];
-    if constexpr (__is_same(In, BF16))
-        return __uint_as_float((unsigned)h << 16);
-    else
-        return (float)__builtin_bit_cast(_Float16, h);
-}
-
-// Max over the wave of two values side by side (their cross-lane steps overlap).
-__device__ __forceinline__ void wave_max2(float& a, float& b) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float ta = __shfl_xor(a, off), tb = __shfl_xor(b, off);
-        a = fmaxf(a, ta);
-        b = fmaxf(b, tb);
-    }
-}
-
+// INT8 cache: one wavefront quantises and stores one (token, kv head) row of K and of V
+// (q8_store_row: per-row amax and scale, codes at the row's lane-chunk positions).
 template <class In, int D>
 __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
     constexpr int PER = D / 64;  // elements per lane
@@ -202,38 +179,8 @@ __global__ __launch_bounds__(256) void append_q8_kernel(AppendParams p) {
         av = fmaxf(av, fabsf(xv[e]));
     }
     wave_max2(ak, av);
-    if (slot < 0) return;
-    if (slot >= p.num_slots) {
-        if (h == 0 && lane == 0) report(p.err, kDevSlot);
-        return;
-    }
-    const int64_t blk = slot / p.block_size;
-    const int t = (int)(slot - blk * p.block_size);
-    const int tau = t & 15;
-    const size_t sub = (((size_t)blk * p.kv_heads + h) * p.block_size + (t - tau)) * (size_t)D;
-    const size_t plane = (size_t)p.num_slots * p.kv_heads * D;  // bytes of the data plane
-    const size_t srow = ((size_t)blk * p.kv_heads + h) * p.block_size + t;
-#pragma unroll
-    for (int is_v = 0; is_v < 2; ++is_v) {
-        char* pool = (char*)(is_v ? p.v_cache : p.k_cache);
-        const float amax = is_v ? av : ak;
-        const float inv = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            float r = amax > 0.f ? rintf((is_v ? xv[e] : xk[e]) * inv) : 0.f;
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            const int xd = lane + 64 * e;
-            size_t pos;
-            if (is_v) {
-                const int n = xd >> 4;
-                pos = (((size_t)(n >> 2) * 4 + (tau >> 2)) * 16 + (xd & 15)) * 16 + (size_t)(n & 3) * 4 + (tau & 3);
-            } else {
-                pos = ((size_t)(xd >> 6) * 64 + (size_t)((xd >> 4) & 3) * 16 + tau) * 16 + (xd & 15);
-            }
-            pool[sub + pos] = (char)(signed char)(int)r;
-        }
-        if (lane == 0) *reinterpret_cast<float*>(pool + plane + srow * 4) = amax > 0.f ? __fdiv_rn(amax, 127.f) : 0.f;
-    }
+    q8_store_row<D>((char*)p.k_cache, (char*)p.v_cache, xk, xv, ak, av, slot, p.block_size, p.kv_heads, h,
+                    p.num_slots, p.err, lane);
 }
 
 // Appends of at least this many tokens take the sub-tile kernel (a decode step's few tokens, one
