@@ -44,15 +44,25 @@ KERNEL_SOURCES = ("api.hip", "append.hip", "decode.hip", "pkv_device.h", "pkv_in
                   "stream.hip")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over KERNEL_SOURCES (names and contents, in that order)."""
+def code_only(text: str) -> str:
+    """C/C++/HIP source without its comments, trailing blanks and empty lines (the sources carry no
+    comment markers inside string literals)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def kernel_source_hash(csrc: str = None) -> str:
+    """sha256 over KERNEL_SOURCES (names and code without comments, in that order): an edit to a
+    comment keeps the committed counters valid, any edit to the code does not."""
     import hashlib
-    csrc = os.path.join(ROOT, "paged_kv_cache_16_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "paged_kv_cache_16_amd", "csrc")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         h.update(name.encode())
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -6,9 +6,9 @@
 // block * P + offset of a physical block that need not be contiguous with the others.
 //
 // A few tokens: one thread moves one 16-byte chunk of one (token, kv head) row. Many tokens:
-// one wave per 16 tokens, kv head and 64 chunks, which writes whole sub-tiles when the tokens
-// fill one.
-// Bytes are copied, never converted.
+// one workgroup per 16 tokens and kv head (a wave per 64 chunks), which writes whole sub-tiles
+// when the tokens fill one. Bytes are copied, never converted (an INT8 cache's rows are
+// quantised: append_q8_kernel).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_q8.h"
@@ -78,12 +78,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
 // Many tokens (a prefill, or a long append): one workgroup per (16 consecutive input tokens,
 // kv head), one wave per group of 64 chunks of the sub-tile (D / 4E waves: the waves read the
-// quarters of the same 128-byte lines together). When the 16 tokens go to the 16 consecutive slots of one sub-tile (slots
-// s0 .. s0 + 15 with s0 a multiple of 16), the wave writes its 64 chunks of the sub-tile whole:
-// a K chunk is 8 (fp32: 4) dims of one token, taken with one 16-byte load; a V chunk holds
-// 4 tokens x 2 (fp32: 1) dims, read back from the 16 rows' block staged in LDS (one 16-byte load
-// per lane); every store is a 16-byte chunk, 1 KiB per wave instruction. Other groups store chunk
-// by chunk as append_kernel does, the group's waves sharing the chunks.
+// quarters of the same 128-byte lines together). When the 16 tokens go to the 16 consecutive
+// slots of one sub-tile (slots s0 .. s0 + 15 with s0 a multiple of 16), each wave writes its 64
+// chunks of the sub-tile whole: a K chunk is 8 (fp32: 4) dims of one token, taken with one
+// 16-byte load; a V chunk holds 4 tokens x 2 (fp32: 1) dims, read back from the 16 rows' block
+// staged in LDS (one 16-byte load per lane); every store is a 16-byte chunk, 1 KiB per wave
+// instruction. Other groups store chunk by chunk as append_kernel does, the group's waves
+// sharing the chunks.
 template <class DT>
 __global__ __launch_bounds__(512) void append_tile_kernel(AppendParams p) {
     constexpr int E = DT::kE;
