@@ -9,9 +9,9 @@
 // are resident on the GPU at once; wave w takes the contiguous units [w*C, (w+1)*C) with
 // C = max(ceil(N / waves), chunk_min), so every wave streams the same number of bytes no
 // matter how ragged the context lengths are, and no wave waits for a second launch round.
-// A wave keeps three units of K/V loads in flight (a 4-deep ring of register buffers) and
-// carries the pipeline across segment boundaries. At the end of its part of a segment it
-// writes either the finished, normalised row (when it holds the whole segment) or an
+// A wave streams its units through a small ring of register buffers (2-deep for 2- and 4-byte
+// caches, 3-deep for INT8), refilled at every segment boundary. At the end of its part of a
+// segment it writes either the finished, normalised row (when it holds the whole segment) or an
 // (o, m, l) partial: piece k = w - first_wave(segment) goes to the segment's own slot k when
 // k < kSegSlots, else to wave w's overflow slot (a piece k >= 1 is the first run of its wave,
 // so a wave fills at most one overflow slot). The wave holding a segment's last unit records
@@ -372,7 +372,8 @@ void decode_stream_kernel(DecodeParams p) {
             // conservatively (ring_load), so about one unit is in flight per wave either way,
             // and the shallower ring asks for less at once when every wave starts (Llama-3-8B
             // layer step 61.3 -> 60.7 us; depth 3 61.0 us). INT8 caches, counted exactly, take
-            // depth 4 (a deeper ring measured slower: more bytes in flight only queue).
+            // depth 3 (kernel 32.8 us against 33.3 us with depth 4 and 33.1 us with depth 2, now
+            // that the widening is a byte permute per two values; more bytes in flight only queue).
             if constexpr (!DT::kQ8) {
                 RingBuf<DT, D> R0, R1;
                 ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
@@ -384,22 +385,18 @@ void decode_stream_kernel(DecodeParams p) {
                     process(R1);
                 }
             } else {
-                RingBuf<DT, D> R0, R1, R2, R3;
+                RingBuf<DT, D> R0, R1, R2;
                 ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
                 ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
-                ring_load<DT, D>(p, R2, my_tok, my_off, 2, n, lane, u0 + ub);
-                for (int k = 0; k < n; k += 4) {
-                    ring_load<DT, D>(p, R3, my_tok, my_off, k + 3, n, lane, u0 + ub);
+                for (int k = 0; k < n; k += 3) {
+                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 2, n, lane, u0 + ub);
                     process(R0);
                     if (k + 1 >= n) break;
-                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 4, n, lane, u0 + ub);
+                    ring_load<DT, D>(p, R0, my_tok, my_off, k + 3, n, lane, u0 + ub);
                     process(R1);
                     if (k + 2 >= n) break;
-                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 5, n, lane, u0 + ub);
+                    ring_load<DT, D>(p, R1, my_tok, my_off, k + 4, n, lane, u0 + ub);
                     process(R2);
-                    if (k + 3 >= n) break;
-                    ring_load<DT, D>(p, R2, my_tok, my_off, k + 6, n, lane, u0 + ub);
-                    process(R3);
                 }
             }
         }
