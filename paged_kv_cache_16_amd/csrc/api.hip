@@ -118,8 +118,9 @@ void choose_path(Plan& pl, const pkv_decode_opts* o) {
         pl.units_per_split = pl.units_bound <= kDirectShortUnits ? kDirectShortUnits : kDirectWideUnits;
     } else {
         pl.path = Plan::kStream;
-        // at least kStreamChunkMin units per wave, and few enough slots per segment for
-        // the combine's LDS table
+        // at least kStreamChunkMin units per wave, and at most kMaxSlots pieces per segment
+        // (past its first kSegSlots + kCombineWide pieces the combine takes one round trip
+        // per kSegSlots more)
         // A run's set-up (query and descriptors fetched, load ring refilled, and the previous
         // run's partial stored) costs a wave about what streaming kRunSetupBytes does, so every
         // segment start counts as that many bytes' worth of units: a wave whose share crosses

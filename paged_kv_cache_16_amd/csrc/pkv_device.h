@@ -123,6 +123,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, in
 __device__ __forceinline__ u32x4 load16_tile_stream(__amdgpu_buffer_rsrc_t r, unsigned voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 2);
 }
+// 4 bytes at byte offset `voff` of the resource, default cache policy.
+__device__ __forceinline__ float load4_buf(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+// PER consecutive floats (1, 2 or 4) at byte offset `voff` of the resource, one load.
+template <int PER>
+__device__ __forceinline__ void load_f32_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, float (&x)[PER]) {
+    static_assert(PER == 1 || PER == 2 || PER == 4, "one 4-, 8- or 16-byte load");
+    if constexpr (PER == 1) {
+        x[0] = load4_buf(r, voff);
+    } else if constexpr (PER == 2) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+        x[0] = __uint_as_float(t[0]);
+        x[1] = __uint_as_float(t[1]);
+    } else {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(t[i]);
+    }
+}
 // 16 bytes at byte offset `voff` of the resource, default cache policy.
 __device__ __forceinline__ u32x4 load16_tile(__amdgpu_buffer_rsrc_t r, unsigned voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
@@ -148,6 +168,25 @@ __device__ __forceinline__ float xor32_sum(float x) {
 __device__ __forceinline__ float xor16_sum(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max / sum over each 16-lane row with DPP (swap neighbours, swap pairs, mirror each half-row,
+// mirror the row): every lane of the row ends with the row's value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+    return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    return x + dpp_f<0x140>(x);
 }
 
 // Inclusive prefix sum over the wave with DPP: shifts by 1, 2, 4 and 8 lanes inside each

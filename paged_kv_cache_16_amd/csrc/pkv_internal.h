@@ -15,8 +15,11 @@ constexpr int kWaves = 4;           // wavefronts per workgroup of the split ker
 constexpr int kStreamWaves = 4;    // wavefronts per workgroup of the persistent kernel
 constexpr int kMaxUnitsPerWave = 64;  // unit descriptors are held one per lane
 constexpr int kMaxSlots = 512;      // most pieces a segment is cut into on the persistent path
-constexpr int kSegSlots = 8;        // partial slots held per segment (its first pieces); later
+constexpr int kSegSlots = 16;       // partial slots held per segment (its first pieces); later
                                     // pieces go to one overflow slot per wave
+constexpr int kCombineWide = 24;   // pieces past the first kSegSlots that the combine requests in its
+                                    // second round trip (at most 32: lanes 0..31 hold their (m, l))
+static_assert(kCombineWide <= 32, "the combine reduces (m, l) over lanes 0..31");
 constexpr int kMaxGroup = 8;        // query heads per kv head (each in 2 of the 16 MFMA columns)
 constexpr int kDirectMaxUnits = 40;  // units per segment the one-kernel path takes (and stages
                                      // logits for, with score export)

@@ -16,7 +16,9 @@
 // k < kSegSlots, else to wave w's overflow slot (a piece k >= 1 is the first run of its wave,
 // so a wave fills at most one overflow slot). The wave holding a segment's last unit records
 // the piece count and the first wave. The combine kernel then merges the pieces by
-// log-sum-exp ([Novita] §關鍵技術 2: partial softmax results merge through max and sum).
+// log-sum-exp ([Novita] §關鍵技術 2: partial softmax results merge through max and sum): one
+// round trip covers the first 8, 12 or 16 pieces, a second the rest of the segment's own slots and
+// up to kCombineWide overflow pieces, and each later one kCombineWide more.
 // Workspace rows: (B * Hkv * kSegSlots + waves) x G, whatever the context lengths.
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -461,13 +463,71 @@ void decode_stream_kernel(DecodeParams p) {
     }
 }
 
-// Merges the partials of one (sequence, query head) row per 64-thread workgroup. The row's
-// slot count and its per-slot (m, l) are uniform, so they arrive through scalar loads; each
-// lane owns D/64 dims and fetches its slices of all partial rows in unrolled batches.
+// A batch of up to KX partials of one row, in consecutive slots G rows apart: lane u holds piece
+// u's (m, l) (m in log2 units), every lane its D/64 dims of each piece's o.
+template <int KX, int PER>
+struct RowBatch {
+    float v[KX][PER];
+    float m, l;
+};
+
+// Requests pieces 0 .. n_load - 1 of a batch starting at row0, all at once, through resources
+// that span only those pieces: reads past them return zero and touch no memory.
+template <int KX, int D>
+__device__ __forceinline__ void load_rows(const DecodeParams& p, RowBatch<KX, D / 64>& rb, size_t row0, int n_load,
+                                          int G, int lane) {
+    static_assert(KX <= 32, "(m, l) are reduced over lanes 0..31");
+    constexpr int PER = D / 64;
+    const __amdgpu_buffer_rsrc_t orr =
+        tile_rsrc(reinterpret_cast<const char*>(p.o_part + row0 * D), n_load * G * D * 4);
+    const __amdgpu_buffer_rsrc_t mr = tile_rsrc(reinterpret_cast<const char*>(p.m_part + row0), n_load * G * 4);
+    const __amdgpu_buffer_rsrc_t lr = tile_rsrc(reinterpret_cast<const char*>(p.l_part + row0), n_load * G * 4);
+#pragma unroll
+    for (int u = 0; u < KX; ++u) load_f32_buf<PER>(orr, (unsigned)((u * G * D + lane * PER) * 4), rb.v[u]);
+    rb.m = load4_buf(mr, (unsigned)(lane * G * 4));
+    rb.l = load4_buf(lr, (unsigned)(lane * G * 4));
+}
+
+// Folds the batch's first n_live pieces, of those the ones that attended a token (l > 0), into
+// the row's running (M, Ls, o).
+template <int KX, int PER>
+__device__ __forceinline__ void merge_rows(float& M, float& Ls, float (&o)[PER], const RowBatch<KX, PER>& rb,
+                                           int n_live, int lane) {
+    const bool live = lane < n_live && rb.l > 0.f;
+    const float bm = __int_as_float(
+        __builtin_amdgcn_readfirstlane(__float_as_int(xor16_max(row16_max(live ? rb.m : kNegInf)))));
+    const float m_new = fmaxf(M, bm);
+    if (m_new == kNegInf) return;
+    const float sc = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+    const float w_lane = live ? __builtin_amdgcn_exp2f(rb.m - m_new) : 0.f;
+    const float lw = __int_as_float(
+        __builtin_amdgcn_readfirstlane(__float_as_int(xor16_sum(row16_sum(live ? w_lane * rb.l : 0.f)))));
+    Ls = Ls * sc + lw;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] *= sc;
+    // pieces past n_live are dropped by selection here and in the sum above, not by a zero
+    // weight: a stale slot may hold inf or NaN
+#pragma unroll
+    for (int u = 0; u < KX; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), u));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += u < n_live ? w * rb.v[u][i] : 0.f;
+    }
+    M = m_new;
+}
+
+// Merges the partials of one (sequence, query head) row per 64-thread workgroup.
 // Rows of sequences without units get out = 0 and lse = -inf here; rows the stream kernel
 // finished itself (count 0) are skipped.
-template <int D, int MODE, int ES>
+// The first KB pieces (KB = 8, 12 or 16, the launch's estimate of the most pieces a segment has) sit
+// in the segment's own slots and are requested whole, together with the count and the context
+// length (the three loads share one round trip); those past the count are dropped by selection
+// (their slots hold stale values, never multiplied in). The rest of the own slots and up to
+// kCombineWide overflow pieces (slots of waves w0 + k) share the second round trip; longer
+// segments take one more per kCombineWide pieces.
+template <int D, int MODE, int ES, int KB>
 __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
+    static_assert(KB <= kSegSlots, "the first batch is the segment's own slots");
     constexpr int PER = D / 64;
     const int r = blockIdx.x;
     if (r >= p.batch * p.q_heads) {
@@ -481,28 +541,13 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     const int b = g / p.kv_heads, kvh = g - b * p.kv_heads;
     const int lane = threadIdx.x;
     const size_t hrow = (size_t)b * p.q_heads + kvh * G + head;
-    // Pieces come in batches of KB, fetched whole; those past the count are dropped by selection
-    // (their slots hold stale values, never multiplied in). The first batch is the segment's own
-    // slots, so it is requested before the count and the context length arrive and the three
-    // loads share one round trip; later batches sit in the overflow slots of waves w0 + k.
-    constexpr int KB = kSegSlots;  // one wave per SIMD leaves at most ~7 pieces per segment at 4k contexts
-    const size_t base = (size_t)g * KB * G + head;  // piece k < KB: row base + k * G
-    const size_t ovf = (size_t)p.batch * p.kv_heads * KB * G + head;  // piece k >= KB: row ovf + (w0 + k) * G
-    float lv[KB], mv[KB], v[KB][PER];
-    auto fetch = [&](auto row_of) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < KB; ++u) {
-            const size_t rk = row_of(u);
-            lv[u] = p.l_part[rk];
-            mv[u] = p.m_part[rk];
-#pragma unroll
-            for (int i = 0; i < PER; ++i) v[u][i] = p.o_part[rk * D + lane * PER + i];
-        }
-    };
+    const size_t base = (size_t)g * kSegSlots * G + head;  // piece k < kSegSlots: row base + k * G
+    const size_t ovf = (size_t)p.batch * p.kv_heads * kSegSlots * G + head;  // later piece k: row ovf + (w0 + k) * G
+    RowBatch<KB, PER> first;
+    load_rows<KB, D>(p, first, base, KB, G, lane);
     int cnt = p.seg_count[2 * g];
     int w0 = p.seg_count[2 * g + 1];
     w0 = w0 < 0 ? 0 : (w0 >= p.waves_total ? p.waves_total - 1 : w0);  // in range by construction
-    fetch([&](int u) { return base + (size_t)u * G; });
     const int nu = seq_units<MODE>(p, b);
     // one branch on both values (no short circuit): with the count tested only past the
     // empty-sequence case, its load was issued after the first batch had returned
@@ -517,42 +562,43 @@ __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     }
     // never past the last wave by construction; keeps every read in bounds
     if (cnt > p.waves_total - w0) cnt = p.waves_total - w0;
-    // online merge over the batches
     float M = kNegInf, Ls = 0.f;
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    for (int k = 0;;) {
-        float bm = kNegInf;
-#pragma unroll
-        for (int u = 0; u < KB; ++u) {
-            const bool live = k + u < cnt && lv[u] > 0.f;
-            bm = fmaxf(bm, live ? mv[u] : kNegInf);
-        }
-        const float m_new = fmaxf(M, bm);
-        if (m_new != kNegInf) {
-            const float sc = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
-            Ls *= sc;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) o[i] *= sc;
-#pragma unroll
-            for (int u = 0; u < KB; ++u) {
-                const bool live = k + u < cnt && lv[u] > 0.f;
-                const float w = live ? __builtin_amdgcn_exp2f(mv[u] - m_new) : 0.f;
-                Ls += live ? w * lv[u] : 0.f;
-#pragma unroll
-                for (int i = 0; i < PER; ++i) o[i] += live ? w * v[u][i] : 0.f;
+    merge_rows<KB, PER>(M, Ls, o, first, cnt, lane);
+    if (cnt > KB) {
+        // The rest of the own slots (KB .. kSegSlots - 1) and the first overflow batch (pieces
+        // kSegSlots, ... in the slots of waves w0 + kSegSlots, ...) depend only on the count and
+        // w0: both are requested before either is merged, one round trip for the two.
+        constexpr int KO = KB < kSegSlots ? kSegSlots - KB : 1;
+        const int n_own = KB < kSegSlots ? (cnt < kSegSlots ? cnt : kSegSlots) - KB : 0;
+        RowBatch<KO, PER> ro;
+        load_rows<KO, D>(p, ro, base + (size_t)KB * G, n_own, G, lane);
+        const int n_ov = cnt - kSegSlots;
+        const size_t row_ov = ovf + (size_t)(w0 + kSegSlots) * G;
+        if (n_ov <= 0) {
+            merge_rows<KO, PER>(M, Ls, o, ro, n_own, lane);
+        } else if (n_ov <= 8) {
+            RowBatch<8, PER> rv;
+            load_rows<8, D>(p, rv, row_ov, n_ov, G, lane);
+            if (n_own > 0) merge_rows<KO, PER>(M, Ls, o, ro, n_own, lane);
+            merge_rows<8, PER>(M, Ls, o, rv, n_ov, lane);
+        } else {
+            const int nx = n_ov < kCombineWide ? n_ov : kCombineWide;
+            RowBatch<kCombineWide, PER> rv;
+            load_rows<kCombineWide, D>(p, rv, row_ov, nx, G, lane);
+            if (n_own > 0) merge_rows<KO, PER>(M, Ls, o, ro, n_own, lane);
+            merge_rows<kCombineWide, PER>(M, Ls, o, rv, nx, lane);
+            // longer segments: the rest of the overflow slots, up to kCombineWide per round trip
+            for (int k = kSegSlots + nx; k < cnt;) {
+                const int n = cnt - k < kCombineWide ? cnt - k : kCombineWide;
+                RowBatch<kCombineWide, PER> rb;
+                load_rows<kCombineWide, D>(p, rb, ovf + (size_t)(w0 + k) * G, n, G, lane);
+                merge_rows<kCombineWide, PER>(M, Ls, o, rb, n, lane);
+                k += n;
             }
-            M = m_new;
         }
-        k += KB;
-        if (k >= cnt) break;
-        // pieces k .. k + KB - 1 in the overflow slots of waves w0 + k + u (a slot past the last
-        // wave belongs to no piece of the count: the last wave's is read instead, and dropped)
-        fetch([&](int u) {
-            const int wv = w0 + k + u < p.waves_total ? w0 + k + u : p.waves_total - 1;
-            return ovf + (size_t)wv * G;
-        });
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
@@ -757,8 +803,18 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
         err = hipEventRecord(e1, s);
         if (err != hipSuccess) return err;
     }
-    stream_combine_kernel<D, MODE, DT::kBytes>
-        <<<dim3((unsigned)(p.batch * p.q_heads + (p.new_slots ? p.batch * p.kv_heads : 0))), dim3(64), 0, s>>>(p);
+    // First batch: as many own slots as a segment has pieces when the lengths are equal
+    // (waves / segments + 1), rounded up to 8, 12 or 16. Where that is more than 16 the segments
+    // need a second round trip anyway, and the narrow first batch costs less.
+    const dim3 cgrid((unsigned)(p.batch * p.q_heads + (p.new_slots ? p.batch * p.kv_heads : 0)));
+    const long long segs = (long long)p.batch * p.kv_heads;
+    const long long est = (p.waves_total + segs - 1) / segs + 1;
+    if (est > 8 && est <= 12)
+        stream_combine_kernel<D, MODE, DT::kBytes, 12><<<cgrid, dim3(64), 0, s>>>(p);
+    else if (est > 12 && est <= 16)
+        stream_combine_kernel<D, MODE, DT::kBytes, 16><<<cgrid, dim3(64), 0, s>>>(p);
+    else
+        stream_combine_kernel<D, MODE, DT::kBytes, 8><<<cgrid, dim3(64), 0, s>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess || !scores) return err;
     if (MODE == kPages && p.score_block == p.block_size) {

@@ -459,6 +459,34 @@ def test_out_dtype_and_explicit_scale():
     assert np.all(np.abs(got - ref_out) <= bound)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_stream_combine_piece_counts(dtype, d):
+    """Persistent path over few, short segments, so that the flat split cuts them into about
+    (units + lead) / 2 pieces each (two units per wave once the whole batch is under two units per
+    wave): counts around the combine's first batch (8, 12 or 16 own slots, by the segment count),
+    the rest of the 16 own slots, and the overflow slots (up to 24 per round trip, then the rest)."""
+    units = [13, 14, 15, 29, 30, 60, 61, 62, 77, 140]
+    lens = [16 * u for u in units[:-2]] + [16 * units[-2] - 5, 16 * units[-1] - 15]
+    log(f"stream combine piece counts {dtype} d={d} lens={lens}")
+    c = make_case(77, B=len(lens), Hq=4, Hkv=1, d=d, dtype=dtype, P=16, lens=lens)
+    assert_close(c, gpu_attend(c), oracle_attend(c), "pieces")
+    c2 = make_case(78, B=3, Hq=12, Hkv=2, d=d, dtype=dtype, P=16, lens=[16 * 33, 16 * 33 + 1, 16 * 64])
+    assert_close(c2, gpu_attend(c2), oracle_attend(c2), "pieces G=6")
+    # many segments (the combine's first batch is 8 wide), a few of them long enough for the
+    # rest of their own slots and the overflow slots
+    lens3 = [16] * 150 + [16 * 12, 16 * 20, 16 * 40, 2000]
+    c3 = make_case(79, B=len(lens3), Hq=2, Hkv=1, d=d, dtype=dtype, P=16, lens=lens3)
+    assert_close(c3, gpu_attend(c3), oracle_attend(c3), "pieces, 154 segments")
+    # 96 and 80 segments: first batches of 12 and 16 own slots, each with a long sequence whose
+    # pieces run past the own slots
+    lens4 = [200] * 30 + [1200, 1201]
+    c4 = make_case(80, B=len(lens4), Hq=6, Hkv=3, d=d, dtype=dtype, P=16, lens=lens4)
+    assert_close(c4, gpu_attend(c4), oracle_attend(c4), "pieces, 96 segments")
+    lens5 = [300] * 18 + [3000, 2900]
+    c5 = make_case(81, B=len(lens5), Hq=8, Hkv=4, d=d, dtype=dtype, P=16, lens=lens5)
+    assert_close(c5, gpu_attend(c5), oracle_attend(c5), "pieces, 80 segments")
+
+
 def test_partial_and_combine_match_oracle_partitions():
     """Partials of the partition path against the oracle's partitions, in full, window and
     page-list mode. Page lists are cut by list entry (every 16-token quarter of every entry,
@@ -515,17 +543,19 @@ def test_status_codes():
     assert e.value.status == 3
 
 
-def test_workspace_reuse():
+@pytest.mark.parametrize("fill", [0xA5, 0xFF])
+def test_workspace_reuse(fill):
     """One workspace serves any number of calls, which all give the same result: its
     contents on entry are ignored, also between calls whose plans differ (full and window
-    attention sharing one workspace, as the layers of one model do)."""
+    attention sharing one workspace, as the layers of one model do). 0xFF bytes are NaN as
+    floats: partial slots past a segment's piece count must be dropped, not weighted by 0."""
     import paged_kv_cache_16_amd as pkv
     lens = [1500, 333, 4000, 2, 0, 129]
     c = make_case(48, B=6, Hq=16, Hkv=4, d=128, dtype="bf16", P=16, lens=lens)
     n = pkv.workspace_size(c.gk, 6, 16, max(lens))
     n_w = pkv.workspace_size(c.gk, 6, 16, max(lens), window=1000, num_sinks=4)
     assert n > 0 and n_w > 0
-    ws = torch.full((max(n, n_w),), 0xA5, dtype=torch.uint8, device="cuda")  # garbage on entry
+    ws = torch.full((max(n, n_w),), fill, dtype=torch.uint8, device="cuda")  # garbage on entry
     ref = oracle_attend(c)
     ref_w = oracle_attend(c, window=1000, sinks=4)
     outs = []
