@@ -255,6 +255,50 @@ def test_fuzz(f):
     assert_close(c, gpu_attend(c, **gkw), oracle_attend(c, **okw), "fuzz")
 
 
+# ---------------------------------------------------------------------------- persistent-path fuzz
+# Longer contexts than the fuzz above, so the persistent kernel runs and cuts segments into many
+# pieces: random batch, group, kv heads, dtype, head dim, mode and ragged lengths up to 6000.
+STREAM_FUZZ = []
+_srng = np.random.default_rng(2027)
+for _i in range(12):
+    STREAM_FUZZ.append(dict(
+        seed=3000 + _i,
+        dtype=("bf16", "f16", "f32")[_i % 3],
+        d=(128, 64)[(_i // 3) % 2],
+        G=(1, 2, 4, 6, 8)[_i % 5],
+        Hkv=int(_srng.integers(1, 4)),
+        B=int(_srng.integers(1, 9)),
+        Lmax=int(_srng.integers(600, 6001)),
+        mode=("full", "window", "pages")[_i % 3],
+    ))
+
+
+@pytest.mark.parametrize("f", STREAM_FUZZ, ids=[f"s{f['seed']}-{f['dtype']}-d{f['d']}-G{f['G']}-H{f['Hkv']}-B{f['B']}-{f['mode']}"
+                                                for f in STREAM_FUZZ])
+def test_stream_fuzz(f):
+    rng = np.random.default_rng(f["seed"])
+    lens = [int(x) for x in rng.integers(1, f["Lmax"] + 1, size=f["B"])]
+    lens[int(rng.integers(0, f["B"]))] = f["Lmax"]  # one sequence at the bound: the persistent path
+    log(f"stream fuzz {f} lens={lens}")
+    c = make_case(f["seed"], B=f["B"], Hq=f["G"] * f["Hkv"], Hkv=f["Hkv"], d=f["d"], dtype=f["dtype"],
+                  P=16, lens=lens)
+    okw, gkw = {}, {}
+    if f["mode"] == "window":
+        W, S = int(rng.integers(300, 2000)), int(rng.integers(0, 40))
+        okw = dict(window=W, sinks=S)
+        gkw = dict(window=W, num_sinks=S)
+    elif f["mode"] == "pages":
+        k = 24
+        pl = np.full((f["B"], k), -1, np.int32)
+        for b, L in enumerate(lens):
+            npg = (L + 15) // 16
+            pick = sorted(rng.choice(npg, size=min(k, npg), replace=False).tolist())
+            pl[b, :len(pick)] = pick
+        okw = dict(page_list=pl)
+        gkw = dict(page_list=pl)
+    assert_close(c, gpu_attend(c, **gkw), oracle_attend(c, **okw), "stream fuzz")
+
+
 # ---------------------------------------------------------------------------- batches past 64
 @pytest.mark.parametrize("B,mode,fused", [(65, "full", False), (129, "full", True), (130, "window", True),
                                           (200, "pages", False), (200, "full", True)])
