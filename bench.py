@@ -579,7 +579,7 @@ def run_layer(w, args, dev):
 
     dt = {"bf16": "BF16", "f16": "F16", "f32": "F32"}[w.dtype]
     if args.kv_dtype == "int8":
-        kname = f"decode_stream_kernel<I8B,{d},full>"
+        kname = f"decode_stream_kernel<I8B,{d},full" + (">" if args.noalloc else ",fused append>")
     elif args.split_tokens:
         kname = f"decode_split_kernel<{dt},{d},full>"
     elif ws_bytes == 0:  # short sequences: the one-kernel path
@@ -590,8 +590,8 @@ def run_layer(w, args, dev):
     step_desc = ("paged_decode_append_attention: append of the new tokens fused into the persistent split "
                  "kernel, then the LSE combine")
     if args.kv_dtype == "int8":
-        step_desc = ("paged_decode_append_attention on an INT8 cache: quantising append of the new tokens, "
-                     "then the persistent split kernel and the LSE combine")
+        step_desc = ("paged_decode_append_attention on an INT8 cache: the new tokens quantised inside the "
+                     "persistent split kernel, then the LSE combine, which stores the quantised rows")
     if args.noalloc:
         step_desc = "kv_cache_append, then paged_decode_attention_noalloc (workspace in the library's scratch)"
     res = {

@@ -246,15 +246,17 @@ pkv_status paged_decode_attention(const pkv_cache_desc* desc /* host */,
  * and the same outputs. On the work-split path of paged_decode_attention both happen in one
  * kernel (plus the combine, which stores the new rows), on the one-kernel path in that kernel
  * (each (sequence, kv head) workgroup stores its row after its own reads); either way the new
- * token enters attention from k_new/v_new directly. Partition-path calls (split_tokens > 0
- * with several partitions) and INT8 caches run a separate append first.
+ * token enters attention from k_new/v_new directly. On an INT8 cache (work-split path only)
+ * the kernel quantises the new row in registers exactly as kv_cache_append does, so the token
+ * enters attention as stored, and the combine stores the quantised row and its scales.
+ * Partition-path calls (split_tokens > 0 with several partitions) run a separate append first.
  *   k_new, v_new:  [batch][num_kv_heads][head_dim], row b = sequence b's new token.
  *   slot_mapping:  [batch] int32, the slot of position context_lens[b] - 1 of sequence b
  *                  (block_table[b][(L-1)/P] * P + (L-1) % P); < 0 skips the write.
  * Precondition: slot_mapping[b] >= 0 is that slot whenever context_lens[b] > 0 (with a
- * negative slot the new token's values are still the ones attended), and no other sequence
- * of the call reads that slot (a page that takes a write belongs to one sequence, as after a
- * copy-on-write of shared pages). Other arguments as in
+ * negative slot the new token's values, quantised on an INT8 cache, are still the ones
+ * attended), and no other sequence of the call reads that slot (a page that takes a write
+ * belongs to one sequence, as after a copy-on-write of shared pages). Other arguments as in
  * paged_decode_attention; the workspace size is the same. */
 pkv_status paged_decode_append_attention(const pkv_cache_desc* desc /* host */,
                                          void* k_cache, void* v_cache,

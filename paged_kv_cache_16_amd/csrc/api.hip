@@ -514,7 +514,8 @@ pkv_status decode_impl(const pkv_cache_desc* desc, const void* k_cache, const vo
         p.l_part = (float*)((char*)workspace + wl.l_off);
     }
 
-    const bool fuse = fa && pl.path != Plan::kPartitions && desc->dtype != PKV_I8;
+    // INT8 caches take the stream path only, where the fused step quantises the new row in the kernels
+    const bool fuse = fa && pl.path != Plan::kPartitions && (desc->dtype != PKV_I8 || pl.path == Plan::kStream);
     if (fuse) {
         p.k_cache_w = (char*)fa->k_cache;
         p.v_cache_w = (char*)fa->v_cache;

@@ -23,6 +23,7 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_plan.h"
+#include "pkv_q8.h"
 
 namespace pkv {
 
@@ -129,7 +130,6 @@ constexpr int kLgFloats = 4096;
 template <class DT, int D, int MODE, bool FUSED, bool SCORES>
 __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(DecodeParams p) {
-    static_assert(!(DT::kQ8 && FUSED), "INT8 caches take the separate quantising append");
     using TI = typename DT::In;               // q type
     using TM = typename DT::Mma;              // MFMA operand type
     static_assert(TI::kE == TM::kE, "q chunks and operand chunks line up");
@@ -205,6 +205,8 @@ void decode_stream_kernel(DecodeParams p) {
     const bool upper = c >= 8;
     __shared__ float lg_stage[kStreamWaves * (SCORES ? kLgFloats : 1)];
     float* lgb = lg_stage + (SCORES ? (threadIdx.x >> 6) * kLgFloats : 0);
+    // INT8 fused step: each wave's stage for dealing out the new row's codes
+    __shared__ __attribute__((aligned(16))) unsigned char q8_stage[kStreamWaves][FUSED && DT::kQ8 ? 2 * D : 16];
     const float qk_scale = p.qk_scale_log2;
     int f_run = f_begin;
     while (f_run < f_end && pos.b < B) {
@@ -260,9 +262,16 @@ void decode_stream_kernel(DecodeParams p) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[a] = zero4();
         NewRow<TI, D> nrow;
+        NewRowRaw<D> nraw;  // INT8: the new row as loaded, quantised into nq once the ring is primed
+        NewRowQ8<D> nq;
         // the token this step appended (past every attended unit when the length was clamped)
         const int t_new = L_b - 1;
-        if constexpr (FUSED) load_new_row<TI, D>(p, nrow, b, kvh, j, c);
+        if constexpr (FUSED) {
+            if constexpr (DT::kQ8)
+                load_new_row_raw<D>(p, nraw, b, kvh, lane);
+            else
+                load_new_row<TI, D>(p, nrow, b, kvh, j, c);
+        }
 
         // score export: the run's logits are staged in LDS and stored in contiguous bursts
         int lg_n = 0, lg_u0 = u0;
@@ -336,6 +345,13 @@ void decode_stream_kernel(DecodeParams p) {
             }
             if (rb.t0 < 0) return;
             if constexpr (DT::kQ8) {
+                if constexpr (FUSED) {
+                    // the unit holding the new token: its row quantised as the append would store
+                    // it, patched in over the cache's stale bytes and scales
+                    // (one unit per segment: the patch is laid out away from the unit loop)
+                    if (__builtin_expect((unsigned)(t_new - rb.t0) < 16u, 0))
+                        patch_tile_q8<D>(rb.k, rb.v, rb.ks, rb.vs, nq, t_new - rb.t0, j, c);
+                }
                 u32x4 kt[NC], vt[NC];
 #pragma unroll
                 for (int m = 0; m < NCC; ++m) {
@@ -390,6 +406,16 @@ void decode_stream_kernel(DecodeParams p) {
                 RingBuf<DT, D> R0, R1, R2;
                 ring_load<DT, D>(p, R0, my_tok, my_off, 0, n, lane, u0 + ub);
                 ring_load<DT, D>(p, R1, my_tok, my_off, 1, n, lane, u0 + ub);
+                // The fused step's new row was requested before the block table, so it has
+                // arrived by now: quantised here, with the ring's first two units in flight, it
+                // waits for nothing, and only its codes stay live through the run (quantising
+                // after the third unit's request measured slower). Only a batch that holds the
+                // new token quantises it (one run per segment).
+                if constexpr (FUSED) {
+                    const bool has_new =
+                        __builtin_amdgcn_ballot_w64(lane < n && my_tok >= 0 && (unsigned)(t_new - my_tok) < 16u) != 0;
+                    if (has_new) quantise_new_row<TI, D>(nraw, nq, q8_stage[threadIdx.x >> 6], lane, j, c);
+                }
                 for (int k = 0; k < n; k += 3) {
                     ring_load<DT, D>(p, R2, my_tok, my_off, k + 2, n, lane, u0 + ub);
                     process(R0);
@@ -525,15 +551,19 @@ __device__ __forceinline__ void merge_rows(float& M, float& Ls, float (&o)[PER],
 // (their slots hold stale values, never multiplied in). The rest of the own slots and up to
 // kCombineWide overflow pieces (slots of waves w0 + k) share the second round trip; longer
 // segments take one more per kCombineWide pieces.
-template <int D, int MODE, int ES, int KB>
+template <class DT, int D, int MODE, int KB>
 __global__ __launch_bounds__(64) void stream_combine_kernel(DecodeParams p) {
     static_assert(KB <= kSegSlots, "the first batch is the segment's own slots");
     constexpr int PER = D / 64;
     const int r = blockIdx.x;
     if (r >= p.batch * p.q_heads) {
         // the fused step's new K/V rows, in workgroups of their own beside the merges (a merge
-        // workgroup that also stored a row waited for the row before fetching its partials)
-        write_new_row<ES, D>(p, r - p.batch * p.q_heads, threadIdx.x);
+        // workgroup that also stored a row waited for the row before fetching its partials);
+        // an INT8 cache takes the row quantised
+        if constexpr (DT::kQ8)
+            write_new_row_q8<typename DT::In, D>(p, r - p.batch * p.q_heads, threadIdx.x);
+        else
+            write_new_row<DT::kBytes, D>(p, r - p.batch * p.q_heads, threadIdx.x);
         return;
     }
     const int G = p.group;
@@ -780,13 +810,7 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
         if (e != hipSuccess) return e;
     }
     const dim3 grid(blocks), block(64 * kStreamWaves);
-    if constexpr (DT::kQ8) {
-        if (fused) return hipErrorInvalidValue;
-        if (scores)
-            decode_stream_kernel<DT, D, MODE, false, true><<<grid, block, 0, s>>>(p);
-        else
-            decode_stream_kernel<DT, D, MODE, false, false><<<grid, block, 0, s>>>(p);
-    } else if (scores) {
+    if (scores) {
         if (fused)
             decode_stream_kernel<DT, D, MODE, true, true><<<grid, block, 0, s>>>(p);
         else
@@ -810,11 +834,11 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
     const long long segs = (long long)p.batch * p.kv_heads;
     const long long est = (p.waves_total + segs - 1) / segs + 1;
     if (est > 8 && est <= 12)
-        stream_combine_kernel<D, MODE, DT::kBytes, 12><<<cgrid, dim3(64), 0, s>>>(p);
+        stream_combine_kernel<DT, D, MODE, 12><<<cgrid, dim3(64), 0, s>>>(p);
     else if (est > 12 && est <= 16)
-        stream_combine_kernel<D, MODE, DT::kBytes, 16><<<cgrid, dim3(64), 0, s>>>(p);
+        stream_combine_kernel<DT, D, MODE, 16><<<cgrid, dim3(64), 0, s>>>(p);
     else
-        stream_combine_kernel<D, MODE, DT::kBytes, 8><<<cgrid, dim3(64), 0, s>>>(p);
+        stream_combine_kernel<DT, D, MODE, 8><<<cgrid, dim3(64), 0, s>>>(p);
     err = hipGetLastError();
     if (err != hipSuccess || !scores) return err;
     if (MODE == kPages && p.score_block == p.block_size) {
