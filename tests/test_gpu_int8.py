@@ -137,9 +137,9 @@ def test_int8_attention(ic):
 @pytest.mark.parametrize("with_scores", [False, True], ids=["plain", "scores"])
 @pytest.mark.parametrize("ic", INT8_CASES, ids=[x["name"] for x in INT8_CASES])
 def test_int8_fused_step_and_scores(ic, with_scores):
-    """paged_decode_append_attention on an INT8 cache (the quantising append, then attention):
-    the cache bytes equal the oracle's append, the outputs and the exported scores match the
-    oracle."""
+    """paged_decode_append_attention on an INT8 cache (the new row quantised inside the attention
+    kernel, stored by the combine): the cache bytes equal the oracle's append, the outputs and the
+    exported scores match the oracle."""
     import paged_kv_cache_16_amd as pkv
     c = make_case8(83, B=ic["B"], Hq=ic["Hq"], Hkv=ic["Hkv"], d=ic["d"], dtype=ic["dtype"], P=ic["P"],
                    lens=ic["lens"], drop_last=True)
@@ -166,6 +166,50 @@ def test_int8_fused_step_and_scores(ic, with_scores):
     err = float(np.abs(gs.cpu().double().numpy() - ref).max())
     log(f"    max|score err| = {err:.3e}")
     assert err <= 1e-5
+
+
+def test_int8_fused_step_edge_rows():
+    """The fused step's in-kernel quantisation at its edges: an all-zero K and V row (scale 0,
+    codes 0), rows with one large element (every other code rounds to 0 or +-1), a sequence of
+    length 1 (the new token alone) and a skipped store (slot -1: the token is still attended,
+    quantised, and the cache keeps what it held)."""
+    import paged_kv_cache_16_amd as pkv
+    lens = [300, 17, 1, 70]
+    B, Hq, Hkv, d, P, dt = 4, 8, 2, 128, 16, "i8bf16"
+    c = make_case8(85, B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dt, P=P, lens=lens, drop_last=True)
+    c.K[0, lens[0] - 1] = 0.0
+    c.V[0, lens[0] - 1] = 0.0
+    c.K[1, lens[1] - 1] = 0.01
+    c.K[1, lens[1] - 1, :, 5] = 50.0
+    c.V[1, lens[1] - 1] = -0.02
+    c.V[1, lens[1] - 1, :, 77] = -3.0
+    kn = torch.stack([c.K[b, L - 1] for b, L in enumerate(lens)])
+    vn = torch.stack([c.V[b, L - 1] for b, L in enumerate(lens)])
+    true_slots = [synth.slot_of(c.bt, b, L - 1, P) for b, L in enumerate(lens)]
+    store_slots = true_slots[:3] + [-1]
+    # oracle pools: the prefixes, then the new rows (all of them for attention, the stored ones
+    # for the cache bytes)
+    pre = synth.token_slots(c.bt, lens, P, last=[L - 1 for L in lens])
+    kp = torch.cat([c.K[b, :L - 1] for b, L in enumerate(lens)])
+    vp = torch.cat([c.V[b, :L - 1] for b, L in enumerate(lens)])
+    base_k = np.full(c.nb * Hkv * P * (d + 4), 0xFF, np.uint8)
+    base_v = base_k.copy()
+    oracle.kv_append(dt, base_k, base_v, synth.raw_numpy(kp), synth.raw_numpy(vp), pre.numpy(), P=P, Hkv=Hkv, d=d)
+    att_k, att_v, st_k, st_v = base_k.copy(), base_v.copy(), base_k.copy(), base_v.copy()
+    oracle.kv_append(dt, att_k, att_v, synth.raw_numpy(kn), synth.raw_numpy(vn), np.array(true_slots, np.int32),
+                     P=P, Hkv=Hkv, d=d)
+    oracle.kv_append(dt, st_k, st_v, synth.raw_numpy(kn), synth.raw_numpy(vn), np.array(store_slots, np.int32),
+                     P=P, Hkv=Hkv, d=d)
+    log(f"int8 fused edge rows lens={lens}")
+    out, lse = pkv.paged_decode_append_attention(c.gq, c.gk, c.gv, kn.cuda(), vn.cuda(),
+                                                 torch.tensor(store_slots, dtype=torch.int32).cuda(), c.gbt, c.gcl,
+                                                 max_context_len=max(lens))
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bytes(c.gk), st_k) and np.array_equal(raw_bytes(c.gv), st_v)
+    ref = oracle.decode_attention(dt, att_k, att_v, synth.raw_numpy(c.q), c.bt.numpy(), np.array(lens, np.int32),
+                                  P=P, Hkv=Hkv, d=d)
+    got = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    assert_close(tol_case(c), got, ref, "int8 fused edge rows")
 
 
 def test_int8_status_codes():
