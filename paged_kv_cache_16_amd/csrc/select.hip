@@ -6,7 +6,8 @@
 //      each page's weight summed over the heads in index order in fp32 (the stated
 //      definition, so the result is exact and deterministic). The score rows are first
 //      staged in LDS with 16-byte loads (a 4-byte load per lane moves a quarter of the bytes
-//      per address cycle, which left this phase bound by the CU's load issue rate).
+//      per address cycle, which left this phase bound by the CU's load issue rate); when all
+//      of them fit, as one contiguous copy through a buffer resource.
 //   2. A radix select (four 8-bit digits, most significant first) finds the key T of the
 //      want-th best page and how many pages with key T are taken (want = k - recent, capped
 //      by the number of older pages). Every wave reads the histogram and derives the digit
@@ -85,6 +86,29 @@ __global__ __launch_bounds__(kThreads) void select_pages_kernel(SelectParams p) 
         // aligned array, checked on the host), then each page's ordered sum from LDS.
         float* stg = reinterpret_cast<float*>(lds + ((p.stride + 3) & ~3));
         const int C = p.stage_pages;  // a multiple of 4
+        if (C >= p.stride) {
+            // One chunk: the staging rows are the score rows as they lie in memory, a contiguous
+            // copy. Every 16-byte load goes out through a buffer resource (no per-lane address
+            // arithmetic; loads past the block read zeros) before any is stored.
+            const int total = p.heads * (p.stride >> 2);
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(reinterpret_cast<const char*>(sc), total * 16);
+            for (int f0 = tid; f0 < total; f0 += kThreads * kStageLoads) {
+                u32x4 v[kStageLoads];
+#pragma unroll
+                for (int i = 0; i < kStageLoads; ++i) v[i] = load16_tile_stream(r, (unsigned)(f0 + i * kThreads) * 16u);
+#pragma unroll
+                for (int i = 0; i < kStageLoads; ++i) {
+                    const int f = f0 + i * kThreads;
+                    if (f < total) *reinterpret_cast<u32x4*>(stg + 4 * (size_t)f) = v[i];
+                }
+            }
+            __syncthreads();
+            for (int q = tid; q < p.stride; q += kThreads) {
+                float acc = 0.f;
+                for (int h = 0; h < p.heads; ++h) acc += stg[(size_t)h * p.stride + q];
+                key[q] = order_key(acc);
+            }
+        } else
         for (int c0 = 0; c0 < p.stride; c0 += C) {
             const int cn = p.stride - c0 < C ? p.stride - c0 : C;
             const int nq4 = cn >> 2;
