@@ -832,7 +832,7 @@ static hipError_t launch_stream_t(bool fused, bool scores, const DecodeParams& p
     // need a second round trip anyway, and the narrow first batch costs less.
     const dim3 cgrid((unsigned)(p.batch * p.q_heads + (p.new_slots ? p.batch * p.kv_heads : 0)));
     const long long segs = (long long)p.batch * p.kv_heads;
-    const long long est = (p.waves_total + segs - 1) / segs + 1;
+    const long long est = segs > 0 ? (p.waves_total + segs - 1) / segs + 1 : 0;
     if (est > 8 && est <= 12)
         stream_combine_kernel<DT, D, MODE, 12><<<cgrid, dim3(64), 0, s>>>(p);
     else if (est > 12 && est <= 16)
