@@ -20,6 +20,10 @@
 // round trip covers the first 8, 12 or 16 pieces, a second the rest of the segment's own slots and
 // up to kCombineWide overflow pieces, and each later one kCombineWide more.
 // Workspace rows: (B * Hkv * kSegSlots + waves) x G, whatever the context lengths.
+// In the fused decode step (FUSED) the run that reaches a segment's newest position takes the
+// new token from k_new / v_new in registers and patches it into the sub-tile that holds it (on
+// an INT8 cache after quantising it in the kernel exactly as the append would store it); the
+// combine's extra workgroups store the new rows once every read of them has returned.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_plan.h"
